@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark: MLA absorbed decode on one MI355X, DeepSeek-V2 shape B=16, T=4096.
+
+A step is one whole decode step of one layer on one batch of synthetic input:
+    mla_absorb_q -> mla_decode_partials -> mla_decode_combine -> mla_out_uv
+(the last two together are mla_decode_attn).  Inputs are resident in HBM
+before the timed region.  Every step uses the next entry of a rotating pool of
+independently seeded (cache, W^UK, W^UV, q) sets totalling > 512 MB, twice the
+256 MB Infinity Cache, so the cache bytes really come from HBM.
+
+Prints ONE JSON line on stdout (everything else goes to stderr).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import head_latent_attention_absorb_amd as mla  # noqa: E402
+from workload import CONFIGS, f32_to_bf16_bits, make_case  # noqa: E402
+
+METRIC = "MLA decode tokens/s and latent-cache HBM GB/s (% roofline), B=16 T=4096"
+WORKLOAD = "dsv2_b16_t4096"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partials_dsv2_b16_t4096_counters.json")
+KERNEL_SOURCE = os.path.join(ROOT, "head_latent_attention_absorb_amd", "csrc", "decode_mfma.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(f32_to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Entry:
+    """One pool entry: a seeded decode input resident on the GPU."""
+
+    def __init__(self, cfg, seed):
+        case = make_case(cfg, seed)
+        self.case = case
+        self.q_c = to_dev(case.q_c)
+        self.q_r = to_dev(case.q_r)
+        self.w_uk = to_dev(case.w_uk)
+        self.w_uv = to_dev(case.w_uv)
+        self.cache_t = to_dev(case.cache)
+        self.lens = torch.from_numpy(case.seq_lens).cuda()
+        self.cache = mla.latent_cache(self.cache_t, self.lens, cfg.d_rope)
+        self.nbytes = sum(t.numel() * t.element_size()
+                          for t in (self.q_c, self.q_r, self.w_uk, self.w_uv, self.cache_t))
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_counters(sha: str):
+    """HBM bytes per launch of the decode kernel from committed rocprofv3 PMC
+    counters, or None when absent or taken on a different kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha") != sha:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(entry: Entry, cfg, n_requests: int):
+    """The oracle (unabsorbed, fp64) on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    case = entry.case
+    reqs = list(range(n_requests))
+    t0 = time.perf_counter()
+    oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens, case.w_uk,
+                                case.w_uv, cfg.scale, requests=reqs)
+    dt = time.perf_counter() - t0
+    return {
+        "value": n_requests / dt,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"unabsorbed fp64 oracle, {n_requests} of {cfg.batch} requests x all "
+                   f"{cfg.n_heads} heads x T={cfg.max_len}, one layer; {dt:.2f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--pool-mb", type=int, default=640,
+                    help="total bytes of the rotating input pool (>= 512 MB defeats the MALL)")
+    ap.add_argument("--cpu-requests", type=int, default=16,
+                    help="requests in the CPU oracle sample (0 skips it)")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = CONFIGS[WORKLOAD]
+    B, nh, row = cfg.batch, cfg.n_heads, cfg.row
+    log(f"[bench] generating pool for {WORKLOAD}")
+    pool = [Entry(cfg, 0)]
+    n_pool = max(1, math.ceil(args.pool_mb * 1e6 / pool[0].nbytes))
+    for i in range(1, n_pool):
+        pool.append(Entry(cfg, i))
+    pool_mb = sum(e.nbytes for e in pool) / 1e6
+    log(f"[bench] pool: {n_pool} entries, {pool_mb:.0f} MB")
+
+    dev = "cuda"
+    plan = mla.decode_plan(nh, cfg.d_latent, cfg.d_rope, torch.bfloat16, pool[0].cache,
+                           split_tokens=args.split_tokens, d_head=cfg.d_head)
+    log(f"[bench] {plan}")
+    ws = mla.workspace_for(plan, dev)
+    q_cat = torch.empty((B, nh, row), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty((B, nh, cfg.d_latent), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, nh), dtype=torch.float32, device=dev)
+    o = torch.empty((B, nh, cfg.d_head), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(e: Entry, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mla.absorb_q(e.q_c, e.q_r, e.w_uk, out=q_cat)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
+        if ev is not None:
+            ev[2].record(stream)
+        mla.decode_combine(e.cache, nh, plan, ws, o_lat, lse)
+        if ev is not None:
+            ev[3].record(stream)
+        mla.out_uv(o_lat, e.w_uv, out=o)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(pool[i % n_pool])
+    torch.cuda.synchronize()
+
+    # Timed region: exactly --steps whole steps.
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e_start.record(stream)
+    for i in range(args.steps):
+        step(pool[i % n_pool])
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e_start.elapsed_time(e_end) / args.steps
+
+    # Same steps again with HIP events between the kernels (per-kernel times).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(pool[i % n_pool], evs[i])
+    torch.cuda.synchronize()
+    phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(4)] for ev in evs])
+    phase_us = phase.mean(axis=0) * 1e3
+    absorb_us, partials_us, combine_us, out_uv_us = (float(x) for x in phase_us)
+    attn_us = partials_us + combine_us
+    log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, partials "
+        f"{partials_us:.1f}, combine {combine_us:.1f}, out_uv {out_uv_us:.1f}")
+
+    # Algorithmic work (split partials excluded).
+    tokens = int(sum(int(x) for x in pool[0].case.seq_lens))
+    cache_bytes = tokens * row * 2
+    q_bytes = B * nh * row * 2
+    olat_bytes = B * nh * cfg.d_latent * 2 + B * nh * 4
+    flops = 2.0 * nh * (row + cfg.d_latent) * tokens
+    k2_bytes = cache_bytes + q_bytes
+    k2_gbps = k2_bytes / (partials_us * 1e-6) / 1e9
+    attn_bytes = cache_bytes + q_bytes + olat_bytes
+    t_roof_us = max(attn_bytes / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    sha = kernel_sha()
+
+    result = {
+        "metric": METRIC,
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD, "batch": B, "seq_len": cfg.max_len, "n_heads": nh,
+            "d_head": cfg.d_head, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope,
+            "cache": "contiguous", "layers_per_step": 1,
+            "rotating_pool_mb": round(pool_mb), "split_tokens": plan.split_tokens,
+            "num_splits": plan.num_splits, "parallelism": "single-gpu",
+        },
+        "latent_cache_GBps": cache_bytes / (attn_us * 1e-6) / 1e9,
+        "decode_attn_us": attn_us,
+        "decode_attn_pct_roofline": 100.0 * t_roof_us / attn_us,
+        "kernels_us": {"absorb_q": absorb_us, "decode_partials": partials_us,
+                       "decode_combine": combine_us, "out_uv": out_uv_us},
+        "roofline": {
+            "kernel": "decode_mfma_kernel (mla_decode_partials)",
+            "bound": "hbm",
+            "achieved": k2_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": k2_gbps / HBM_PEAK_GBPS,
+            "traffic": traffic_from_counters(sha),
+            "alg_bytes_per_launch": k2_bytes,
+            "mfma_tflops": flops / (partials_us * 1e-6) / 1e12,
+            "kernel_source_sha": sha,
+        },
+    }
+    if args.cpu_requests > 0:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_requests} requests")
+        result["cpu_baseline"] = cpu_baseline(pool[0], cfg, args.cpu_requests)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

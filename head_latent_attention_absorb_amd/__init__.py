@@ -1,0 +1,284 @@
+"""MI355X-native MLA absorbed decode: thin Python binding over libmla_absorb.so.
+
+Every call marshals torch tensors (device memory and the current HIP stream)
+into the C ABI declared in include/mla_absorb.h; all arithmetic happens in the
+library's gfx950 kernels.  There is no CPU or PyTorch fallback: if the
+library is missing or the device is not a gfx950, calls raise.
+
+Decode step of one layer (DeepSeek-V2 read-through, 2kiu.com/news/6085339,
+section 2.3):
+    q_cat = absorb_q(q_c, q_r, w_uk)                # [q_lat | q^R]
+    o_lat, lse = decode_attn(q_cat, cache, scale)   # latent-space attention
+    o = out_uv(o_lat, w_uv)                         # W^UV applied last
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmla_absorb.so")
+
+MLA_F32, MLA_BF16 = 0, 1
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("max_len", ctypes.c_int32), ("num_pages", ctypes.c_int64)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("split_tokens", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("kernel", ctypes.c_int32), ("head_groups", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+    def __repr__(self):
+        return (f"Plan(split_tokens={self.split_tokens}, num_splits={self.num_splits}, "
+                f"kernel={'mfma' if self.kernel == 1 else 'generic'}, "
+                f"head_groups={self.head_groups}, workspace_bytes={self.workspace_bytes})")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla_absorb.so (built by ``head_latent_attention_absorb_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -m head_latent_attention_absorb_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.mla_status_str.restype = ctypes.c_char_p
+    L.mla_status_str.argtypes = [ctypes.c_int]
+    L.mla_abi_version.restype = i32
+    L.mla_absorb_q.restype = ctypes.c_int
+    L.mla_absorb_q.argtypes = [ctypes.POINTER(Dims), i32, vp, vp, vp, vp, vp]
+    L.mla_decode_plan.restype = ctypes.c_int
+    L.mla_decode_plan.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(CacheDesc), i32,
+                                  ctypes.POINTER(Plan)]
+    L.mla_decode_attn.restype = ctypes.c_int
+    L.mla_decode_attn.argtypes = [ctypes.POINTER(Dims), i32, vp, ctypes.POINTER(CacheDesc),
+                                  ctypes.c_float, ctypes.POINTER(Plan), vp, vp, vp, sz, vp]
+    L.mla_decode_partials.restype = ctypes.c_int
+    L.mla_decode_partials.argtypes = [ctypes.POINTER(Dims), i32, vp, ctypes.POINTER(CacheDesc),
+                                      ctypes.c_float, ctypes.POINTER(Plan), vp, sz, vp]
+    L.mla_decode_combine.restype = ctypes.c_int
+    L.mla_decode_combine.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(CacheDesc),
+                                     ctypes.POINTER(Plan), vp, sz, vp, vp, vp]
+    L.mla_out_uv.restype = ctypes.c_int
+    L.mla_out_uv.argtypes = [ctypes.POINTER(Dims), i32, vp, vp, vp, vp]
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MLAError(fn, status, lib().mla_status_str(status).decode())
+
+
+_DT = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+@dataclasses.dataclass
+class LatentCache:
+    """One layer's latent cache on the device.
+
+    data: contiguous [B, max_len, d_latent + d_rope] or paged
+          [num_pages, page_size, d_latent + d_rope]
+    seq_lens: int32 [B]; page_table: int32 [B, max_len // page_size] or None.
+    """
+
+    data: torch.Tensor
+    seq_lens: torch.Tensor
+    d_rope: int
+    page_table: Optional[torch.Tensor] = None
+    page_size: int = 0
+    max_len: int = 0
+
+    def desc(self) -> CacheDesc:
+        d = CacheDesc()
+        d.data = self.data.data_ptr()
+        d.seq_lens = self.seq_lens.data_ptr()
+        d.page_table = self.page_table.data_ptr() if self.page_table is not None else None
+        d.page_size = self.page_size if self.page_table is not None else 0
+        d.max_len = self.max_len if self.page_table is not None else self.data.shape[1]
+        d.num_pages = self.data.shape[0] if self.page_table is not None else 0
+        return d
+
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+
+def make_dims(n_heads: int, d_head: int, d_rope: int, d_latent: int, dtype) -> Dims:
+    return Dims(n_heads, d_head, d_rope, d_latent,
+                _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype))
+
+
+def absorb_q(q_c: torch.Tensor, q_r: torch.Tensor, w_uk: torch.Tensor,
+             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q_cat[b,i] = [W^UK_i^T q^C[b,i] | q^R[b,i]]  -> [B, n_h, d_c + d_h^R]."""
+    B, nh, dh = q_c.shape
+    dr = q_r.shape[2]
+    dc = w_uk.shape[2]
+    dims = make_dims(nh, dh, dr, dc, _dtype_code(q_c))
+    _require(q_r, "q_r", (B, nh, dr), q_c.dtype, q_c.device)
+    _require(w_uk, "w_uk", (nh, dh, dc), q_c.dtype, q_c.device)
+    _require(q_c, "q_c", (B, nh, dh), q_c.dtype, q_c.device)
+    if out is None:
+        out = torch.empty((B, nh, dc + dr), dtype=q_c.dtype, device=q_c.device)
+    _require(out, "out", (B, nh, dc + dr), q_c.dtype, q_c.device)
+    _check("mla_absorb_q", lib().mla_absorb_q(ctypes.byref(dims), B, _ptr(q_c), _ptr(q_r),
+                                              _ptr(w_uk), _ptr(out), _stream(stream)))
+    return out
+
+
+def decode_plan(n_heads: int, d_latent: int, d_rope: int, dtype, cache: LatentCache,
+                split_tokens: int = 0, d_head: int = 1) -> Plan:
+    dims = make_dims(n_heads, d_head, d_rope, d_latent, dtype)
+    plan = Plan()
+    desc = cache.desc()
+    _check("mla_decode_plan", lib().mla_decode_plan(ctypes.byref(dims), cache.batch(),
+                                                    ctypes.byref(desc), split_tokens,
+                                                    ctypes.byref(plan)))
+    return plan
+
+
+def workspace_for(plan: Plan, device) -> torch.Tensor:
+    """A device workspace of plan.workspace_bytes (256-byte aligned)."""
+    n = max(int(plan.workspace_bytes), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode_attn(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,
+                plan: Optional[Plan] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None, split_tokens: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Latent-space decode attention; returns (o_lat [B,n_h,d_c], lse [B,n_h] fp32)."""
+    B, nh, row = q_cat.shape
+    if cache.data.shape[2] != row:
+        raise ValueError(f"cache row width {cache.data.shape[2]} != q_cat width {row}")
+    d_rope = int(cache.d_rope)
+    d_latent = row - d_rope
+    dev = q_cat.device
+    _require(cache.seq_lens, "seq_lens", (B,), torch.int32, dev)
+    if cache.data.dtype != q_cat.dtype:
+        raise TypeError("cache and q_cat dtypes differ")
+    dims = make_dims(nh, 1, d_rope, d_latent, _dtype_code(q_cat))
+    desc = cache.desc()
+    if plan is None:
+        plan = Plan()
+        _check("mla_decode_plan", lib().mla_decode_plan(ctypes.byref(dims), B,
+                                                        ctypes.byref(desc), split_tokens,
+                                                        ctypes.byref(plan)))
+    if workspace is None:
+        workspace = workspace_for(plan, dev)
+    if out is None:
+        out = torch.empty((B, nh, d_latent), dtype=q_cat.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, nh), dtype=torch.float32, device=dev)
+    _require(out, "out", (B, nh, d_latent), q_cat.dtype, dev)
+    _require(lse, "lse", (B, nh), torch.float32, dev)
+    _check("mla_decode_attn", lib().mla_decode_attn(
+        ctypes.byref(dims), B, _ptr(q_cat), ctypes.byref(desc), float(softmax_scale),
+        ctypes.byref(plan), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def decode_partials(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,
+                    plan: Plan, workspace: torch.Tensor, stream=None) -> None:
+    """First phase of decode_attn: per-split partials into `workspace`."""
+    B, nh, row = q_cat.shape
+    d_rope = int(cache.d_rope)
+    dims = make_dims(nh, 1, d_rope, row - d_rope, _dtype_code(q_cat))
+    desc = cache.desc()
+    _check("mla_decode_partials", lib().mla_decode_partials(
+        ctypes.byref(dims), B, _ptr(q_cat), ctypes.byref(desc), float(softmax_scale),
+        ctypes.byref(plan), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def decode_combine(cache: LatentCache, n_heads: int, plan: Plan, workspace: torch.Tensor,
+                   out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Second phase of decode_attn: merge the partials into out (and lse)."""
+    B = cache.batch()
+    d_rope = int(cache.d_rope)
+    d_latent = out.shape[2]
+    dims = make_dims(n_heads, 1, d_rope, d_latent, _dtype_code(out))
+    desc = cache.desc()
+    _check("mla_decode_combine", lib().mla_decode_combine(
+        ctypes.byref(dims), B, ctypes.byref(desc), ctypes.byref(plan), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def out_uv(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """o[b,i,h] = sum_c o_lat[b,i,c] W^UV[i,c,h] -> [B, n_h, d_h]."""
+    B, nh, dc = o_lat.shape
+    dh = w_uv.shape[2]
+    dims = make_dims(nh, dh, 0, dc, _dtype_code(o_lat))
+    _require(w_uv, "w_uv", (nh, dc, dh), o_lat.dtype, o_lat.device)
+    if out is None:
+        out = torch.empty((B, nh, dh), dtype=o_lat.dtype, device=o_lat.device)
+    _require(out, "out", (B, nh, dh), o_lat.dtype, o_lat.device)
+    _check("mla_out_uv", lib().mla_out_uv(ctypes.byref(dims), B, _ptr(o_lat), _ptr(w_uv),
+                                          _ptr(out), _stream(stream)))
+    return out
+
+
+def latent_cache(data: torch.Tensor, seq_lens: torch.Tensor, d_rope: int,
+                 page_table: Optional[torch.Tensor] = None, page_size: int = 0,
+                 max_len: Optional[int] = None) -> LatentCache:
+    """Describe a contiguous ([B, max_len, row]) or paged ([pages, page_size, row]) cache."""
+    if page_table is None:
+        return LatentCache(data, seq_lens, int(d_rope), None, 0, int(data.shape[1]))
+    ml = int(max_len) if max_len is not None else int(page_table.shape[1]) * page_size
+    return LatentCache(data, seq_lens, int(d_rope), page_table, page_size, ml)

@@ -1,0 +1,306 @@
+// C ABI of the MLA absorbed-decode library: argument checks, split-KV
+// planning and kernel dispatch.  Declared in include/mla_absorb.h.
+
+#include <mutex>
+#include <string.h>
+
+#include "../../include/mla_absorb.h"
+#include "mla_internal.h"
+
+namespace {
+
+using mla::DecodeArgs;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  bool valid = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+// Properties of the current device, queried once per device.
+mla_status_t current_device(DeviceInfo* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.valid) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_DEVICE;
+    d.cus = prop.multiProcessorCount;
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.valid = true;
+  }
+  if (!d.gfx950) return MLA_ERR_DEVICE;
+  *out = d;
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mla_status_t check_dims(const mla_dims_t* d) {
+  if (d == nullptr) return MLA_ERR_NULL;
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (d->n_heads < 1 || d->n_heads > 1024 || d->d_head < 1 || d->d_head > 1024 ||
+      d->d_rope < 0 || d->d_rope > 1024 || d->d_latent < 1 || d->d_latent > 2048)
+    return MLA_ERR_DIMS;
+  return MLA_OK;
+}
+
+bool use_mfma(const mla_dims_t* d) {
+  return d->dtype == MLA_BF16 && d->d_latent == 512 && d->d_rope == 64 &&
+         d->n_heads % mla::kMfmaHeadsPerGroup == 0;
+}
+
+mla_status_t check_cache(const mla_cache_t* c) {
+  if (c == nullptr) return MLA_ERR_NULL;
+  if (c->max_len < 0) return MLA_ERR_DIMS;
+  if (c->page_table != nullptr) {
+    if (c->page_size < 1 || c->max_len % c->page_size != 0 || c->num_pages < 1)
+      return MLA_ERR_DIMS;
+  } else if (c->page_size != 0) {
+    return MLA_ERR_DIMS;
+  }
+  return MLA_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t workspace_for(const mla_dims_t* d, int batch, int num_splits) {
+  const size_t parts = static_cast<size_t>(batch) * num_splits * d->n_heads;
+  return round256(parts * d->d_latent * sizeof(float)) + round256(parts * sizeof(float));
+}
+
+mla_status_t make_plan(const mla_dims_t* d, int batch, const mla_cache_t* c, int split_req,
+                       const DeviceInfo& dev, mla_decode_plan_t* plan) {
+  const bool mfma = use_mfma(d);
+  const int granule = mfma ? mla::kMfmaTokenGranule : 1;
+  const int groups = mfma ? d->n_heads / mla::kMfmaHeadsPerGroup : d->n_heads;
+  const int max_len = c->max_len;
+  const int len_cap = max_len > 0 ? (max_len + granule - 1) / granule * granule : granule;
+  int split;
+  if (split_req < 0) return MLA_ERR_DIMS;
+  if (split_req > 0) {
+    split = (split_req + granule - 1) / granule * granule;
+  } else {
+    // About one workgroup per compute unit when every request is at max_len.
+    const long long per_split = static_cast<long long>(batch > 0 ? batch : 1) * groups;
+    const long long target = mfma ? dev.cus : 2LL * dev.cus;
+    const long long splits = (target + per_split - 1) / per_split;
+    const long long raw = (max_len + splits - 1) / (splits > 0 ? splits : 1);
+    split = static_cast<int>((raw + granule - 1) / granule * granule);
+    const int floor_tokens = mfma ? 2 * granule : 64;
+    if (split < floor_tokens) split = floor_tokens;
+  }
+  if (split > len_cap) split = len_cap;
+  const int num_splits = max_len > 0 ? (max_len + split - 1) / split : 1;
+  plan->split_tokens = split;
+  plan->num_splits = num_splits;
+  plan->kernel = mfma ? 1 : 0;
+  plan->head_groups = groups;
+  plan->workspace_bytes = workspace_for(d, batch, num_splits);
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_DIMS: return "MLA_ERR_DIMS: size out of range or inconsistent";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unsupported storage type";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: device pointer not 16-byte aligned";
+    case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: kernel launch failed";
+    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: no current gfx950 device";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+int32_t mla_abi_version(void) { return 1; }
+
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch, const void* q_c,
+                          const void* q_r, const void* w_uk, void* q_cat, void* stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0) return MLA_ERR_DIMS;
+  if (batch == 0) return MLA_OK;
+  if (q_c == nullptr || w_uk == nullptr || q_cat == nullptr ||
+      (dims->d_rope > 0 && q_r == nullptr))
+    return MLA_ERR_NULL;
+  if (!aligned16(q_c) || !aligned16(w_uk) || !aligned16(q_cat) ||
+      (q_r != nullptr && !aligned16(q_r)))
+    return MLA_ERR_ALIGN;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != MLA_OK) return st;
+  (void)hipGetLastError();
+  const hipError_t e = mla::launch_absorb_q(dims->dtype, batch, dims->n_heads, dims->d_head,
+                                            dims->d_rope, dims->d_latent, q_c, q_r, w_uk,
+                                            q_cat, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status_t mla_decode_plan(const mla_dims_t* dims, int32_t batch, const mla_cache_t* cache,
+                             int32_t split_tokens, mla_decode_plan_t* plan) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (plan == nullptr) return MLA_ERR_NULL;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch < 0) return MLA_ERR_DIMS;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != MLA_OK) return st;
+  return make_plan(dims, batch, cache, split_tokens, dev, plan);
+}
+
+}  // extern "C"
+
+namespace {
+
+enum DecodePart { kPartials = 1, kCombine = 2 };
+
+// Validate a decode call and fill the kernel arguments.  `parts` says which
+// of the two phases will run, so only their pointers are required.
+mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q_cat,
+                            const mla_cache_t* cache, float softmax_scale,
+                            const mla_decode_plan_t* plan, void* out_lat, float* lse,
+                            const void* workspace, size_t workspace_bytes, void* stream,
+                            int parts, mla_decode_plan_t* plan_out, DecodeArgs* a) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch < 0) return MLA_ERR_DIMS;
+  if (batch == 0) return MLA_OK;  // nothing to do; callers return before launching
+  if (cache->seq_lens == nullptr) return MLA_ERR_NULL;
+  if ((parts & kPartials) && (q_cat == nullptr || cache->data == nullptr)) return MLA_ERR_NULL;
+  if ((parts & kCombine) && out_lat == nullptr) return MLA_ERR_NULL;
+  if (((parts & kPartials) && (!aligned16(q_cat) || !aligned16(cache->data))) ||
+      ((parts & kCombine) && (!aligned16(out_lat) ||
+                              (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)))
+    return MLA_ERR_ALIGN;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != MLA_OK) return st;
+
+  if (plan == nullptr) {
+    if ((st = make_plan(dims, batch, cache, 0, dev, plan_out)) != MLA_OK) return st;
+  } else {
+    // A caller's plan must be one this library would produce for these sizes.
+    if ((st = make_plan(dims, batch, cache, plan->split_tokens, dev, plan_out)) != MLA_OK)
+      return st;
+    if (plan_out->split_tokens != plan->split_tokens ||
+        plan_out->num_splits != plan->num_splits || plan_out->kernel != plan->kernel ||
+        plan_out->head_groups != plan->head_groups ||
+        plan_out->workspace_bytes != plan->workspace_bytes)
+      return MLA_ERR_DIMS;
+  }
+  if (workspace == nullptr || workspace_bytes < plan_out->workspace_bytes)
+    return MLA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MLA_ERR_ALIGN;
+
+  const size_t parts_n = static_cast<size_t>(batch) * plan_out->num_splits * dims->n_heads;
+  a->batch = batch;
+  a->n_heads = dims->n_heads;
+  a->d_latent = dims->d_latent;
+  a->d_rope = dims->d_rope;
+  a->dtype = dims->dtype;
+  a->q_cat = q_cat;
+  a->cache.data = static_cast<const uint8_t*>(cache->data);
+  a->cache.seq_lens = cache->seq_lens;
+  a->cache.page_table = cache->page_table;
+  a->cache.page_size = cache->page_table ? cache->page_size : 0;
+  a->cache.max_len = cache->max_len;
+  a->cache.max_pages = cache->page_table ? cache->max_len / cache->page_size : 0;
+  a->softmax_scale = softmax_scale;
+  a->split_tokens = plan_out->split_tokens;
+  a->num_splits = plan_out->num_splits;
+  a->head_groups = plan_out->head_groups;
+  a->out_lat = out_lat;
+  a->lse = lse;
+  a->part_o = static_cast<float*>(const_cast<void*>(workspace));
+  a->part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(workspace)) +
+                                         round256(parts_n * dims->d_latent * sizeof(float)));
+  a->stream = static_cast<hipStream_t>(stream);
+  return MLA_OK;
+}
+
+mla_status_t run_partials(const DecodeArgs& a, const mla_decode_plan_t& plan) {
+  const hipError_t e = plan.kernel == 1 ? mla::launch_partials_mfma(a)
+                                        : mla::launch_partials_generic(a);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status_t run_combine(const DecodeArgs& a, const mla_decode_plan_t& plan) {
+  const hipError_t e = mla::launch_combine(a, plan.kernel == 1);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_decode_partials(const mla_dims_t* dims, int32_t batch, const void* q_cat,
+                                 const mla_cache_t* cache, float softmax_scale,
+                                 const mla_decode_plan_t* plan, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  mla_decode_plan_t p;
+  DecodeArgs a;
+  mla_status_t st = prepare_decode(dims, batch, q_cat, cache, softmax_scale, plan, nullptr,
+                                   nullptr, workspace, workspace_bytes, stream, kPartials, &p,
+                                   &a);
+  if (st != MLA_OK || batch == 0) return st;
+  (void)hipGetLastError();
+  return run_partials(a, p);
+}
+
+mla_status_t mla_decode_combine(const mla_dims_t* dims, int32_t batch, const mla_cache_t* cache,
+                                const mla_decode_plan_t* plan, const void* workspace,
+                                size_t workspace_bytes, void* out_lat, float* lse,
+                                void* stream) {
+  mla_decode_plan_t p;
+  DecodeArgs a;
+  mla_status_t st = prepare_decode(dims, batch, nullptr, cache, 0.f, plan, out_lat, lse,
+                                   workspace, workspace_bytes, stream, kCombine, &p, &a);
+  if (st != MLA_OK || batch == 0) return st;
+  (void)hipGetLastError();
+  return run_combine(a, p);
+}
+
+mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* q_cat,
+                             const mla_cache_t* cache, float softmax_scale,
+                             const mla_decode_plan_t* plan, void* out_lat, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  mla_decode_plan_t p;
+  DecodeArgs a;
+  mla_status_t st = prepare_decode(dims, batch, q_cat, cache, softmax_scale, plan, out_lat, lse,
+                                   workspace, workspace_bytes, stream, kPartials | kCombine,
+                                   &p, &a);
+  if (st != MLA_OK || batch == 0) return st;
+  (void)hipGetLastError();
+  if ((st = run_partials(a, p)) != MLA_OK) return st;
+  return run_combine(a, p);
+}
+
+mla_status_t mla_out_uv(const mla_dims_t* dims, int32_t batch, const void* out_lat,
+                        const void* w_uv, void* out, void* stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0) return MLA_ERR_DIMS;
+  if (batch == 0) return MLA_OK;
+  if (out_lat == nullptr || w_uv == nullptr || out == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(out_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != MLA_OK) return st;
+  (void)hipGetLastError();
+  const hipError_t e = mla::launch_out_uv(dims->dtype, batch, dims->n_heads, dims->d_head,
+                                          dims->d_latent, out_lat, w_uv, out,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,231 @@
+// Generic split-KV latent decode and the split combines.
+//
+// The generic decode serves fp32 storage and any (n_heads, d_latent, d_rope):
+// one workgroup owns one (request, head, split) and walks the split in tiles
+// of 256 tokens.  Scores are the full-row dot product
+//   s_j = scale * q_cat . [c_j | k^R_j]
+// (the absorbed content score plus the decoupled RoPE score, DeepSeek-V2
+// read-through, 2kiu.com/news/6085339, sections 2.3-2.4), the softmax is kept
+// online (running max and sum), and the weighted sum is taken over the latent
+// part of the row only (section 2.3: the weighted sum happens in latent space).
+//
+// Partials are normalised by their own softmax sum and stored with their
+// natural-log sum-exp; the combine merges splits s with weights
+// exp(lse_s - max_s lse_s).
+
+#include "device_common.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxLatentPerThread = 8;  // d_latent <= 2048
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// grid: x = split, y = head, z = request.  Partials row-major:
+// part_o[((b * S + s) * n_heads + i) * d_latent + c], part_lse[(b * S + s) * n_heads + i].
+template <typename T>
+__global__ __launch_bounds__(kThreads) void decode_generic_kernel(
+    const T* __restrict__ q_cat, CacheView cache, int n_heads, int d_latent, int d_rope,
+    float scale, int split_tokens, int num_splits, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
+  extern __shared__ float sm[];
+  const int row = d_latent + d_rope;
+  float* q_s = sm;                 // [row]
+  float* p_s = sm + row;           // [kThreads]
+  float* red = p_s + kThreads;     // [4]
+  const int s = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+  const int len = cache.seq_lens[b];
+  const int t0 = s * split_tokens;
+  const int t1 = min(t0 + split_tokens, len);
+  if (t0 >= t1) return;  // the combine never reads splits past the length
+
+  const T* q = q_cat + (static_cast<size_t>(b) * n_heads + i) * row;
+  for (int k = threadIdx.x; k < row; k += kThreads) q_s[k] = ld(q + k);
+  __syncthreads();
+
+  float m = -INFINITY, l = 0.f;
+  float o[kMaxLatentPerThread];
+#pragma unroll
+  for (int r = 0; r < kMaxLatentPerThread; ++r) o[r] = 0.f;
+  const int row_bytes = row * static_cast<int>(sizeof(T));
+
+  for (int tile = t0; tile < t1; tile += kThreads) {
+    const int j = tile + threadIdx.x;
+    float sj = -INFINITY;
+    if (j < t1) {
+      const T* rp = reinterpret_cast<const T*>(cache_row(cache, b, j, row_bytes));
+      float dot = 0.f;
+      for (int k = 0; k < row; ++k) dot = fmaf(q_s[k], ld(rp + k), dot);
+      sj = dot * scale;
+    }
+    const float tmax = block_max(sj, red);
+    const float m_new = fmaxf(m, tmax);
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
+    const float pj = (j < t1) ? expf(sj - m_new) : 0.f;
+    p_s[threadIdx.x] = pj;
+    const float psum = block_sum(pj, red);  // its barriers also publish p_s
+    l = l * alpha + psum;
+    m = m_new;
+    const int nt = min(kThreads, t1 - tile);
+#pragma unroll
+    for (int r = 0; r < kMaxLatentPerThread; ++r) {
+      const int c = threadIdx.x + r * kThreads;
+      if (c < d_latent) {
+        float acc = o[r] * alpha;
+        for (int jj = 0; jj < nt; ++jj) {
+          const T* rp = reinterpret_cast<const T*>(cache_row(cache, b, tile + jj, row_bytes));
+          acc = fmaf(p_s[jj], ld(rp + c), acc);
+        }
+        o[r] = acc;
+      }
+    }
+    __syncthreads();  // p_s is rewritten by the next tile
+  }
+
+  const float inv = 1.f / l;
+  const size_t base = (static_cast<size_t>(b) * num_splits + s) * n_heads + i;
+#pragma unroll
+  for (int r = 0; r < kMaxLatentPerThread; ++r) {
+    const int c = threadIdx.x + r * kThreads;
+    if (c < d_latent) part_o[base * d_latent + c] = o[r] * inv;
+  }
+  if (threadIdx.x == 0) part_lse[base] = m + logf(l);
+}
+
+// Number of splits that hold tokens of a request of length len.
+__device__ __forceinline__ int used_splits(int len, int split_tokens) {
+  return len > 0 ? (len + split_tokens - 1) / split_tokens : 0;
+}
+
+// Combine for row-major partials.  grid: x = head, y = request.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_rowmajor_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const int32_t* __restrict__ seq_lens, int n_heads, int d_latent, int split_tokens,
+    int num_splits, T* __restrict__ out_lat, float* __restrict__ lse_out) {
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int ns = used_splits(seq_lens[b], split_tokens);
+  const size_t obase = (static_cast<size_t>(b) * n_heads + i) * d_latent;
+  const size_t pbase = static_cast<size_t>(b) * num_splits * n_heads + i;
+  float L = -INFINITY;
+  for (int s = 0; s < ns; ++s) L = fmaxf(L, part_lse[pbase + static_cast<size_t>(s) * n_heads]);
+  float W = 0.f;
+  for (int s = 0; s < ns; ++s) W += expf(part_lse[pbase + static_cast<size_t>(s) * n_heads] - L);
+  const float invW = ns > 0 ? 1.f / W : 0.f;
+  for (int c = threadIdx.x; c < d_latent; c += kThreads) {
+    float acc = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const size_t ps = pbase + static_cast<size_t>(s) * n_heads;
+      acc = fmaf(expf(part_lse[ps] - L), part_o[ps * d_latent + c], acc);
+    }
+    st(out_lat + obase + c, acc * invW);
+  }
+  if (lse_out != nullptr && threadIdx.x == 0)
+    lse_out[static_cast<size_t>(b) * n_heads + i] = ns > 0 ? L + logf(W) : -INFINITY;
+}
+
+}  // namespace
+
+// Combine for fragment-order partials written by the MFMA decode kernel.
+// Fragment layout, per (request b, split s, 32-head block hb):
+//   part_o[(((b * S + s) * NHB + hb) * 256 + cb * 16 + v) * 64 + lane]
+//     = O[head hb*32 + lane%32][latent cb*32 + (v/4)*8 + (lane/32)*4 + v%4]
+// grid: x = 32-head block, y = request; 256 threads, wave w handles latent
+// blocks cb = 4w .. 4w+3.
+__global__ __launch_bounds__(kThreads) void combine_fragment_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const int32_t* __restrict__ seq_lens, int n_heads, int split_tokens, int num_splits,
+    __bf16* __restrict__ out_lat, float* __restrict__ lse_out) {
+  const int hb = blockIdx.x, b = blockIdx.y;
+  const int nhb = n_heads / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int head = hb * 32 + (lane & 31), half = lane >> 5;
+  const int ns = used_splits(seq_lens[b], split_tokens);
+  const size_t lbase = static_cast<size_t>(b) * num_splits * n_heads + head;
+  float L = -INFINITY;
+  for (int s = 0; s < ns; ++s) L = fmaxf(L, part_lse[lbase + static_cast<size_t>(s) * n_heads]);
+  float W = 0.f;
+  for (int s = 0; s < ns; ++s) W += expf(part_lse[lbase + static_cast<size_t>(s) * n_heads] - L);
+  const float invW = ns > 0 ? 1.f / W : 0.f;
+
+  __bf16* orow = out_lat + static_cast<size_t>(b * n_heads + head) * 512;
+  for (int cb = wave * 4; cb < wave * 4 + 4; ++cb) {
+    float acc[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float w = expf(part_lse[lbase + static_cast<size_t>(s) * n_heads] - L);
+      const float* frag =
+          part_o + ((static_cast<size_t>(b) * num_splits + s) * nhb + hb) * 16384 + cb * 1024;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = fmaf(w, frag[v * 64 + lane], acc[v]);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4_t pk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pk[r] = static_cast<__bf16>(acc[g * 4 + r] * invW);
+      *reinterpret_cast<bf16x4_t*>(orow + cb * 32 + g * 8 + half * 4) = pk;
+    }
+  }
+  if (lse_out != nullptr && wave == 0 && half == 0)
+    lse_out[static_cast<size_t>(b) * n_heads + head] = ns > 0 ? L + logf(W) : -INFINITY;
+}
+
+hipError_t launch_partials_generic(const DecodeArgs& a) {
+  if (a.batch == 0) return hipSuccess;
+  const int row = a.d_latent + a.d_rope;
+  const size_t lds = sizeof(float) * (row + kThreads + 4);
+  const dim3 grid(a.num_splits, a.n_heads, a.batch);
+  if (a.dtype == 0) {
+    decode_generic_kernel<float><<<grid, kThreads, lds, a.stream>>>(
+        static_cast<const float*>(a.q_cat), a.cache, a.n_heads, a.d_latent, a.d_rope,
+        a.softmax_scale, a.split_tokens, a.num_splits, a.part_o, a.part_lse);
+  } else {
+    decode_generic_kernel<__bf16><<<grid, kThreads, lds, a.stream>>>(
+        static_cast<const __bf16*>(a.q_cat), a.cache, a.n_heads, a.d_latent, a.d_rope,
+        a.softmax_scale, a.split_tokens, a.num_splits, a.part_o, a.part_lse);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeArgs& a, bool fragment) {
+  if (a.batch == 0) return hipSuccess;
+  if (fragment) {
+    combine_fragment_kernel<<<dim3(a.n_heads / 32, a.batch), kThreads, 0, a.stream>>>(
+        a.part_o, a.part_lse, a.cache.seq_lens, a.n_heads, a.split_tokens, a.num_splits,
+        static_cast<__bf16*>(a.out_lat), a.lse);
+    return hipGetLastError();
+  }
+  const dim3 cgrid(a.n_heads, a.batch);
+  if (a.dtype == 0) {
+    combine_rowmajor_kernel<float><<<cgrid, kThreads, 0, a.stream>>>(
+        a.part_o, a.part_lse, a.cache.seq_lens, a.n_heads, a.d_latent, a.split_tokens,
+        a.num_splits, static_cast<float*>(a.out_lat), a.lse);
+  } else {
+    combine_rowmajor_kernel<__bf16><<<cgrid, kThreads, 0, a.stream>>>(
+        a.part_o, a.part_lse, a.cache.seq_lens, a.n_heads, a.d_latent, a.split_tokens,
+        a.num_splits, static_cast<__bf16*>(a.out_lat), a.lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

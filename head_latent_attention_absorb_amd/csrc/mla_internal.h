@@ -1,0 +1,63 @@
+// Internal declarations shared by the kernels and the C-ABI layer.
+// Nothing here is part of the public ABI (include/mla_absorb.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Split-KV partial results of the decode kernels live in the caller's
+// workspace: fp32 partial outputs (normalised by their own softmax sum) and
+// fp32 natural-log sum-exp per (request, split, head).
+struct PartialLayout {
+  enum Kind { kRowMajor = 0, kFragment = 1 };
+};
+
+struct CacheView {
+  const uint8_t* data;      // cache rows, (d_latent + d_rope) elements each
+  const int32_t* seq_lens;  // [batch]
+  const int32_t* page_table;  // [batch, max_pages] or nullptr
+  int32_t page_size;        // 0 => contiguous
+  int32_t max_len;
+  int32_t max_pages;        // max_len / page_size when paged
+};
+
+struct DecodeArgs {
+  int32_t batch, n_heads, d_latent, d_rope, dtype;
+  const void* q_cat;
+  CacheView cache;
+  float softmax_scale;
+  int32_t split_tokens, num_splits, head_groups;
+  void* out_lat;
+  float* lse;           // may be nullptr
+  float* part_o;        // workspace
+  float* part_lse;      // workspace
+  hipStream_t stream;
+};
+
+// Launchers return the hipError_t of the launch (hipSuccess when nothing
+// needed launching).
+hipError_t launch_absorb_q(int dtype, int batch, int n_heads, int d_head, int d_rope,
+                           int d_latent, const void* q_c, const void* q_r,
+                           const void* w_uk, void* q_cat, hipStream_t stream);
+hipError_t launch_out_uv(int dtype, int batch, int n_heads, int d_head, int d_latent,
+                         const void* out_lat, const void* w_uv, void* out,
+                         hipStream_t stream);
+
+// Generic split-KV partials (fp32 VALU arithmetic, any dims, fp32 or bf16
+// storage), row-major partial layout.
+hipError_t launch_partials_generic(const DecodeArgs& a);
+// bf16 MFMA split-KV partials for d_latent = 512, d_rope = 64,
+// n_heads % 64 == 0, fragment-order partial layout.
+hipError_t launch_partials_mfma(const DecodeArgs& a);
+// Merge the partials of each request into out_lat / lse.  `fragment` selects
+// the partial layout written by the MFMA kernel.
+hipError_t launch_combine(const DecodeArgs& a, bool fragment);
+
+// Constants of the MFMA decode kernel that the planner needs.
+constexpr int kMfmaHeadsPerGroup = 64;   // heads handled by one workgroup
+constexpr int kMfmaTokenGranule = 32;    // tokens consumed per workgroup iteration
+
+}  // namespace mla

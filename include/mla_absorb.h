@@ -1,0 +1,183 @@
+/*
+ * mla_absorb.h -- C ABI of the MI355X (gfx950) library for DeepSeek-V2
+ * Multi-head Latent Attention decode with matrix absorption.
+ *
+ * What is computed (sources cited by page title and section):
+ *   Every request caches, per token and layer, only the joint K/V latent
+ *   c^KV (width d_c) and the shared, already-rotated RoPE key k^R (width
+ *   d_h^R), stored as one row [c^KV | k^R]  (DeepSeek-V3 technical report
+ *   read-through, 2kiu.com/news/6340724, sections 2.2 and 2.4; DeepSeek-V2
+ *   read-through, 2kiu.com/news/6085339, section 5.1).
+ *   W^UK is absorbed into the query, q_lat,i = W^UK_i^T q^C_i, so scores are
+ *   taken directly against the cached row; the softmax-weighted sum stays in
+ *   latent space and W^UV is applied last  (V2 read-through, section 2.3;
+ *   zeeklog "Transformer 15: DeepSeek-V2 architecture", equations 9-11 and
+ *   the absorption paragraph after them).
+ *   A decode step of one layer is three calls:
+ *     mla_absorb_q    q_cat[b,i] = [ W^UK_i^T q^C[b,i] | q^R[b,i] ]
+ *     mla_decode_attn o_lat[b,i] = sum_j softmax_j(scale * q_cat[b,i] . row_j) c_j
+ *     mla_out_uv      o[b,i,h]   = sum_c o_lat[b,i,c] W^UV[i,c,h]
+ *
+ * Conventions shared by every call:
+ *   - Every pointer to tensor data is a DEVICE pointer (HIP memory on the
+ *     current device), unless the argument says "host".  The caller owns and
+ *     frees all memory, including the workspace; the library never allocates
+ *     device memory and never synchronises the stream.
+ *   - Tensors are dense, row-major, innermost dimension contiguous.  Float
+ *     tensors use the storage type dims->dtype (fp32 or bf16); lse, split
+ *     partials and all accumulation are fp32.  Integer tensors are int32.
+ *   - Device pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued asynchronously on it; pointers must stay valid
+ *     until that work completes.
+ *   - Arguments are checked on the host before anything is enqueued; on
+ *     failure a non-zero status is returned and nothing is launched.  A
+ *     launch the runtime rejects returns MLA_ERR_LAUNCH.  Device-side data
+ *     (seq_lens, page_table) is trusted: values outside the documented
+ *     ranges are undefined behaviour.
+ *   - Calls on different streams may run concurrently; the library keeps no
+ *     mutable global state apart from a per-device property cache.
+ */
+#ifndef MLA_ABSORB_H
+#define MLA_ABSORB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  MLA_ERR_DIMS = 2,      /* a size is out of range or sizes are inconsistent  */
+  MLA_ERR_DTYPE = 3,     /* unsupported storage type                          */
+  MLA_ERR_WORKSPACE = 4, /* workspace NULL or smaller than the plan needs     */
+  MLA_ERR_ALIGN = 5,     /* a device pointer is not 16-byte aligned           */
+  MLA_ERR_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch          */
+  MLA_ERR_DEVICE = 7     /* no current HIP device, or it is not gfx950        */
+} mla_status_t;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
+
+/* Model dimensions of one MLA layer (DeepSeek-V2: 128, 128, 64, 512; zeeklog
+ * notes, the remark under the cache table: d_c = 4 d_h, d_h^R = d_h / 2). */
+typedef struct {
+  int32_t n_heads;  /* n_h, 1..1024                                        */
+  int32_t d_head;   /* d_h, content width per head, 1..1024                */
+  int32_t d_rope;   /* d_h^R, width of q^R and of the shared k^R, 0..1024  */
+  int32_t d_latent; /* d_c, width of c^KV, 1..2048                         */
+  int32_t dtype;    /* mla_dtype_t: storage type of every float tensor     */
+} mla_dims_t;
+
+/* The latent cache of one layer.  Row = d_latent + d_rope elements,
+ * [c^KV | k^R].  Rows [0, seq_lens[b]) of request b are attended; the
+ * current token's row must already be appended (the query attends positions
+ * 1..t, zeeklog notes, decode paragraphs). */
+typedef struct {
+  const void* data;          /* contiguous: [batch, max_len, row];
+                                paged:      [num_pages, page_size, row]        */
+  const int32_t* seq_lens;   /* device [batch], each in [0, max_len]           */
+  const int32_t* page_table; /* device [batch, max_len / page_size] physical
+                                page ids in [0, num_pages); NULL = contiguous  */
+  int32_t page_size;         /* tokens per page (paged only; 0 = contiguous)   */
+  int32_t max_len;           /* host-known bound on every seq_lens[b]; the row
+                                stride between requests of a contiguous cache;
+                                a multiple of page_size when paged            */
+  int64_t num_pages;         /* paged: pages in the pool; ignored otherwise    */
+} mla_cache_t;
+
+/* Split-KV plan: each request's tokens are cut into partitions of
+ * split_tokens tokens that run on different compute units and are merged by
+ * their log-sum-exp weights.  Produced by mla_decode_plan. */
+typedef struct {
+  int32_t split_tokens;   /* tokens per partition                              */
+  int32_t num_splits;     /* partitions per request, ceil(max_len/split_tokens) */
+  int32_t kernel;         /* 0 = generic fp32-VALU kernel, 1 = bf16 MFMA kernel */
+  int32_t head_groups;    /* heads are processed in this many groups           */
+  size_t workspace_bytes; /* device bytes mla_decode_attn needs                */
+} mla_decode_plan_t;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* mla_status_str(mla_status_t status);
+
+/* Library ABI version (incremented on any signature change). */
+int32_t mla_abi_version(void);
+
+/* Absorb W^UK into the query (V2 read-through section 2.3; V3 read-through
+ * section 2.3):
+ *   q_cat[b, i, c]       = sum_h q_c[b, i, h] * w_uk[i, h, c]   (c < d_latent)
+ *   q_cat[b, i, d_c + r] = q_r[b, i, r]                          (r < d_rope)
+ * q_c  [batch, n_heads, d_head], q_r [batch, n_heads, d_rope],
+ * w_uk [n_heads, d_head, d_latent] (head i's d_h x d_c block of W^UK),
+ * q_cat [batch, n_heads, d_latent + d_rope] (output; mirrors the cache row).
+ * Accumulates in fp32; the result is rounded once to dims->dtype.
+ * batch 0 is a no-op returning MLA_OK. */
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch, const void* q_c,
+                          const void* q_r, const void* w_uk, void* q_cat, void* stream);
+
+/* Choose the split-KV plan for mla_decode_attn on the current device.
+ * split_tokens = 0 lets the library choose; otherwise the value is rounded up
+ * to the kernel's tile granule (32 tokens for the MFMA kernel, 1 otherwise)
+ * and capped at max_len rounded up to that granule.
+ * `plan` is a host pointer that receives the result. */
+mla_status_t mla_decode_plan(const mla_dims_t* dims, int32_t batch, const mla_cache_t* cache,
+                             int32_t split_tokens, mla_decode_plan_t* plan);
+
+/* Latent-space decode attention over the cache (V2 read-through section 2.3:
+ * scores against the cached latent, weighted sum in latent space; zeeklog MHA
+ * equation for the softmax):
+ *   s[b,i,j]     = softmax_scale * q_cat[b,i,:] . row_j(b)[:]   (j < seq_lens[b])
+ *   out_lat[b,i] = sum_j softmax_j(s[b,i,:]) * row_j(b)[0:d_latent]
+ *   lse[b,i]     = ln sum_j exp(s[b,i,j])
+ * q_cat [batch, n_heads, d_latent + d_rope]; out_lat [batch, n_heads,
+ * d_latent] (dims->dtype); lse [batch, n_heads] fp32, may be NULL.
+ * A request with seq_lens[b] == 0 yields out_lat = 0 and lse = -inf.
+ * `plan` (host pointer) may be NULL: the library plans with split_tokens = 0.
+ * A plan passed in must come from mla_decode_plan with the same dims, batch
+ * and cache bounds.  workspace: device, >= plan->workspace_bytes, 256-byte
+ * aligned, contents need no initialisation; calls that share a workspace
+ * must be ordered on one stream. */
+mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* q_cat,
+                             const mla_cache_t* cache, float softmax_scale,
+                             const mla_decode_plan_t* plan, void* out_lat, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two phases of mla_decode_attn, for callers that merge partial results
+ * themselves (for example across devices that each hold a slice of a long
+ * cache) or time them separately.  mla_decode_attn(...) is exactly
+ * mla_decode_partials(...) followed by mla_decode_combine(...) on the same
+ * stream with the same plan and workspace.
+ *
+ * mla_decode_partials: for every request b, split s and head i with tokens in
+ *   [s*split_tokens, min((s+1)*split_tokens, seq_lens[b])), writes into the
+ *   workspace the split's softmax-normalised latent sum and its natural-log
+ *   sum-exp (fp32).  The workspace layout is private to the library and
+ *   depends on plan->kernel.  Splits with no tokens are not written.
+ * mla_decode_combine: merges the used splits of each request with weights
+ *   exp(lse_s - max_s lse_s) into out_lat (dims->dtype) and lse (fp32, may be
+ *   NULL); it reads only seq_lens from `cache` (data may be NULL).
+ * Arguments, errors and the plan rule are those of mla_decode_attn. */
+mla_status_t mla_decode_partials(const mla_dims_t* dims, int32_t batch, const void* q_cat,
+                                 const mla_cache_t* cache, float softmax_scale,
+                                 const mla_decode_plan_t* plan, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+mla_status_t mla_decode_combine(const mla_dims_t* dims, int32_t batch, const mla_cache_t* cache,
+                                const mla_decode_plan_t* plan, const void* workspace,
+                                size_t workspace_bytes, void* out_lat, float* lse,
+                                void* stream);
+
+/* Apply W^UV after the latent-space sum (V2 read-through section 2.3):
+ *   out[b, i, h] = sum_c out_lat[b, i, c] * w_uv[i, c, h]
+ * out_lat [batch, n_heads, d_latent], w_uv [n_heads, d_latent, d_head]
+ * (head i's up-projection stored d_c x d_h), out [batch, n_heads, d_head].
+ * Accumulates in fp32, rounds once to dims->dtype. */
+mla_status_t mla_out_uv(const mla_dims_t* dims, int32_t batch, const void* out_lat,
+                        const void* w_uv, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_ABSORB_H */

@@ -1,0 +1,139 @@
+"""The C ABI: the library loads, exports every symbol include/*.h declares, and
+rejects bad arguments before launching anything."""
+
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_absorb_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(mla_[a-z0-9_]+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = mla.lib()
+    names = _declared_functions()
+    assert {"mla_absorb_q", "mla_decode_attn", "mla_out_uv", "mla_decode_plan"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/ but not exported"
+    assert L.mla_abi_version() == 1
+
+
+def test_status_strings():
+    L = mla.lib()
+    for code in range(8):
+        s = L.mla_status_str(code).decode()
+        assert s.startswith("MLA_")
+    assert L.mla_status_str(99).decode() == "MLA_ERR_UNKNOWN"
+
+
+def test_struct_sizes_match_header():
+    # mla_dims_t: 5 x int32; mla_cache_t: 3 pointers, 2 int32, int64; plan: 4 int32 + size_t.
+    assert ctypes.sizeof(mla.Dims) == 20
+    assert ctypes.sizeof(mla.CacheDesc) == 40
+    assert ctypes.sizeof(mla.Plan) == 24
+
+
+def _dims(**kw):
+    d = dict(n_heads=128, d_head=128, d_rope=64, d_latent=512, dtype=mla.MLA_BF16)
+    d.update(kw)
+    return mla.Dims(d["n_heads"], d["d_head"], d["d_rope"], d["d_latent"], d["dtype"])
+
+
+# Host-side argument checks run before any device query, so they work on a
+# machine without a GPU.
+
+def test_null_and_bad_dims_rejected_on_host():
+    L = mla.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.mla_absorb_q(None, 1, fake, fake, fake, fake, None) == 1          # NULL dims
+    assert L.mla_absorb_q(ctypes.byref(_dims(dtype=7)), 1, fake, fake, fake, fake, None) == 3
+    assert L.mla_absorb_q(ctypes.byref(_dims(n_heads=0)), 1, fake, fake, fake, fake, None) == 2
+    assert L.mla_absorb_q(ctypes.byref(_dims(d_latent=4096)), 1, fake, fake, fake, fake,
+                          None) == 2
+    assert L.mla_absorb_q(ctypes.byref(_dims()), -1, fake, fake, fake, fake, None) == 2
+    assert L.mla_absorb_q(ctypes.byref(_dims()), 0, None, None, None, None, None) == 0
+    assert L.mla_absorb_q(ctypes.byref(_dims()), 2, None, fake, fake, fake, None) == 1
+    assert L.mla_absorb_q(ctypes.byref(_dims()), 2, ctypes.c_void_p(0x1004), fake, fake, fake,
+                          None) == 5
+    assert L.mla_out_uv(ctypes.byref(_dims()), 2, fake, None, fake, None) == 1
+    cache = mla.CacheDesc(0x1000, 0x2000, 0x3000, 0, 64, 1)  # paged without page_size
+    assert L.mla_decode_attn(ctypes.byref(_dims()), 1, fake, ctypes.byref(cache), 1.0, None,
+                             fake, None, fake, 1 << 20, None) == 2
+    cache = mla.CacheDesc(0x1000, 0x2000, None, 0, 64, 0)
+    assert L.mla_decode_attn(ctypes.byref(_dims()), 1, None, ctypes.byref(cache), 1.0, None,
+                             fake, None, fake, 1 << 20, None) == 1
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_no_device_is_reported_without_gpu():
+    L = mla.lib()
+    fake = ctypes.c_void_p(0x1000)
+    st = L.mla_absorb_q(ctypes.byref(_dims()), 1, fake, fake, fake, fake, None)
+    assert st == 7
+
+
+# ----------------------------------------------------------------------------
+# Device-side checks (need the GPU for the device query)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.gpu
+def test_plan_shapes_and_workspace_errors():
+    L = mla.lib()
+    B, T = 16, 4096
+    data = torch.zeros((B, T, 576), dtype=torch.bfloat16, device="cuda")
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    cache = mla.latent_cache(data, lens, 64)
+    plan = mla.decode_plan(128, 512, 64, torch.bfloat16, cache)
+    assert plan.kernel == 1 and plan.head_groups == 2
+    assert plan.split_tokens % 32 == 0 and plan.num_splits * plan.split_tokens >= T
+    assert plan.workspace_bytes >= B * plan.num_splits * 128 * 513 * 4
+    q = torch.zeros((B, 128, 576), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, 128, 512), dtype=torch.bfloat16, device="cuda")
+    ws = mla.workspace_for(plan, "cuda")
+    d = _dims()
+    desc = cache.desc()
+    st = L.mla_decode_attn(ctypes.byref(d), B, q.data_ptr(), ctypes.byref(desc), 0.07,
+                           ctypes.byref(plan), out.data_ptr(), None, ws.data_ptr(),
+                           plan.workspace_bytes - 1, None)
+    assert st == 4
+    st = L.mla_decode_attn(ctypes.byref(d), B, q.data_ptr() + 2, ctypes.byref(desc), 0.07,
+                           ctypes.byref(plan), out.data_ptr(), None, ws.data_ptr(),
+                           plan.workspace_bytes, None)
+    assert st == 5
+    # A plan whose split count does not match its split length is rejected.
+    bad = mla.Plan(plan.split_tokens, plan.num_splits - 1, plan.kernel, plan.head_groups,
+                   plan.workspace_bytes)
+    st = L.mla_decode_attn(ctypes.byref(d), B, q.data_ptr(), ctypes.byref(desc), 0.07,
+                           ctypes.byref(bad), out.data_ptr(), None, ws.data_ptr(),
+                           plan.workspace_bytes, None)
+    assert st == 2
+    torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+def test_generic_and_mfma_plans_selected_by_dims():
+    data = torch.zeros((2, 64, 40), dtype=torch.float32, device="cuda")
+    lens = torch.full((2,), 64, dtype=torch.int32, device="cuda")
+    cache = mla.latent_cache(data, lens, 8)
+    assert mla.decode_plan(4, 32, 8, torch.float32, cache).kernel == 0
+    data = torch.zeros((2, 64, 576), dtype=torch.bfloat16, device="cuda")
+    cache = mla.latent_cache(data, lens, 64)
+    assert mla.decode_plan(128, 512, 64, torch.bfloat16, cache).kernel == 1
+    assert mla.decode_plan(96, 512, 64, torch.bfloat16, cache).kernel == 0
+    assert mla.decode_plan(128, 512, 64, torch.bfloat16, cache, split_tokens=33).split_tokens == 64

@@ -1,0 +1,357 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (fp32 accumulation everywhere): bf16 storage -- relative L2 error
+<= 1e-2 and max abs error <= 2e-2; fp32 storage -- relative L2 error <= 1e-5.
+
+References:
+  * full decode step o  -> oracle.mla_decode_reference (unabsorbed, fp64)
+  * q_cat (absorb)      -> oracle.absorb_query
+  * o_lat, lse (decode) -> oracle.latent_attention, which the oracle pins equal
+                           to the unabsorbed reference with identity W^UK/W^UV
+  * o from o_lat        -> oracle.project_out
+The decode and output steps are also tested on their own with seeded inputs
+(draw_latent_query / draw_latent_output), never with values produced by the
+HIP path.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_absorb_amd as mla
+import oracle
+from tests.gpu_util import DevCase, assert_close, from_dev, max_abs, rel_l2
+from workload import CONFIGS, draw_latent_output, draw_latent_query, make_case
+
+pytestmark = pytest.mark.gpu
+
+DSV2 = CONFIGS["dsv2_b16_t4096"]
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bf16_dev(x: np.ndarray) -> torch.Tensor:
+    from workload import f32_to_bf16_bits
+    return torch.from_numpy(f32_to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _latent_ref(case, q_cat: np.ndarray, requests=None, heads=None):
+    """oracle.latent_attention per request on the given (seeded) absorbed query."""
+    cfg = case.cfg
+    B = cfg.batch
+    reqs = range(B) if requests is None else requests
+    hs = np.arange(cfg.n_heads) if heads is None else np.asarray(heads)
+    o = np.zeros((B, cfg.n_heads, cfg.d_latent))
+    lse = np.full((B, cfg.n_heads), -np.inf)
+    for b in reqs:
+        rows = oracle.gather_rows(case.cache, b, int(case.seq_lens[b]), case.page_table,
+                                  cfg.page_size)
+        o[b, hs], lse[b, hs] = oracle.latent_attention(q_cat[b, hs], rows, cfg.d_latent,
+                                                       cfg.scale)
+    return o, lse
+
+
+def _decode_only(case, dc: DevCase, seed: int, split_tokens=0):
+    q_np = draw_latent_query(case.cfg, seed)
+    q_dev = _bf16_dev(q_np) if case.cfg.dtype == "bf16" else torch.from_numpy(q_np).cuda()
+    o_lat, lse = mla.decode_attn(q_dev, dc.cache, case.cfg.scale, split_tokens=split_tokens)
+    torch.cuda.synchronize()
+    return q_np, from_dev(o_lat), from_dev(lse)
+
+
+# ----------------------------------------------------------------------------
+# Tiny fp32 config: B=1, n_h=4, d_h=16, d_h^R=8, d_c=32, T=64, seeds 0-9
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(10))
+def test_tiny_f32_full_chain(seed):
+    cfg = CONFIGS["tiny_f32"]
+    case = make_case(cfg, seed)
+    _log(f"[tiny_f32] seed={seed}")
+    q_cat, o_lat, lse, o = DevCase(case).run()
+    o_ref, lse_ref = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache,
+                                                 case.seq_lens, case.w_uk, case.w_uv, cfg.scale)
+    assert_close(from_dev(o), o_ref, "f32", "o")
+    assert_close(from_dev(lse), lse_ref, "f32", "lse")
+    assert_close(from_dev(q_cat), oracle.absorb_query(case.q_c, case.q_r, case.w_uk), "f32",
+                 "q_cat")
+
+
+@pytest.mark.parametrize("split", [0, 1, 7, 64])
+def test_tiny_f32_splits(split):
+    cfg = CONFIGS["tiny_f32"]
+    case = make_case(cfg, 3)
+    _log(f"[tiny_f32 splits] split={split}")
+    dc = DevCase(case)
+    q_np, o_lat, lse = _decode_only(case, dc, 3, split_tokens=split)
+    o_ref, lse_ref = _latent_ref(case, q_np)
+    assert_close(o_lat, o_ref, "f32", "o_lat")
+    assert_close(lse, lse_ref, "f32", "lse")
+
+
+# ----------------------------------------------------------------------------
+# DeepSeek-V2 dims at small sizes: several tiles, ragged tails, paging
+# ----------------------------------------------------------------------------
+
+SMALL = DSV2.replace(name="dsv2_small", batch=3, len_lo=1, len_hi=320, max_len=320)
+SMALL_PAGED = DSV2.replace(name="dsv2_small_paged", batch=5, len_lo=1, len_hi=384,
+                           max_len=384, page_size=64)
+
+
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_PAGED], ids=["contiguous", "paged"])
+@pytest.mark.parametrize("split", [0, 32, 64, 96, 320])
+def test_decode_small_bf16(cfg, split):
+    lens = np.array([1, 37, 300, 384, 129][:cfg.batch], np.int32)
+    lens = np.minimum(lens, cfg.max_len)
+    case = make_case(cfg, 11, seq_lens=lens, pad_value=np.nan)
+    _log(f"[decode small] {cfg.name} split={split} lens={lens.tolist()}")
+    dc = DevCase(case)
+    q_np, o_lat, lse = _decode_only(case, dc, 11, split_tokens=split)
+    o_ref, lse_ref = _latent_ref(case, q_np)
+    assert np.isfinite(o_lat).all() and np.isfinite(lse).all()
+    assert_close(o_lat, o_ref, "bf16", "o_lat")
+    assert_close(lse, lse_ref, "bf16", "lse")
+
+
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_PAGED], ids=["contiguous", "paged"])
+def test_chain_small_bf16(cfg):
+    case = make_case(cfg, 5)
+    _log(f"[chain small] {cfg.name} lens={case.seq_lens.tolist()}")
+    q_cat, o_lat, lse, o = DevCase(case).run()
+    o_ref, lse_ref = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
+                                                 case.w_uk, case.w_uv, cfg.scale,
+                                                 case.page_table, cfg.page_size)
+    assert_close(from_dev(o), o_ref, "bf16", "o")
+    assert_close(from_dev(lse), lse_ref, "bf16", "lse")
+    assert_close(from_dev(q_cat), oracle.absorb_query(case.q_c, case.q_r, case.w_uk), "bf16",
+                 "q_cat")
+
+
+def test_absorb_q_bf16_b16():
+    cfg = DSV2.replace(len_lo=1, len_hi=1, max_len=1)
+    case = make_case(cfg, 2)
+    dc = DevCase(case)
+    q_cat = mla.absorb_q(dc.q_c, dc.q_r, dc.w_uk)
+    torch.cuda.synchronize()
+    assert_close(from_dev(q_cat), oracle.absorb_query(case.q_c, case.q_r, case.w_uk), "bf16",
+                 "q_cat")
+
+
+@pytest.mark.parametrize("batch", [1, 16, 128])
+def test_out_uv_bf16(batch):
+    cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1)
+    case = make_case(cfg, 4)
+    o_lat_np = draw_latent_output(cfg, 4)
+    o = mla.out_uv(_bf16_dev(o_lat_np), DevCase(case).w_uv)
+    torch.cuda.synchronize()
+    assert_close(from_dev(o), oracle.project_out(o_lat_np, case.w_uv), "bf16", "o")
+
+
+# ----------------------------------------------------------------------------
+# Edge cases and invariants
+# ----------------------------------------------------------------------------
+
+def test_zero_length_requests():
+    cfg = SMALL
+    lens = np.array([0, 40, 0], np.int32)
+    case = make_case(cfg, 6, seq_lens=lens, pad_value=np.nan)
+    dc = DevCase(case)
+    q_np, o_lat, lse = _decode_only(case, dc, 6)
+    assert np.all(o_lat[0] == 0) and np.all(o_lat[2] == 0)
+    assert np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2]))
+    o_ref, lse_ref = _latent_ref(case, q_np, requests=[1])
+    assert_close(o_lat[1], o_ref[1], "bf16", "o_lat[1]")
+
+
+def test_single_token_request_equals_row():
+    """T = 1: the output is the cached latent itself, for every head."""
+    cfg = SMALL.replace(batch=1)
+    case = make_case(cfg, 8, seq_lens=np.array([1], np.int32))
+    dc = DevCase(case)
+    _, o_lat, _ = _decode_only(case, dc, 8)
+    row = case.cache[0, 0, :cfg.d_latent]
+    assert np.array_equal(o_lat[0], np.broadcast_to(row, o_lat[0].shape))
+
+
+def test_page_permutation_is_bitwise_invariant():
+    cfg = SMALL_PAGED
+    case = make_case(cfg, 9)
+    dc = DevCase(case)
+    q_np, o1, l1 = _decode_only(case, dc, 9, split_tokens=64)
+    # Move every page to a new physical slot.
+    perm = np.random.default_rng(1).permutation(case.cache.shape[0])
+    pool2 = np.empty_like(case.cache)
+    pool2[perm] = case.cache
+    case2 = make_case(cfg, 9)
+    case2.cache = pool2
+    case2.page_table = perm[case.page_table].astype(np.int32)
+    _, o2, l2 = _decode_only(case2, DevCase(case2), 9, split_tokens=64)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_paged_equals_contiguous_bitwise():
+    cfg = SMALL_PAGED
+    case = make_case(cfg, 12)
+    q_np, o_p, l_p = _decode_only(case, DevCase(case), 12, split_tokens=64)
+    cont = np.zeros((cfg.batch, cfg.max_len, cfg.row), np.float32)
+    for b in range(cfg.batch):
+        n = int(case.seq_lens[b])
+        cont[b, :n] = case.cache.reshape(-1, cfg.row)[case.logical_row_index(b)]
+    case_c = make_case(cfg.replace(page_size=0), 12)
+    case_c.cache = cont
+    case_c.seq_lens = case.seq_lens
+    case_c.page_table = None
+    _, o_c, l_c = _decode_only(case_c, DevCase(case_c), 12, split_tokens=64)
+    assert np.array_equal(o_p, o_c) and np.array_equal(l_p, l_c)
+
+
+def test_request_independence_and_determinism():
+    cfg = SMALL
+    case = make_case(cfg, 13)
+    dc = DevCase(case)
+    _, o1, l1 = _decode_only(case, dc, 13)
+    _, o2, l2 = _decode_only(case, dc, 13)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # Request 0 alone gives bitwise the same result as inside the batch.
+    case1 = make_case(cfg.replace(batch=1), 13)
+    case1.cache = case.cache[:1].copy()
+    case1.seq_lens = case.seq_lens[:1].copy()
+    q_full = draw_latent_query(cfg, 13)
+    q_dev = _bf16_dev(q_full[:1])
+    dc1 = DevCase(case1)
+    o_lat, lse = mla.decode_attn(q_dev, dc1.cache, cfg.scale,
+                                 split_tokens=mla.decode_plan(128, 512, 64, torch.bfloat16,
+                                                              dc.cache).split_tokens)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(o_lat)[0], o1[0])
+
+
+def test_large_scores_rescale_path():
+    """Scores that keep growing along the sequence (by ~30 in natural-log units
+    over 300 tokens) push later tiles far past the running max, exercising the
+    accumulator rescale; the result must still match."""
+    cfg = SMALL
+    lens = np.array([300, 300, 300], np.int32)
+    case = make_case(cfg, 14, seq_lens=lens)
+    from workload import round_to_bf16
+    q_np = round_to_bf16((draw_latent_query(cfg, 14) * 8.0).astype(np.float32))
+    for b in range(cfg.batch):
+        ramp = (np.arange(300, dtype=np.float32) / 1000.0)[:, None]
+        case.cache[b, :300, :cfg.d_latent] += ramp * np.sign(q_np[b, 0, :cfg.d_latent])
+    case.cache = round_to_bf16(case.cache)
+    dc = DevCase(case)
+    o_lat, lse = mla.decode_attn(_bf16_dev(q_np), dc.cache, cfg.scale, split_tokens=320)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _latent_ref(case, q_np)
+    # Head 0 of every request is the one whose scores ramp up.
+    assert lse_ref[:, 0].min() > lse_ref[:, 1:].max() - 5
+    # These outputs reach |o| ~ 4.4, where one bf16 ulp is 2^-6: the absolute
+    # bound (stated for unit-scale data) is scaled by max|o|.
+    got = from_dev(o_lat)
+    scale = max(1.0, float(np.abs(o_ref).max()))
+    assert rel_l2(got, o_ref) <= 1e-2
+    assert max_abs(got, o_ref) <= 2e-2 * scale
+    assert_close(from_dev(lse), lse_ref, "bf16", "lse")
+
+
+# ----------------------------------------------------------------------------
+# Full-size configurations
+# ----------------------------------------------------------------------------
+
+def test_dsv2_b16_t4096_full():
+    cfg = DSV2
+    _log("[dsv2_b16_t4096] generating")
+    case = make_case(cfg, 0)
+    dc = DevCase(case)
+    q_np, o_lat, lse = _decode_only(case, dc, 0)
+    _log("[dsv2_b16_t4096] decode done; oracle on every request and head")
+    o_ref, lse_ref = _latent_ref(case, q_np)
+    r, m = assert_close(o_lat, o_ref, "bf16", "o_lat")
+    assert_close(lse, lse_ref, "bf16", "lse")
+    _log(f"[dsv2_b16_t4096] o_lat rel_l2={r:.2e} max_abs={m:.2e}")
+    # Whole decode step on sampled (request, head) pairs against the unabsorbed form.
+    _, _, _, o = dc.run()
+    heads = [0, 37, 64, 127]
+    reqs = [0, 9, 15]
+    o_ref, _ = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
+                                           case.w_uk, case.w_uv, cfg.scale,
+                                           requests=reqs, heads=heads)
+    got = from_dev(o)[np.ix_(reqs, heads)]
+    assert_close(got, o_ref[np.ix_(reqs, heads)], "bf16", "o (sampled)")
+
+
+def test_dsv2_b16_t4096_seed1_chain_sampled():
+    cfg = DSV2
+    case = make_case(cfg, 1)
+    _, o_lat, lse, o = DevCase(case).run()
+    heads = [3, 100]
+    reqs = [4, 11]
+    o_ref, lse_ref = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
+                                                 case.w_uk, case.w_uv, cfg.scale,
+                                                 requests=reqs, heads=heads)
+    assert_close(from_dev(o)[np.ix_(reqs, heads)], o_ref[np.ix_(reqs, heads)], "bf16", "o")
+    assert_close(from_dev(lse)[np.ix_(reqs, heads)], lse_ref[np.ix_(reqs, heads)], "bf16",
+                 "lse")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ragged_b4_long(seed):
+    cfg = CONFIGS["ragged_b4_16k_32k"]
+    case = make_case(cfg, seed, pad_value=np.nan)
+    _log(f"[ragged_b4] seed={seed} lens={case.seq_lens.tolist()}")
+    dc = DevCase(case)
+    q_np, o_lat, lse = _decode_only(case, dc, seed)
+    assert np.isfinite(o_lat).all()
+    heads = np.arange(0, 128, 4)
+    o_ref, lse_ref = _latent_ref(case, q_np, heads=heads)
+    assert_close(o_lat[:, heads], o_ref[:, heads], "bf16", "o_lat")
+    assert_close(lse[:, heads], lse_ref[:, heads], "bf16", "lse")
+    _, _, _, o = dc.run()
+    o_ref, _ = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
+                                           case.w_uk, case.w_uv, cfg.scale, requests=[0, 3],
+                                           heads=[5, 77])
+    assert_close(from_dev(o)[np.ix_([0, 3], [5, 77])], o_ref[np.ix_([0, 3], [5, 77])], "bf16",
+                 "o (sampled)")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_paged_b128(seed):
+    cfg = CONFIGS["paged_b128_t2048"]
+    case = make_case(cfg, seed, pad_value=np.nan)
+    _log(f"[paged_b128] seed={seed}")
+    dc = DevCase(case)
+    q_np, o_lat, lse = _decode_only(case, dc, seed)
+    assert np.isfinite(o_lat).all()
+    reqs = list(range(0, 128, 8)) + [int(np.argmin(case.seq_lens)), int(np.argmax(case.seq_lens))]
+    o_ref, lse_ref = _latent_ref(case, q_np, requests=reqs)
+    assert_close(o_lat[reqs], o_ref[reqs], "bf16", "o_lat")
+    assert_close(lse[reqs], lse_ref[reqs], "bf16", "lse")
+    _, _, _, o = dc.run()
+    o_ref, _ = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
+                                           case.w_uk, case.w_uv, cfg.scale, case.page_table,
+                                           cfg.page_size, requests=reqs[:4], heads=[1, 90])
+    assert_close(from_dev(o)[np.ix_(reqs[:4], [1, 90])], o_ref[np.ix_(reqs[:4], [1, 90])],
+                 "bf16", "o (sampled)")
+
+
+@pytest.mark.parametrize("layer", [0, 59])
+def test_ctx128k_layer(layer):
+    cfg = CONFIGS["ctx128k_b2_60l"]
+    _log(f"[ctx128k] layer={layer} generating")
+    case = make_case(cfg, 1000 + layer)
+    dc = DevCase(case)
+    q_np, o_lat, lse = _decode_only(case, dc, 1000 + layer)
+    heads = [0, 31, 64, 127]
+    _log(f"[ctx128k] layer={layer} oracle")
+    o_ref, lse_ref = _latent_ref(case, q_np, heads=heads)
+    assert_close(o_lat[:, heads], o_ref[:, heads], "bf16", "o_lat")
+    assert_close(lse[:, heads], lse_ref[:, heads], "bf16", "lse")
+    _, _, _, o = dc.run()
+    o_ref, _ = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
+                                           case.w_uk, case.w_uv, cfg.scale, heads=[7, 99])
+    assert_close(from_dev(o)[:, [7, 99]], o_ref[:, [7, 99]], "bf16", "o (sampled)")

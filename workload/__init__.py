@@ -11,6 +11,8 @@ from .gen import (  # noqa: F401
     Case,
     WorkloadConfig,
     bf16_bits_to_f32,
+    draw_latent_output,
+    draw_latent_query,
     f32_to_bf16_bits,
     make_case,
     round_to_bf16,

@@ -223,3 +223,24 @@ def make_case(cfg: WorkloadConfig, seed: int, *, pad_value: float = 0.0,
         flat[idx, dc:] = k_r[start:start + n]
         start += n
     return case
+
+
+def draw_latent_query(cfg: WorkloadConfig, seed: int, batch: Optional[int] = None) -> np.ndarray:
+    """Seeded stand-in for an absorbed query [B, n_h, d_c + d_h^R], used to
+    test the decode step on its own.  The latent part is N(0, d_h / d_c) (the
+    variance an absorbed query has when q^C ~ N(0,1) and W^UK ~ N(0, 1/d_c));
+    the RoPE part is N(0, 1).  Rounded to bf16 for bf16 configs."""
+    rng = np.random.Generator(np.random.PCG64(seed ^ 0x5EED0001))
+    B = cfg.batch if batch is None else batch
+    lat = _draw(rng, (B, cfg.n_heads, cfg.d_latent), math.sqrt(cfg.d_head / cfg.d_latent),
+                cfg.dtype)
+    rope = _draw(rng, (B, cfg.n_heads, cfg.d_rope), 1.0, cfg.dtype)
+    return np.concatenate([lat, rope], axis=2)
+
+
+def draw_latent_output(cfg: WorkloadConfig, seed: int, batch: Optional[int] = None) -> np.ndarray:
+    """Seeded stand-in for a latent-space attention output [B, n_h, d_c],
+    N(0, 1), used to test the W^UV projection on its own."""
+    rng = np.random.Generator(np.random.PCG64(seed ^ 0x5EED0002))
+    B = cfg.batch if batch is None else batch
+    return _draw(rng, (B, cfg.n_heads, cfg.d_latent), 1.0, cfg.dtype)
