@@ -4,7 +4,7 @@
 #include <mutex>
 #include <string.h>
 
-#include "../../include/mla_absorb.h"
+#include "mla_absorb.h"
 #include "mla_internal.h"
 
 namespace {
@@ -51,9 +51,10 @@ mla_status_t check_dims(const mla_dims_t* d) {
   return MLA_OK;
 }
 
-bool use_mfma(const mla_dims_t* d) {
+bool use_mfma(const mla_dims_t* d, const mla_cache_t* c) {
   return d->dtype == MLA_BF16 && d->d_latent == 512 && d->d_rope == 64 &&
-         d->n_heads % mla::kMfmaHeadsPerGroup == 0;
+         d->n_heads % mla::kMfmaHeadsPerGroup == 0 &&
+         (c->page_table == nullptr || (c->page_size % 8 == 0 && c->page_size >= 8));
 }
 
 mla_status_t check_cache(const mla_cache_t* c) {
@@ -77,7 +78,7 @@ size_t workspace_for(const mla_dims_t* d, int batch, int num_splits) {
 
 mla_status_t make_plan(const mla_dims_t* d, int batch, const mla_cache_t* c, int split_req,
                        const DeviceInfo& dev, mla_decode_plan_t* plan) {
-  const bool mfma = use_mfma(d);
+  const bool mfma = use_mfma(d, c);
   const int granule = mfma ? mla::kMfmaTokenGranule : 1;
   const int groups = mfma ? d->n_heads / mla::kMfmaHeadsPerGroup : d->n_heads;
   const int max_len = c->max_len;
@@ -97,6 +98,12 @@ mla_status_t make_plan(const mla_dims_t* d, int batch, const mla_cache_t* c, int
     if (split < floor_tokens) split = floor_tokens;
   }
   if (split > len_cap) split = len_cap;
+  if (mfma && c->page_table != nullptr) {
+    // The MFMA kernel keeps a partition's page ids in one register per lane:
+    // a partition may touch at most 64 pages.
+    const int max_split = (63 * c->page_size) / granule * granule;
+    if (split > max_split) split = max_split;
+  }
   const int num_splits = max_len > 0 ? (max_len + split - 1) / split : 1;
   plan->split_tokens = split;
   plan->num_splits = num_splits;

@@ -99,12 +99,125 @@ __global__ __launch_bounds__(kThreads) void out_uv_kernel(
   }
 }
 
+// bf16 MFMA form of both products, for the DeepSeek-V2 widths:
+//   Y[b, i, n] = sum_{k < K} X[b, i, k] W[i, k, n]      (n < N, per head i)
+// absorption: X = q^C (K = d_head = 128), W = W^UK (N = d_latent = 512)
+// output:     X = o_lat (K = d_latent = 512), W = W^UV (N = d_head = 128)
+// One workgroup owns head i and an NB-column block of W, stages that
+// [K x NB] block in LDS (the only HBM stream: every weight element is read
+// once), and computes all batch rows with v_mfma_f32_32x32x16_bf16.  The
+// 4 waves split the block into NS column sub-blocks of 32 and 4/NS K parts;
+// K parts are summed through LDS.  Batch rows are the A operand (M tiles of
+// 32, loaded straight from global memory, zero past `batch`); the weight is
+// the B operand, read with the transposing LDS read (within a 16-lane group,
+// lane i receives element i%4 of the 8-byte chunk addressed by lane 4j + i/4,
+// for j = 0..3).
+template <int K, int NB, int NS>
+__global__ __launch_bounds__(256) void head_proj_mfma_kernel(
+    const __bf16* __restrict__ X, const __bf16* __restrict__ W, __bf16* __restrict__ Y,
+    int batch, int n_heads, int N, int y_row, const __bf16* __restrict__ tail_src,
+    int tail_w) {
+  constexpr int KP = 4 / NS;          // K parts
+  constexpr int KW = K / KP;          // K range of one wave
+  constexpr int KSTEPS = KW / 16;
+  static_assert(NS * KP == 4 && KW % 16 == 0 && NB == NS * 32, "");
+  __shared__ __attribute__((aligned(16))) __bf16 w_s[K * NB];
+  __shared__ __attribute__((aligned(16))) float red[(KP > 1 ? KP - 1 : 1) * 16 * 64];
+
+  const int i = blockIdx.y;
+  const int n0 = blockIdx.x * NB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int ns = wave % NS, kp = wave / NS;
+
+  // Stage W[i][0:K][n0:n0+NB] (row-major, NB contiguous).
+  constexpr int kChunksPerRow = NB / 8;
+  const __bf16* wsrc = W + static_cast<size_t>(i) * K * N + n0;
+#pragma unroll
+  for (int ch = tid; ch < K * kChunksPerRow; ch += 256) {
+    const int k = ch / kChunksPerRow, cc = ch - k * kChunksPerRow;
+    *reinterpret_cast<bf16x8_t*>(w_s + k * NB + cc * 8) =
+        *reinterpret_cast<const bf16x8_t*>(wsrc + static_cast<size_t>(k) * N + cc * 8);
+  }
+  // The RoPE tail of the absorbed query is copied unchanged (absorption only).
+  if (tail_src != nullptr && blockIdx.x == 0) {
+    for (int e = tid; e < batch * tail_w; e += 256) {
+      const int b = e / tail_w, r = e - b * tail_w;
+      Y[(static_cast<size_t>(b) * n_heads + i) * y_row + N + r] =
+          tail_src[(static_cast<size_t>(b) * n_heads + i) * tail_w + r];
+    }
+  }
+  __syncthreads();
+
+  // Transposing-read source coordinates of this lane (see above).
+  const int G = lane >> 4, r16 = lane & 15;
+  const int tr_k = ((G >> 1) << 3) + (r16 >> 2);
+  const int tr_n = ns * 32 + ((G & 1) << 4) + ((r16 & 3) << 2);
+
+  for (int m0 = 0; m0 < batch; m0 += 32) {
+    const int b = m0 + l32;
+    const __bf16* xrow = X + (static_cast<size_t>(b) * n_heads + i) * K + kp * KW + half * 8;
+    f32x16_t acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      bf16x8_t a;
+      if (b < batch) {
+        a = *reinterpret_cast<const bf16x8_t*>(xrow + ks * 16);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = static_cast<__bf16>(0.f);
+      }
+      const int k0 = kp * KW + ks * 16;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k) * NB + tr_n));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k + 4) * NB + tr_n));
+      const bf16x8_t bop =
+          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
+    }
+    if constexpr (KP > 1) {
+      if (kp > 0) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[((kp - 1) * 16 + v) * 64 + lane] = acc[v];
+      }
+      __syncthreads();
+      if (kp == 0) {
+#pragma unroll
+        for (int q = 0; q < KP - 1; ++q)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[v] += red[(q * 16 + v) * 64 + lane];
+      }
+      __syncthreads();
+    }
+    if (kp == 0) {
+      // Accumulator register v of this lane: row (v/4)*8 + half*4 + v%4, column l32.
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int bb = m0 + (v >> 2) * 8 + half * 4 + (v & 3);
+        if (bb < batch)
+          Y[(static_cast<size_t>(bb) * n_heads + i) * y_row + n0 + ns * 32 + l32] =
+              static_cast<__bf16>(acc[v]);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_absorb_q(int dtype, int batch, int n_heads, int d_head, int d_rope,
                            int d_latent, const void* q_c, const void* q_r,
                            const void* w_uk, void* q_cat, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
+  if (dtype == 1 && d_head == 128 && d_latent % 128 == 0) {
+    head_proj_mfma_kernel<128, 128, 4><<<dim3(d_latent / 128, n_heads), 256, 0, stream>>>(
+        static_cast<const __bf16*>(q_c), static_cast<const __bf16*>(w_uk),
+        static_cast<__bf16*>(q_cat), batch, n_heads, d_latent, d_latent + d_rope,
+        d_rope > 0 ? static_cast<const __bf16*>(q_r) : nullptr, d_rope);
+    return hipGetLastError();
+  }
   const dim3 grid((d_latent + d_rope + kThreads - 1) / kThreads, n_heads,
                   (batch + kRows - 1) / kRows);
   const size_t lds = sizeof(float) * kRows * d_head;
@@ -126,6 +239,12 @@ hipError_t launch_out_uv(int dtype, int batch, int n_heads, int d_head, int d_la
                          const void* out_lat, const void* w_uv, void* out,
                          hipStream_t stream) {
   if (batch == 0) return hipSuccess;
+  if (dtype == 1 && d_latent == 512 && d_head % 32 == 0) {
+    head_proj_mfma_kernel<512, 32, 1><<<dim3(d_head / 32, n_heads), 256, 0, stream>>>(
+        static_cast<const __bf16*>(out_lat), static_cast<const __bf16*>(w_uv),
+        static_cast<__bf16*>(out), batch, n_heads, d_head, d_head, nullptr, 0);
+    return hipGetLastError();
+  }
   const dim3 grid((d_head + kThreads - 1) / kThreads, n_heads, (batch + kRows - 1) / kRows);
   const size_t lds = sizeof(float) * kRows * d_latent;
   if (dtype == 0) {

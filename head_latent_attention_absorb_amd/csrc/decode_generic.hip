@@ -148,13 +148,13 @@ __global__ __launch_bounds__(kThreads) void combine_rowmajor_kernel(
 // Fragment layout, per (request b, split s, 32-head block hb):
 //   part_o[(((b * S + s) * NHB + hb) * 256 + cb * 16 + v) * 64 + lane]
 //     = O[head hb*32 + lane%32][latent cb*32 + (v/4)*8 + (lane/32)*4 + v%4]
-// grid: x = 32-head block, y = request; 256 threads, wave w handles latent
-// blocks cb = 4w .. 4w+3.
+// grid: x = group of 4 latent blocks, y = 32-head block, z = request; wave w
+// of the workgroup handles latent block cb = 4 * blockIdx.x + w.
 __global__ __launch_bounds__(kThreads) void combine_fragment_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     const int32_t* __restrict__ seq_lens, int n_heads, int split_tokens, int num_splits,
     __bf16* __restrict__ out_lat, float* __restrict__ lse_out) {
-  const int hb = blockIdx.x, b = blockIdx.y;
+  const int hb = blockIdx.y, b = blockIdx.z;
   const int nhb = n_heads / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int head = hb * 32 + (lane & 31), half = lane >> 5;
@@ -167,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void combine_fragment_kernel(
   const float invW = ns > 0 ? 1.f / W : 0.f;
 
   __bf16* orow = out_lat + static_cast<size_t>(b * n_heads + head) * 512;
-  for (int cb = wave * 4; cb < wave * 4 + 4; ++cb) {
+  {
+    const int cb = blockIdx.x * 4 + wave;
     float acc[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void combine_fragment_kernel(
       *reinterpret_cast<bf16x4_t*>(orow + cb * 32 + g * 8 + half * 4) = pk;
     }
   }
-  if (lse_out != nullptr && wave == 0 && half == 0)
+  if (lse_out != nullptr && blockIdx.x == 0 && wave == 0 && half == 0)
     lse_out[static_cast<size_t>(b) * n_heads + head] = ns > 0 ? L + logf(W) : -INFINITY;
 }
 
@@ -210,7 +211,7 @@ hipError_t launch_partials_generic(const DecodeArgs& a) {
 hipError_t launch_combine(const DecodeArgs& a, bool fragment) {
   if (a.batch == 0) return hipSuccess;
   if (fragment) {
-    combine_fragment_kernel<<<dim3(a.n_heads / 32, a.batch), kThreads, 0, a.stream>>>(
+    combine_fragment_kernel<<<dim3(4, a.n_heads / 32, a.batch), kThreads, 0, a.stream>>>(
         a.part_o, a.part_lse, a.cache.seq_lens, a.n_heads, a.split_tokens, a.num_splits,
         static_cast<__bf16*>(a.out_lat), a.lse);
     return hipGetLastError();

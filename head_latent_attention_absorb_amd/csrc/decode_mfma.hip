@@ -44,12 +44,13 @@ constexpr int kRow = 576;             // d_latent + d_rope
 constexpr int kRowBytes = kRow * 2;
 constexpr int kTile = 32;             // tokens per step
 constexpr int kTileBytes = kTile * kRowBytes;        // 36864
-constexpr int kStages = 3;            // LDS ring depth; kStages - 1 tiles in flight
+constexpr int kStages = 4;            // LDS ring depth; kStages - 1 tiles in flight
 constexpr int kGroups = kRow / 64;    // 9 column groups of 128 bytes
 constexpr int kHalfKSteps = kRow / 16 / 2;           // 18 score K-steps per wave
 constexpr int kHalfCBlocks = 512 / 32 / 2;           // 8 latent blocks per wave
-constexpr int kXchBytes = 2 * 2 * 2 * 64 * 16 * 4;   // parity x pair x wave x frag
+constexpr int kXchBytes = 2 * 2 * 64 * 16 * 4;       // pair x wave x fragment
 constexpr int kLdsBytes = kStages * kTileBytes + kXchBytes;
+static_assert(kStages == 4, "the main loop is unrolled over exactly four stage arrays");
 constexpr float kRescaleThreshold = 8.f;             // log2 units
 
 static_assert(kTileBytes == 4 * kGroups * 1024, "each wave issues kGroups loads per tile");
@@ -69,6 +70,25 @@ struct MfmaParams {
   float* part_lse;
 };
 
+// 16-byte direct-to-LDS load: every lane reads 16 bytes at `src` and writes
+// them at LDS byte address lds_base + 16 * lane (lds_base wave-uniform, in M0).
+// Issued as inline asm so the compiler's wait insertion does not see it: it
+// cannot tell the ring stages apart and would otherwise drain every
+// outstanding load before each LDS read.  The kernel waits for these loads
+// itself (s_waitcnt vmcnt) before the barrier that publishes a stage.  The
+// instruction has no result registers; its address is read at issue.  No
+// other instruction in this kernel uses M0.
+__device__ __forceinline__ void load_to_lds16(const void* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS const void*)p));
+}
+
 // LDS byte offset (within a tile) of 16-byte chunk `chunk` (0..71) of token `n`.
 __device__ __forceinline__ int swz(int n, int chunk) {
   return (((chunk >> 3) * kTile + n) << 7) + (((chunk & 7) ^ (n & 7)) << 4);
@@ -76,7 +96,14 @@ __device__ __forceinline__ int swz(int n, int chunk) {
 
 template <bool kPaged>
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  // Four ring stages (3 tiles in flight) plus the score exchange fill the
+  // 160 KiB of LDS exactly.  The stages are distinct arrays and the loop is
+  // unrolled over them, so every stage offset is a compile-time constant.
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) float xch[kXchBytes / 4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hb = wave >> 1, hf = wave & 1;
@@ -129,67 +156,141 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   const uint8_t* req_base =
       kPaged ? p.cache.data
              : p.cache.data + static_cast<size_t>(b) * p.cache.max_len * kRowBytes;
-  auto issue_tile = [&](int stage, int tile_t0) {
+  // Paged cache: lane j holds the physical id of the partition's j-th page
+  // (at most 64 pages, which the planner guarantees), fetched once here.  A
+  // wave's 8 tokens of a tile are 8-aligned, so with page_size % 8 == 0 they
+  // share one page, picked per tile with readlane: no memory access, and no
+  // load the compiler would have to wait for inside the loop.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int page_of_lane = 0, first_page = 0;
+  if constexpr (kPaged) {
+    first_page = t0 / p.cache.page_size;
+    const int npages = (t1 - 1) / p.cache.page_size - first_page + 1;
+    if (lane < npages)
+      page_of_lane = p.cache.page_table[static_cast<size_t>(b) * p.cache.max_pages +
+                                        first_page + lane];
+  }
+  auto issue_tile = [&](uint8_t* stage, int tile_t0) {
     const int t = min(tile_t0 + n_load, t1 - 1);
     const uint8_t* src;
     if constexpr (kPaged) {
-      const int page = p.cache.page_table[static_cast<size_t>(b) * p.cache.max_pages +
-                                          t / p.cache.page_size];
+      const int t_first = min(tile_t0 + wave_u * 8, t1 - 1);
+      const int page =
+          __builtin_amdgcn_readlane(page_of_lane, t_first / p.cache.page_size - first_page);
       src = req_base + (static_cast<size_t>(page) * p.cache.page_size + t % p.cache.page_size) *
                            kRowBytes;
     } else {
       src = req_base + static_cast<size_t>(t) * kRowBytes;
     }
     src += chunk_off;
-    uint8_t* dst = lds + stage * kTileBytes + wave * 1024;
+    const unsigned dst = lds_address(stage) + wave * 1024;
 #pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(src + gi * 128),
-          (__attribute__((address_space(3))) void*)(dst + gi * 4096), 16, 0, 0);
+    for (int gi = 0; gi < kGroups; ++gi) load_to_lds16(src + gi * 128, dst + gi * 4096);
   };
 
-  float* xch = reinterpret_cast<float*>(lds + kStages * kTileBytes);
   // Per-lane coordinates of the transposing reads of the PV operand.
   const int tr_tok = (half << 2) + ((lane >> 2) & 3);
   const int tr_col = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-  issue_tile(0, t0);
-  if (ntiles > 1) issue_tile(1, t0 + kTile);
+  // Prologue: tiles 0..2 in flight, then one wait (visible to the compiler)
+  // for them and for the query fragments, which every step needs at once.
+  // From here on the compiler sees no outstanding loads, and the tile loads
+  // are governed only by the waits below.  Every step issues exactly one
+  // tile (past the last tile they re-read the partition's last row into a
+  // stage that is never read again), so "this wave's loads of tile it have
+  // landed" is always vmcnt(18): the two younger tiles may stay in flight.
+  issue_tile(stage0, t0);
+  issue_tile(stage1, t0 + kTile);
+  issue_tile(stage2, t0 + 2 * kTile);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One step: tile `it` is in `tile`; tile it+3 is loaded into `next3`.
+  auto step = [&](int it, const uint8_t* tile, uint8_t* next3) {
     // Wait for this wave's loads of tile `it` (those of tile it+1 may stay in
-    // flight), then for everyone's.
-    if (it + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroups));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    // Everyone is past iteration it-1, so its stage can be refilled.
-    if (it + 2 < ntiles) issue_tile((it + 2) % kStages, t0 + (it + 2) * kTile);
+    // flight), then for everyone's.  A raw s_barrier, not __syncthreads(): the
+    // latter also waits for every outstanding global load and would drain the
+    // prefetch at each barrier.  The compiler fence keeps LDS accesses on
+    // their side of the barrier.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGroups));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // Everyone is past step it-1, whose stage is `next3`: refill it.
+    issue_tile(next3, t0 + (it + 3) * kTile);
 
-    const uint8_t* tile = lds + (it % kStages) * kTileBytes;
     const int nvalid = t1 - (t0 + it * kTile);
 
-    // Partial S^T[token, head] over this wave's half of K.
+    // Per-lane LDS offsets.  Score operand of K-step ks: swz(l32, chunk) with
+    // chunk = 36 hf + 2 ks + half, which equals qoff[ks % 4] + (ks / 4) * 4096.
+    // PV operand of latent block cb, K-step kk, read lo/hi:
+    // voff[cb % 2] + (cb / 2) * 4096 + kk * 2048 + hi * 1024.  The empty asm
+    // keeps these few offsets from being hoisted out of the loop per stage
+    // (three stages x 50 addresses would not fit in registers).
+    int qoff[4], voff[2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) qoff[q] = swz(l32, (hf * kHalfKSteps + q) * 2 + half);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = (hf * kHalfCBlocks + q) * 32 + tr_col;
+      voff[q] = swz(tr_tok, c >> 3) + (c & 7) * 2;
+    }
+    asm volatile("" : "+v"(qoff[0]), "+v"(qoff[1]), "+v"(qoff[2]), "+v"(qoff[3]),
+                 "+v"(voff[0]), "+v"(voff[1]));
+
+    // Partial S^T[token, head] over this wave's half of K.  All 18 operand
+    // reads are issued before the MFMA chain so LDS latency overlaps it.
+    bf16x8_t ta[kHalfKSteps];
+#pragma unroll
+    for (int ks = 0; ks < kHalfKSteps; ++ks)
+      ta[ks] = *reinterpret_cast<const bf16x8_t*>(tile + qoff[ks & 3] + (ks >> 2) * 4096);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMA chain
     f32x16_t sacc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < kHalfKSteps; ++ks) {
-      const int chunk = (hf * kHalfKSteps + ks) * 2 + half;
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(tile + swz(l32, chunk));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < kHalfKSteps; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[ks], qf[ks], sacc, 0, 0, 0);
 
     // Sum the two half-K partials of this head block through LDS.  Both waves
     // add (K-half 0) + (K-half 1) in that order, so their scores match bitwise.
-    float* xw = xch + ((it & 1) * 4 + hb * 2) * 1024;  // [wave of pair][reg][lane]
+    // One buffer serves every step: each wave consumes its partner's values
+    // (softmax below) before it reaches the next step's barrier, and nobody
+    // rewrites the buffer before passing that barrier.
+    float* xw = xch + hb * 2 * 1024;  // [wave of pair][reg][lane]
 #pragma unroll
     for (int v = 0; v < 16; v += 4)
       *reinterpret_cast<f32x4_t*>(xw + hf * 1024 + v * 64 + lane * 4) =
           f32x4_t{sacc[v], sacc[v + 1], sacc[v + 2], sacc[v + 3]};
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the exchange writes are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    // O^T[latent, head] += V^T[latent, token] . P^T[token, head] over this
+    // wave's 256 latent columns.  K slot j of lane half `half` in K-step kk is
+    // token kk*16 + (j/4)*8 + half*4 + j%4, matching the P^T registers below.
+    // The A operand (lane: one latent column, 8 tokens) comes from two
+    // transposing LDS reads: within each 16-lane group, ds_read_b64_tr_b16
+    // gives lane i the (i%4)-th element of the 8-byte chunk addressed by lane
+    // 4j + i/4, for j = 0..3.  So lane (group G, index r) addresses token
+    // kk*16 + {0,8} + (G/2)*4 + r/4 at latent column 16*(G%2) + 4*(r%4).
+    // The first half of these reads is issued before the softmax math, which
+    // then runs while they are in flight.
+    bf16x8_t va[kHalfCBlocks][2];
+    auto read_v = [&](int cb) {
+      const uint8_t* vb = tile + voff[cb & 1] + (cb >> 1) * 4096;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const i16x4_t lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4_t*)(vb + kk * 2048));
+        const i16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4_t*)(vb + kk * 2048 + 1024));
+        va[cb][kk] =
+            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+#pragma unroll
+    for (int cb = 0; cb < kHalfCBlocks / 2; ++cb) read_v(cb);
+    __builtin_amdgcn_sched_barrier(0);
+
     float sv[16];
 #pragma unroll
     for (int v = 0; v < 16; v += 4) {
@@ -245,30 +346,24 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     }
     l += psum;
 
-    // O^T[latent, head] += V^T[latent, token] . P^T[token, head] over this
-    // wave's 256 latent columns.  K slot j of lane half `half` in K-step kk is
-    // token kk*16 + (j/4)*8 + half*4 + j%4, matching the P^T registers above.
-    // The A operand (lane: one latent column, 8 tokens) comes from two
-    // transposing LDS reads: within each 16-lane group, ds_read_b64_tr_b16
-    // gives lane i the (i%4)-th element of the 8-byte chunk addressed by lane
-    // 4j + i/4, for j = 0..3.  So lane (group G, index r) addresses token
-    // kk*16 + {0,8} + (G/2)*4 + r/4 at latent column 16*(G%2) + 4*(r%4).
 #pragma unroll
-    for (int cb = 0; cb < kHalfCBlocks; ++cb) {
-      const int c = (hf * kHalfCBlocks + cb) * 32 + tr_col;
+    for (int cb = kHalfCBlocks / 2; cb < kHalfCBlocks; ++cb) read_v(cb);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int n = kk * 16 + tr_tok;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (MLA_LDS i16x4_t*)(tile + swz(n, c >> 3) + (c & 7) * 2));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (MLA_LDS i16x4_t*)(tile + swz(n + 8, c >> 3) + (c & 7) * 2));
-        const bf16x8_t a =
-            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], acc[cb], 0, 0, 0);
-      }
-    }
+    for (int cb = 0; cb < kHalfCBlocks; ++cb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb][kk], pb[kk], acc[cb], 0, 0, 0);
+  };
+
+  for (int it = 0; it < ntiles; it += kStages) {
+    step(it, stage0, stage3);
+    if (it + 1 < ntiles) step(it + 1, stage1, stage0);
+    if (it + 2 < ntiles) step(it + 2, stage2, stage1);
+    if (it + 3 < ntiles) step(it + 3, stage3, stage2);
   }
+  // The trailing loads must land before the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // Softmax sum over both lane halves (each half saw half of the tokens).
   l = halves_sum(l);
