@@ -104,6 +104,19 @@ def cpu_baseline(entry: Entry, cfg, n_requests: int):
     }
 
 
+def copy_calibration(n_bytes: int = 256 << 20, copies: int = 6):
+    """Plain device-to-device copies of a known size.  Under rocprofv3 --pmc the
+    ratio of FETCH_SIZE (or WRITE_SIZE) per copy dispatch to n_bytes is the factor
+    that turns those counters into bytes for the decode kernel."""
+    src = [torch.full((n_bytes,), i, dtype=torch.uint8, device="cuda") for i in range(2)]
+    dst = [torch.empty(n_bytes, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    torch.cuda.synchronize()
+    for i in range(copies):
+        dst[i % 3].copy_(src[i % 2])
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n_bytes, "copies": copies}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,7 +127,13 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests in the CPU oracle sample (0 skips it)")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 256 MiB device copies (a known-size kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
