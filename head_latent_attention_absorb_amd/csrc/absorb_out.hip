@@ -7,10 +7,13 @@
 // after the latent-space sum (V2 read-through section 2.3).
 //
 // Both are HBM-bound at decode batch sizes: every weight element is read once
-// per call and used for `batch` multiply-adds.  One workgroup owns one head
-// and a 256-wide slice of output columns; the batch rows it serves are staged
-// in LDS as fp32 and each thread keeps kRows accumulators, so a weight element
-// loaded once feeds kRows FMAs.
+// per call and used for `batch` multiply-adds.  Two forms:
+//  * head_proj_mfma_kernel, bf16 at the DeepSeek-V2 widths: a workgroup stages
+//    one [K x NB] weight block in LDS and multiplies it on MFMA (see below).
+//  * absorb_q_kernel / out_uv_kernel, any widths and fp32: one workgroup owns
+//    one head and a 256-wide slice of output columns; the batch rows it serves
+//    are staged in LDS as fp32 and each thread keeps kRows accumulators, so a
+//    weight element loaded once feeds kRows FMAs.
 
 #include "device_common.h"
 
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
   constexpr int KSTEPS = KW / 16;
   static_assert(NS * KP == 4 && KW % 16 == 0 && NB == NS * 32, "");
   __shared__ __attribute__((aligned(16))) __bf16 w_s[K * NB];
-  __shared__ __attribute__((aligned(16))) float red[(KP > 1 ? KP - 1 : 1) * 16 * 64];
+  __shared__ __attribute__((aligned(16))) float red[(KP > 1 ? KP - 1 : 1) * NS * 16 * 64];
 
   const int i = blockIdx.y;
   const int n0 = blockIdx.x * NB;
@@ -130,45 +133,86 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
   const int half = lane >> 5, l32 = lane & 31;
   const int ns = wave % NS, kp = wave / NS;
 
-  // Stage W[i][0:K][n0:n0+NB] (row-major, NB contiguous).
-  constexpr int kChunksPerRow = NB / 8;
-  const __bf16* wsrc = W + static_cast<size_t>(i) * K * N + n0;
-#pragma unroll
-  for (int ch = tid; ch < K * kChunksPerRow; ch += 256) {
-    const int k = ch / kChunksPerRow, cc = ch - k * kChunksPerRow;
-    *reinterpret_cast<bf16x8_t*>(w_s + k * NB + cc * 8) =
-        *reinterpret_cast<const bf16x8_t*>(wsrc + static_cast<size_t>(k) * N + cc * 8);
-  }
-  // The RoPE tail of the absorbed query is copied unchanged (absorption only).
-  if (tail_src != nullptr && blockIdx.x == 0) {
-    for (int e = tid; e < batch * tail_w; e += 256) {
-      const int b = e / tail_w, r = e - b * tail_w;
-      Y[(static_cast<size_t>(b) * n_heads + i) * y_row + N + r] =
-          tail_src[(static_cast<size_t>(b) * n_heads + i) * tail_w + r];
-    }
-  }
-  __syncthreads();
-
   // Transposing-read source coordinates of this lane (see above).
   const int G = lane >> 4, r16 = lane & 15;
   const int tr_k = ((G >> 1) << 3) + (r16 >> 2);
   const int tr_n = ns * 32 + ((G & 1) << 4) + ((r16 & 3) << 2);
 
-  for (int m0 = 0; m0 < batch; m0 += 32) {
+  // A operand fragments of one 32-row M tile: row m0 + l32, K elements
+  // kp*KW + ks*16 + half*8 .. +7.  Rows past `batch` are zero.
+  bf16x8_t a[KSTEPS], a_next[KSTEPS];
+  auto load_a = [&](int m0, bf16x8_t(&dst)[KSTEPS]) {
     const int b = m0 + l32;
     const __bf16* xrow = X + (static_cast<size_t>(b) * n_heads + i) * K + kp * KW + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (b < batch) {
+        dst[ks] = *reinterpret_cast<const bf16x8_t*>(xrow + ks * 16);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[ks][j] = static_cast<__bf16>(0.f);
+      }
+    }
+  };
+  // The first tile's rows are requested before the weight block so that both
+  // HBM round trips overlap.
+  load_a(0, a);
+
+  // The RoPE tail of the absorbed query is copied unchanged (absorption only),
+  // in 4-element vectors spread over the gridDim.x workgroups of this head.
+  // The first round is loaded here so that it overlaps the weight stream.
+  const int tail_q = tail_w / 4;
+  const int tail_vecs = tail_src != nullptr ? batch * tail_q : 0;
+  const int tv0 = blockIdx.x * 256 + tid, tv_step = gridDim.x * 256;
+  auto tail_at = [&](int e) {
+    const int b = e / tail_q, r4 = e - b * tail_q;
+    return reinterpret_cast<const bf16x4_t*>(
+        tail_src + (static_cast<size_t>(b) * n_heads + i) * tail_w + r4 * 4);
+  };
+  auto tail_dst = [&](int e) {
+    const int b = e / tail_q, r4 = e - b * tail_q;
+    return reinterpret_cast<bf16x4_t*>(Y + (static_cast<size_t>(b) * n_heads + i) * y_row + N +
+                                       r4 * 4);
+  };
+  bf16x4_t tv;
+  if (tv0 < tail_vecs) tv = tail_at(tv0)[0];
+
+  // Stage W[i][0:K][n0:n0+NB] (row-major, NB contiguous): all loads first,
+  // then the LDS stores.
+  constexpr int kChunksPerRow = NB / 8;
+  constexpr int kLoads = K * kChunksPerRow / 256;
+  static_assert(K * kChunksPerRow % 256 == 0, "");
+  const __bf16* wsrc = W + static_cast<size_t>(i) * K * N + n0;
+  bf16x8_t wv[kLoads];
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u) {
+    const int ch = tid + u * 256;
+    const int k = ch / kChunksPerRow, cc = ch - k * kChunksPerRow;
+    wv[u] = *reinterpret_cast<const bf16x8_t*>(wsrc + static_cast<size_t>(k) * N + cc * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u) {
+    const int ch = tid + u * 256;
+    const int k = ch / kChunksPerRow, cc = ch - k * kChunksPerRow;
+    *reinterpret_cast<bf16x8_t*>(w_s + k * NB + cc * 8) = wv[u];
+  }
+  // Second half of the RoPE tail copy: store what was loaded above, then the
+  // further rounds needed when the tail has more vectors than the head's
+  // workgroups have threads.
+  if (tv0 < tail_vecs) {
+    tail_dst(tv0)[0] = tv;
+    for (int e = tv0 + tv_step; e < tail_vecs; e += tv_step) tail_dst(e)[0] = tail_at(e)[0];
+  }
+  __syncthreads();
+
+  for (int m0 = 0; m0 < batch; m0 += 32) {
+    // The next M tile's rows are requested before this tile's products.
+    if (m0 + 32 < batch) load_a(m0 + 32, a_next);
     f32x16_t acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      bf16x8_t a;
-      if (b < batch) {
-        a = *reinterpret_cast<const bf16x8_t*>(xrow + ks * 16);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[j] = static_cast<__bf16>(0.f);
-      }
       const int k0 = kp * KW + ks * 16;
       const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k) * NB + tr_n));
@@ -176,19 +220,19 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
           (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k + 4) * NB + tr_n));
       const bf16x8_t bop =
           __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bop, acc, 0, 0, 0);
     }
     if constexpr (KP > 1) {
       if (kp > 0) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) red[((kp - 1) * 16 + v) * 64 + lane] = acc[v];
+        for (int v = 0; v < 16; ++v) red[(((kp - 1) * NS + ns) * 16 + v) * 64 + lane] = acc[v];
       }
       __syncthreads();
       if (kp == 0) {
 #pragma unroll
         for (int q = 0; q < KP - 1; ++q)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[v] += red[(q * 16 + v) * 64 + lane];
+          for (int v = 0; v < 16; ++v) acc[v] += red[((q * NS + ns) * 16 + v) * 64 + lane];
       }
       __syncthreads();
     }
@@ -202,6 +246,10 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
               static_cast<__bf16>(acc[v]);
       }
     }
+    if (m0 + 32 < batch) {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) a[ks] = a_next[ks];
+    }
   }
 }
 
@@ -211,7 +259,7 @@ hipError_t launch_absorb_q(int dtype, int batch, int n_heads, int d_head, int d_
                            int d_latent, const void* q_c, const void* q_r,
                            const void* w_uk, void* q_cat, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  if (dtype == 1 && d_head == 128 && d_latent % 128 == 0) {
+  if (dtype == 1 && d_head == 128 && d_latent % 128 == 0 && d_rope % 4 == 0) {
     head_proj_mfma_kernel<128, 128, 4><<<dim3(d_latent / 128, n_heads), 256, 0, stream>>>(
         static_cast<const __bf16*>(q_c), static_cast<const __bf16*>(w_uk),
         static_cast<__bf16*>(q_cat), batch, n_heads, d_latent, d_latent + d_rope,
@@ -239,8 +287,8 @@ hipError_t launch_out_uv(int dtype, int batch, int n_heads, int d_head, int d_la
                          const void* out_lat, const void* w_uv, void* out,
                          hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  if (dtype == 1 && d_latent == 512 && d_head % 32 == 0) {
-    head_proj_mfma_kernel<512, 32, 1><<<dim3(d_head / 32, n_heads), 256, 0, stream>>>(
+  if (dtype == 1 && d_latent == 512 && d_head % 64 == 0) {
+    head_proj_mfma_kernel<512, 64, 2><<<dim3(d_head / 64, n_heads), 256, 0, stream>>>(
         static_cast<const __bf16*>(out_lat), static_cast<const __bf16*>(w_uv),
         static_cast<__bf16*>(out), batch, n_heads, d_head, d_head, nullptr, 0);
     return hipGetLastError();
