@@ -71,9 +71,12 @@ mla_status_t check_cache(const mla_cache_t* c) {
 
 size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-size_t workspace_for(const mla_dims_t* d, int batch, int num_splits) {
+// Bytes of one partial output element: the MFMA kernel stores bf16 partials.
+size_t partial_elem_bytes(bool mfma) { return mfma ? 2 : sizeof(float); }
+
+size_t workspace_for(const mla_dims_t* d, int batch, int num_splits, bool mfma) {
   const size_t parts = static_cast<size_t>(batch) * num_splits * d->n_heads;
-  return round256(parts * d->d_latent * sizeof(float)) + round256(parts * sizeof(float));
+  return round256(parts * d->d_latent * partial_elem_bytes(mfma)) + round256(parts * sizeof(float));
 }
 
 mla_status_t make_plan(const mla_dims_t* d, int batch, const mla_cache_t* c, int split_req,
@@ -109,7 +112,7 @@ mla_status_t make_plan(const mla_dims_t* d, int batch, const mla_cache_t* c, int
   plan->num_splits = num_splits;
   plan->kernel = mfma ? 1 : 0;
   plan->head_groups = groups;
-  plan->workspace_bytes = workspace_for(d, batch, num_splits);
+  plan->workspace_bytes = workspace_for(d, batch, num_splits, mfma);
   return MLA_OK;
 }
 
@@ -229,9 +232,10 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
   a->head_groups = plan_out->head_groups;
   a->out_lat = out_lat;
   a->lse = lse;
-  a->part_o = static_cast<float*>(const_cast<void*>(workspace));
-  a->part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(const_cast<void*>(workspace)) +
-                                         round256(parts_n * dims->d_latent * sizeof(float)));
+  a->part_o = const_cast<void*>(workspace);
+  a->part_lse = reinterpret_cast<float*>(
+      static_cast<uint8_t*>(const_cast<void*>(workspace)) +
+      round256(parts_n * dims->d_latent * partial_elem_bytes(plan_out->kernel == 1)));
   a->stream = static_cast<hipStream_t>(stream);
   return MLA_OK;
 }

@@ -6,34 +6,40 @@
 //           DeepSeek-V2 read-through, 2kiu.com/news/6085339, sections 2.3-2.4)
 //   O_i   = sum_j softmax_j(s) * row_j[0:512]           (weighted sum in latent
 //           space, section 2.3; the cached latent serves as both K and V)
-// written as a partial normalised by its own softmax sum plus its log-sum-exp.
+// written as a bf16 partial normalised by its own softmax sum plus its fp32
+// log-sum-exp.
 //
 // Mapping onto CDNA4:
-//  * One workgroup = 4 waves (one per SIMD) = (request, 64 heads, partition).
-//    Wave (hb, hf): hb picks a 32-head block; hf picks half of the score
-//    contraction (K = 288 of 576) and half of the latent output (256 of 512).
-//    All four waves consume the same 32-token tile per step.
+//  * One workgroup = 4 waves (one per SIMD) = (request, 128 heads, partition).
+//    Wave w owns 32 heads over the whole score contraction (K = 576) and the
+//    whole latent output (512): 144 registers of query fragments and 256
+//    accumulator registers per lane.  Every cached token is read from HBM by
+//    exactly one workgroup.
 //  * Tiles move HBM -> LDS with 16-byte direct-to-LDS loads (no VGPR
-//    staging) through a 3-stage ring, two tiles in flight.  A 32-token tile is
-//    stored column-group major: the 576-element row is cut into 9 groups of 64
-//    elements (128 B); group g of token n sits at ((g * 32 + n) * 128), its
-//    eight 16-byte chunks XOR-swizzled by (n & 7) so MFMA operand reads are
-//    conflict free.  A load instruction fills 8 tokens x one group: each lane
-//    owns one token row per tile and every global access is a whole 128-byte
-//    segment.
+//    staging) through a 4-stage ring.  A 32-token tile is stored column-group
+//    major: the 576-element row is cut into 9 groups of 64 elements (128 B);
+//    group g of token n sits at ((g * 32 + n) * 128), its eight 16-byte chunks
+//    XOR-swizzled by (n & 7) so MFMA operand reads are conflict free.  A load
+//    instruction fills 8 tokens x one group: each lane owns one token row per
+//    tile and every global access is a whole 128-byte segment.
 //  * Scores are computed transposed, S^T[token, head] = tile . Q^T, with
 //    v_mfma_f32_32x32x16_bf16: the tile is the A operand (LDS), the query the
-//    B operand (registers for the whole kernel).  The two half-K partial
-//    scores of a head block are summed through LDS (same order in both waves,
-//    so both hold bitwise identical scores and softmax state).  In the
-//    accumulator layout each lane owns one head, so the softmax max and sum
-//    need one cross-lane step (lane l <-> l^32).
+//    B operand (registers for the whole kernel).  In the accumulator layout
+//    each lane owns one head, so the softmax max and sum need one cross-lane
+//    step (lane l <-> l^32).
 //  * The probabilities stay in registers: the S^T accumulator converted to
 //    bf16 is exactly the B operand of O^T[latent, head] += V^T . P^T, with the
-//    token (K) index permuted identically on both operands.  O^T is 8
-//    accumulator tiles (128 registers per lane).
+//    token (K) index permuted identically on both operands.
+//  * Software pipeline, one wave per SIMD: step t issues the softmax
+//    arithmetic of tile t between the score MFMAs of tile t+1, so the matrix
+//    pipe has independent work while that arithmetic runs, then the PV product
+//    of tile t.  Tiles t and t+1 are resident in the ring during step t,
+//    tiles t+2 and t+3 in flight.
 //  * The running max only moves when a tile's max exceeds it by more than 8
 //    (exp2 units), so the accumulator rescale runs rarely and p <= 256.
+
+#include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 
@@ -44,18 +50,21 @@ constexpr int kRow = 576;             // d_latent + d_rope
 constexpr int kRowBytes = kRow * 2;
 constexpr int kTile = 32;             // tokens per step
 constexpr int kTileBytes = kTile * kRowBytes;        // 36864
-constexpr int kStages = 4;            // LDS ring depth; kStages - 1 tiles in flight
+constexpr int kStages = 4;            // LDS ring depth
 constexpr int kGroups = kRow / 64;    // 9 column groups of 128 bytes
-constexpr int kHalfKSteps = kRow / 16 / 2;           // 18 score K-steps per wave
-constexpr int kHalfCBlocks = 512 / 32 / 2;           // 8 latent blocks per wave
-constexpr int kXchBytes = 2 * 2 * 64 * 16 * 4;       // pair x wave x fragment
-constexpr int kLdsBytes = kStages * kTileBytes + kXchBytes;
-static_assert(kStages == 4, "the main loop is unrolled over exactly four stage arrays");
+constexpr int kKSteps = kRow / 16;    // 36 score K-steps
+constexpr int kCBlocks = 512 / 32;    // 16 latent blocks
+constexpr int kPv = 2 * kCBlocks;     // 32 PV MFMAs per tile
+constexpr int kKWindow = 3;           // score operand reads in flight
+constexpr int kVWindow = 4;           // PV operands (two reads each) in flight
+constexpr int kQkLead = 8;            // score MFMAs issued between the softmax pieces
+constexpr int kLdsBytes = kStages * kTileBytes;
 constexpr float kRescaleThreshold = 8.f;             // log2 units
 
 static_assert(kTileBytes == 4 * kGroups * 1024, "each wave issues kGroups loads per tile");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(kMfmaHeadsPerGroup == 64 && kMfmaTokenGranule == kTile, "");
+static_assert((kStages & (kStages - 1)) == 0, "stage index uses a mask");
+static_assert(kMfmaHeadsPerGroup == 4 * 32 && kMfmaTokenGranule == kTile, "");
 
 // s_waitcnt immediate: wait until at most `n` vector-memory loads are
 // outstanding; expcnt and lgkmcnt are left at their maxima (no wait).
@@ -66,7 +75,7 @@ struct MfmaParams {
   CacheView cache;
   int n_heads, split_tokens, num_splits, head_groups, work_items;
   float scale_log2;       // softmax scale * log2(e)
-  float* part_o;
+  uint16_t* part_o;       // bf16 partials
   float* part_lse;
 };
 
@@ -76,14 +85,53 @@ struct MfmaParams {
 // cannot tell the ring stages apart and would otherwise drain every
 // outstanding load before each LDS read.  The kernel waits for these loads
 // itself (s_waitcnt vmcnt) before the barrier that publishes a stage.  The
-// instruction has no result registers; its address is read at issue.  No
-// other instruction in this kernel uses M0.
+// instruction has no result registers; its address (`src` plus the
+// immediate kOffset) is read at issue.  No other instruction in this kernel
+// uses M0.  The result lands at lds_base + 16 * lane.
+template <int kOffset>
 __device__ __forceinline__ void load_to_lds16(const void* src, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  // The immediate offset is added to the LDS address as well as to the
+  // global one, so M0 carries the LDS base minus that offset.
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
                :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base) - kOffset), "i"(kOffset)
                : "memory", "m0");
 }
+
+// The kGroups column groups of one token row: group gi sits gi * 128 bytes
+// into the row (an immediate offset) and fills LDS at dst + gi * 4096.
+template <int... gi>
+__device__ __forceinline__ void load_row_groups(const void* src, unsigned dst,
+                                                std::integer_sequence<int, gi...>) {
+  (load_to_lds16<gi * 128>(src, dst + gi * 4096), ...);
+}
+
+// The two products are issued through inline asm so that they keep the
+// order written below: the compiler may not sink the softmax arithmetic
+// behind them or regroup them, which would serialise the matrix pipe behind
+// LDS latency.  Scores accumulate in ordinary VGPRs (the O accumulators fill
+// the whole accumulation register file), O in accumulation registers.  The
+// compiler does not see these as MFMAs, so the wait states it would insert
+// are spelled out: two before each product (an operand may have just been
+// written by a VALU instruction), none between back-to-back products
+// accumulating into the same registers, and an explicit drain after the last
+// product into an accumulator before any other instruction reads it.
+__device__ __forceinline__ void mfma_first(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_a(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// Wait states between the last product writing an accumulator and any other
+// access to it: at least 18 for this product (s_nop n waits n + 1).
+__device__ __forceinline__ void drain_v(f32x16_t& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(c));
+}
+// Pins the computation of x before this point of the instruction stream.
+__device__ __forceinline__ void anchor(float x) { asm volatile("" ::"v"(x)); }
 
 __device__ __forceinline__ unsigned lds_address(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS const void*)p));
@@ -96,22 +144,13 @@ __device__ __forceinline__ int swz(int n, int chunk) {
 
 template <bool kPaged>
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
-  // Four ring stages (3 tiles in flight) plus the score exchange fill the
-  // 160 KiB of LDS exactly.  The stages are distinct arrays and the loop is
-  // unrolled over them, so every stage offset is a compile-time constant.
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) float xch[kXchBytes / 4];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int hb = wave >> 1, hf = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
 
   // XCD-aware work mapping: workgroup x runs on XCD x % 8; give every XCD a
-  // contiguous range of work ids so the head groups of one partition
-  // (adjacent ids) share that XCD's L2.
+  // contiguous range of work ids (the partitions of a request stay together).
   const int nwg = gridDim.x;
   const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
   if (work >= p.work_items) return;
@@ -125,23 +164,22 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   const int t1 = min(t0 + p.split_tokens, len);
   if (t0 >= t1) return;  // the combine never reads partitions past the length
 
-  const int hblock = g * 2 + hb;
+  const int hblock = g * 4 + wave;
   const int head = hblock * 32 + l32;
 
   // Query as the B operand: lane holds head `head`, K slots half*8..+7 of
-  // each of this wave's 18 K-steps.
-  bf16x8_t qf[kHalfKSteps];
+  // each of the 36 K-steps.
+  bf16x8_t qf[kKSteps];
   {
-    const uint16_t* qrow = p.q_cat + (static_cast<size_t>(b) * p.n_heads + head) * kRow +
-                           hf * (kRow / 2) + half * 8;
+    const uint16_t* qrow = p.q_cat + (static_cast<size_t>(b) * p.n_heads + head) * kRow + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < kHalfKSteps; ++ks)
+    for (int ks = 0; ks < kKSteps; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
   }
 
-  f32x16_t acc[kHalfCBlocks];
+  f32x16_t acc[kCBlocks];
 #pragma unroll
-  for (int cb = 0; cb < kHalfCBlocks; ++cb)
+  for (int cb = 0; cb < kCBlocks; ++cb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
   float m = -INFINITY, l = 0.f;
@@ -170,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       page_of_lane = p.cache.page_table[static_cast<size_t>(b) * p.cache.max_pages +
                                         first_page + lane];
   }
-  auto issue_tile = [&](uint8_t* stage, int tile_t0) {
+  auto issue_tile = [&](int stage, int tile_t0) {
     const int t = min(tile_t0 + n_load, t1 - 1);
     const uint8_t* src;
     if constexpr (kPaged) {
@@ -183,144 +221,178 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       src = req_base + static_cast<size_t>(t) * kRowBytes;
     }
     src += chunk_off;
-    const unsigned dst = lds_address(stage) + wave * 1024;
-#pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) load_to_lds16(src + gi * 128, dst + gi * 4096);
+    const unsigned dst = lds_address(lds + stage * kTileBytes) + wave * 1024;
+    load_row_groups(src, dst, std::make_integer_sequence<int, kGroups>{});
   };
 
-  // Per-lane coordinates of the transposing reads of the PV operand.
+  // Per-lane LDS offsets within a tile.  Score operand of K-step ks:
+  // swz(l32, 2 ks + half) = qoff[ks % 4] + (ks / 4) * 4096.  PV operand of
+  // latent block cb, K-step kk, read lo/hi: voff[cb % 2] + (cb / 2) * 4096 +
+  // kk * 2048 + hi * 1024.  The transposing read of lane (16-lane group G,
+  // index r) addresses token {0,8} + (G/2)*4 + r/4 at latent column
+  // 16*(G%2) + 4*(r%4) of its block.
   const int tr_tok = (half << 2) + ((lane >> 2) & 3);
   const int tr_col = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
+  int qoff0[4], voff0[2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) qoff0[q] = lds_address(lds) + swz(l32, q * 2 + half);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = q * 32 + tr_col;
+    voff0[q] = lds_address(lds) + swz(tr_tok, c >> 3) + (c & 7) * 2;
+  }
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+
+  // Operand reads.  Score operand of K-step ks of the tile whose offsets are
+  // in `qoff`; PV operand i = kk * 16 + cb of the tile whose offsets are in
+  // `voff` (consecutive PV MFMAs then update different accumulators).
+  auto read_k = [&](const int (&qoff)[4], int ks) {
+    return *(MLA_LDS const bf16x8_t*)(uintptr_t)(qoff[ks & 3] + (ks >> 2) * 4096);
+  };
+  auto read_v = [&](const int (&voff)[2], int i) {
+    const int kk = i >> 4, cb = i & 15;
+    const unsigned a = voff[cb & 1] + (cb >> 1) * 4096 + kk * 2048;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4_t*)(uintptr_t)a);
+    const i16x4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4_t*)(uintptr_t)(a + 1024));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // Operand offsets of ring stages; the empty asm keeps the compiler from
+  // precomputing every operand address of every stage.
+  auto k_offsets = [&](int stage, int (&qoff)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) qoff[q] = qoff0[q] + stage * kTileBytes;
+    asm volatile("" : "+v"(qoff[0]), "+v"(qoff[1]), "+v"(qoff[2]), "+v"(qoff[3]));
+  };
+  auto v_offsets = [&](int stage, int (&voff)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) voff[q] = voff0[q] + stage * kTileBytes;
+    asm volatile("" : "+v"(voff[0]), "+v"(voff[1]));
+  };
+
+  // Scores S^T accumulate in one chain; inside a step its MFMAs alternate
+  // with independent PV MFMAs, which covers the chain's dependency latency.
+  f32x16_t sc;
+  auto qk = [&](bf16x8_t (&ta)[kKSteps], const int (&qoff)[4], int ks) {
+    if (ks + kKWindow < kKSteps) ta[ks + kKWindow] = read_k(qoff, ks + kKWindow);
+    if (ks == 0)
+      mfma_first(sc, ta[ks], qf[ks]);
+    else
+      mfma_v(sc, ta[ks], qf[ks]);
+  };
+
   // Prologue: tiles 0..2 in flight, then one wait (visible to the compiler)
-  // for them and for the query fragments, which every step needs at once.
-  // From here on the compiler sees no outstanding loads, and the tile loads
-  // are governed only by the waits below.  Every step issues exactly one
-  // tile (past the last tile they re-read the partition's last row into a
-  // stage that is never read again), so "this wave's loads of tile it have
-  // landed" is always vmcnt(18): the two younger tiles may stay in flight.
-  issue_tile(stage0, t0);
-  issue_tile(stage1, t0 + kTile);
-  issue_tile(stage2, t0 + 2 * kTile);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  // for tile 0 and the query fragments.  From here on the compiler sees no
+  // outstanding loads, and the tile loads are governed only by the waits
+  // below.  Every step issues exactly one tile (past the last tile they
+  // re-read the partition's last row into a stage that is never read
+  // again), so "this wave's loads of tile t have landed" while two younger
+  // tiles may stay in flight is always vmcnt(2 * kGroups).
+  issue_tile(0, t0);
+  issue_tile(1, t0 + kTile);
+  issue_tile(2, t0 + 2 * kTile);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGroups));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
-  // One step: tile `it` is in `tile`; tile it+3 is loaded into `next3`.
-  auto step = [&](int it, const uint8_t* tile, uint8_t* next3) {
-    // Wait for this wave's loads of tile `it` (those of tile it+1 may stay in
-    // flight), then for everyone's.  A raw s_barrier, not __syncthreads(): the
-    // latter also waits for every outstanding global load and would drain the
-    // prefetch at each barrier.  The compiler fence keeps LDS accesses on
-    // their side of the barrier.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGroups));
+  // Scores of tile 0.
+  {
+    int qoff[4];
+    k_offsets(0, qoff);
+    bf16x8_t ta[kKSteps];
+#pragma unroll
+    for (int ks = 0; ks < kKWindow; ++ks) ta[ks] = read_k(qoff, ks);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qk(ta, qoff, ks);
+    drain_v(sc);
+  }
+
+  // One step: the softmax of tile t (stage t % 4) is issued between the first
+  // score MFMAs of tile t+1 (stage (t+1) % 4); then every PV MFMA of tile t
+  // is paired with a score MFMA of tile t+1.
+  auto step = [&](int t, auto has_next) {
+    constexpr bool kNext = decltype(has_next)::value;
+    // Wait for this wave's loads of tile t+1 (tile t+2 may stay in flight),
+    // then for everyone's.  A raw s_barrier, not __syncthreads(): the latter
+    // also waits for every outstanding global load and would drain the
+    // prefetch.  The compiler fence keeps LDS accesses on their side of the
+    // barrier.  After it every wave is past step t-1, so the stage of tile
+    // t-1, (t+3) % 4, is refilled with tile t+3.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroups));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // Everyone is past step it-1, whose stage is `next3`: refill it.
-    issue_tile(next3, t0 + (it + 3) * kTile);
+    issue_tile((t + 3) & (kStages - 1), t0 + (t + 3) * kTile);
 
-    const int nvalid = t1 - (t0 + it * kTile);
-
-    // Per-lane LDS offsets.  Score operand of K-step ks: swz(l32, chunk) with
-    // chunk = 36 hf + 2 ks + half, which equals qoff[ks % 4] + (ks / 4) * 4096.
-    // PV operand of latent block cb, K-step kk, read lo/hi:
-    // voff[cb % 2] + (cb / 2) * 4096 + kk * 2048 + hi * 1024.  The empty asm
-    // keeps these few offsets from being hoisted out of the loop per stage
-    // (three stages x 50 addresses would not fit in registers).
+    const int nvalid = t1 - (t0 + t * kTile);
     int qoff[4], voff[2];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) qoff[q] = swz(l32, (hf * kHalfKSteps + q) * 2 + half);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int c = (hf * kHalfCBlocks + q) * 32 + tr_col;
-      voff[q] = swz(tr_tok, c >> 3) + (c & 7) * 2;
-    }
-    asm volatile("" : "+v"(qoff[0]), "+v"(qoff[1]), "+v"(qoff[2]), "+v"(qoff[3]),
-                 "+v"(voff[0]), "+v"(voff[1]));
+    k_offsets((t + 1) & (kStages - 1), qoff);
+    v_offsets(t & (kStages - 1), voff);
 
-    // Partial S^T[token, head] over this wave's half of K.  All 18 operand
-    // reads are issued before the MFMA chain so LDS latency overlaps it.
-    bf16x8_t ta[kHalfKSteps];
-#pragma unroll
-    for (int ks = 0; ks < kHalfKSteps; ++ks)
-      ta[ks] = *reinterpret_cast<const bf16x8_t*>(tile + qoff[ks & 3] + (ks >> 2) * 4096);
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMA chain
-    f32x16_t sacc;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < kHalfKSteps; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[ks], qf[ks], sacc, 0, 0, 0);
-
-    // Sum the two half-K partials of this head block through LDS.  Both waves
-    // add (K-half 0) + (K-half 1) in that order, so their scores match bitwise.
-    // One buffer serves every step: each wave consumes its partner's values
-    // (softmax below) before it reaches the next step's barrier, and nobody
-    // rewrites the buffer before passing that barrier.
-    float* xw = xch + hb * 2 * 1024;  // [wave of pair][reg][lane]
-#pragma unroll
-    for (int v = 0; v < 16; v += 4)
-      *reinterpret_cast<f32x4_t*>(xw + hf * 1024 + v * 64 + lane * 4) =
-          f32x4_t{sacc[v], sacc[v + 1], sacc[v + 2], sacc[v + 3]};
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the exchange writes are done
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-
-    // O^T[latent, head] += V^T[latent, token] . P^T[token, head] over this
-    // wave's 256 latent columns.  K slot j of lane half `half` in K-step kk is
-    // token kk*16 + (j/4)*8 + half*4 + j%4, matching the P^T registers below.
-    // The A operand (lane: one latent column, 8 tokens) comes from two
-    // transposing LDS reads: within each 16-lane group, ds_read_b64_tr_b16
-    // gives lane i the (i%4)-th element of the 8-byte chunk addressed by lane
-    // 4j + i/4, for j = 0..3.  So lane (group G, index r) addresses token
-    // kk*16 + {0,8} + (G/2)*4 + r/4 at latent column 16*(G%2) + 4*(r%4).
-    // The first half of these reads is issued before the softmax math, which
-    // then runs while they are in flight.
-    bf16x8_t va[kHalfCBlocks][2];
-    auto read_v = [&](int cb) {
-      const uint8_t* vb = tile + voff[cb & 1] + (cb >> 1) * 4096;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const i16x4_t lo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4_t*)(vb + kk * 2048));
-        const i16x4_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4_t*)(vb + kk * 2048 + 1024));
-        va[cb][kk] =
-            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
-#pragma unroll
-    for (int cb = 0; cb < kHalfCBlocks / 2; ++cb) read_v(cb);
-    __builtin_amdgcn_sched_barrier(0);
-
+    // The scores of tile t leave the accumulators.
     float sv[16];
 #pragma unroll
-    for (int v = 0; v < 16; v += 4) {
-      const f32x4_t o =
-          *reinterpret_cast<const f32x4_t*>(xw + (hf ^ 1) * 1024 + v * 64 + lane * 4);
+    for (int v = 0; v < 16; ++v) sv[v] = sc[v];
+
+    bf16x8_t ta[kKSteps];
+    if constexpr (kNext) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[v + r] = hf == 0 ? sacc[v + r] + o[r] : o[r] + sacc[v + r];
+      for (int ks = 0; ks < kKWindow; ++ks) ta[ks] = read_k(qoff, ks);
     }
 
-    // Accumulator row of register v in this lane: token (v/4)*8 + half*4 + v%4.
+    // Softmax of tile t, without branches: the new running max is decided
+    // here, the (rare) accumulator rescale it implies runs after the lead-in.
+    // Accumulator row of register v in this lane: token (v/4)*8 + half*4 +
+    // v%4, valid while (v/4)*8 + v%4 < nvalid - half*4.
+    const int lim = nvalid - half * 4;
     float tmax = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int n = (v >> 2) * 8 + half * 4 + (v & 3);
-      sv[v] = n < nvalid ? sv[v] * p.scale_log2 : -INFINITY;
+    for (int v = 0; v < 8; ++v) {
+      sv[v] = (v >> 2) * 8 + (v & 3) < lim ? sv[v] * p.scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sv[v]);
+    }
+    anchor(tmax);
+    if constexpr (kNext) { qk(ta, qoff, 0); qk(ta, qoff, 1); }
+#pragma unroll
+    for (int v = 8; v < 16; ++v) {
+      sv[v] = (v >> 2) * 8 + (v & 3) < lim ? sv[v] * p.scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, sv[v]);
     }
     tmax = halves_max(tmax);
+    const bool rescale = __builtin_amdgcn_ballot_w64(tmax > m + kRescaleThreshold) != 0;
+    const float m_new = rescale ? fmaxf(m, tmax) : m;
+    anchor(m_new);
+    if constexpr (kNext) { qk(ta, qoff, 2); qk(ta, qoff, 3); }
+    bf16x8_t pb[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const float pv = __builtin_amdgcn_exp2f(sv[v] - m_new);
+      psum += pv;
+      pb[0][v] = static_cast<__bf16>(pv);
+    }
+    anchor(psum);
+    if constexpr (kNext) { qk(ta, qoff, 4); qk(ta, qoff, 5); }
+#pragma unroll
+    for (int v = 8; v < 16; ++v) {
+      const float pv = __builtin_amdgcn_exp2f(sv[v] - m_new);
+      psum += pv;
+      pb[1][v - 8] = static_cast<__bf16>(pv);
+    }
+    anchor(psum);
+    if constexpr (kNext) { qk(ta, qoff, 6); qk(ta, qoff, 7); }
 
-    if (__builtin_amdgcn_ballot_w64(tmax > m + kRescaleThreshold) != 0) {
-      const float m_new = fmaxf(m, tmax);
+    bf16x8_t va[kPv];
+#pragma unroll
+    for (int i = 0; i < kVWindow; ++i) va[i] = read_v(voff, i);
+
+    if (rescale) {
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
-      // Scale the accumulators in place in the accumulation registers: going
-      // through inline asm keeps the compiler from giving all accumulator
-      // values a second home in ordinary VGPRs.  The MFMAs that last wrote
-      // them retired a whole score pass ago; the s_nops cover the
-      // MFMA-to-read wait states regardless.
+      // Scale the accumulators in place in the accumulation registers.  The
+      // PV MFMAs that last wrote them retired a whole score pass ago; the
+      // s_nops cover the MFMA-to-read wait states regardless.
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
 #pragma unroll
-      for (int cb = 0; cb < kHalfCBlocks; ++cb)
+      for (int cb = 0; cb < kCBlocks; ++cb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float x = acc[cb][v], tmp;
@@ -333,49 +405,55 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
           acc[cb][v] = x;
         }
       l *= alpha;
-      m = m_new;
-    }
-
-    bf16x8_t pb[2];
-    float psum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float pv = __builtin_amdgcn_exp2f(sv[v] - m);
-      psum += pv;
-      pb[v >> 3][v & 7] = static_cast<__bf16>(pv);
     }
     l += psum;
+    m = m_new;
 
+    // PV of tile t, each MFMA paired with the next score MFMA of tile t+1.
 #pragma unroll
-    for (int cb = kHalfCBlocks / 2; cb < kHalfCBlocks; ++cb) read_v(cb);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < kPv; ++i) {
+      if (i + kVWindow < kPv) va[i + kVWindow] = read_v(voff, i + kVWindow);
+      mfma_a(acc[i & 15], va[i], pb[i >> 4]);
+      if constexpr (kNext) {
+        if (kQkLead + i < kKSteps) qk(ta, qoff, kQkLead + i);
+      }
+    }
+    if constexpr (kNext) {
 #pragma unroll
-    for (int cb = 0; cb < kHalfCBlocks; ++cb)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb][kk], pb[kk], acc[cb], 0, 0, 0);
+      for (int ks = kQkLead + kPv; ks < kKSteps; ++ks) qk(ta, qoff, ks);
+      drain_v(sc);
+    }
   };
 
-  for (int it = 0; it < ntiles; it += kStages) {
-    step(it, stage0, stage3);
-    if (it + 1 < ntiles) step(it + 1, stage1, stage0);
-    if (it + 2 < ntiles) step(it + 2, stage2, stage1);
-    if (it + 3 < ntiles) step(it + 3, stage3, stage2);
-  }
-  // The trailing loads must land before the workgroup's LDS is released.
+  for (int t = 0; t + 1 < ntiles; ++t) step(t, std::true_type{});
+  step(ntiles - 1, std::false_type{});
+  // The trailing loads must land before the workgroup's LDS is released, and
+  // the last PV products before the accumulators are read.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+  for (int cb = 0; cb < kCBlocks; ++cb) asm volatile("" : "+a"(acc[cb]));
 
   // Softmax sum over both lane halves (each half saw half of the tokens).
   l = halves_sum(l);
   const float inv = 1.f / l;
-  float* dst = p.part_o +
-               ((static_cast<size_t>(b) * p.num_splits + s) * (p.n_heads / 32) + hblock) * 16384 +
-               hf * kHalfCBlocks * 1024 + lane;
+  // bf16 partial, 16 contiguous values per lane and latent block:
+  // part_o[((((b * S + s) * NHB + hblock) * 16 + cb) * 64 + lane) * 16 + v].
+  uint16_t* dst = p.part_o +
+                  ((static_cast<size_t>(b) * p.num_splits + s) * (p.n_heads / 32) + hblock) * 16384 +
+                  lane * 16;
 #pragma unroll
-  for (int cb = 0; cb < kHalfCBlocks; ++cb)
+  for (int cb = 0; cb < kCBlocks; ++cb) {
+    bf16x8_t lo, hi;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) dst[(cb * 16 + v) * 64] = acc[cb][v] * inv;
-  if (hf == 0 && half == 0)
+    for (int v = 0; v < 8; ++v) {
+      lo[v] = static_cast<__bf16>(acc[cb][v] * inv);
+      hi[v] = static_cast<__bf16>(acc[cb][v + 8] * inv);
+    }
+    *reinterpret_cast<bf16x8_t*>(dst + cb * 1024) = lo;
+    *reinterpret_cast<bf16x8_t*>(dst + cb * 1024 + 8) = hi;
+  }
+  if (half == 0)
     p.part_lse[(static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + head] =
         (m + __log2f(l)) * kLn2;
 }
@@ -393,7 +471,7 @@ hipError_t launch_partials_mfma(const DecodeArgs& a) {
   p.head_groups = a.head_groups;
   p.work_items = a.batch * a.num_splits * a.head_groups;
   p.scale_log2 = a.softmax_scale * kLog2e;
-  p.part_o = a.part_o;
+  p.part_o = static_cast<uint16_t*>(a.part_o);
   p.part_lse = a.part_lse;
   const int grid = (p.work_items + 7) / 8 * 8;  // multiple of the 8 XCDs
   if (a.cache.page_table != nullptr)

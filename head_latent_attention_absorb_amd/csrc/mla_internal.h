@@ -9,8 +9,9 @@
 namespace mla {
 
 // Split-KV partial results of the decode kernels live in the caller's
-// workspace: fp32 partial outputs (normalised by their own softmax sum) and
-// fp32 natural-log sum-exp per (request, split, head).
+// workspace: partial outputs normalised by their own softmax sum (fp32 from
+// the generic kernel, bf16 from the MFMA kernel) and the fp32 natural-log
+// sum-exp per (request, split, head).
 struct PartialLayout {
   enum Kind { kRowMajor = 0, kFragment = 1 };
 };
@@ -32,7 +33,7 @@ struct DecodeArgs {
   int32_t split_tokens, num_splits, head_groups;
   void* out_lat;
   float* lse;           // may be nullptr
-  float* part_o;        // workspace
+  void* part_o;         // workspace: fp32 (generic kernel) or bf16 (MFMA kernel)
   float* part_lse;      // workspace
   hipStream_t stream;
 };
@@ -50,14 +51,14 @@ hipError_t launch_out_uv(int dtype, int batch, int n_heads, int d_head, int d_la
 // storage), row-major partial layout.
 hipError_t launch_partials_generic(const DecodeArgs& a);
 // bf16 MFMA split-KV partials for d_latent = 512, d_rope = 64,
-// n_heads % 64 == 0, fragment-order partial layout.
+// n_heads % 128 == 0, fragment-order partial layout.
 hipError_t launch_partials_mfma(const DecodeArgs& a);
 // Merge the partials of each request into out_lat / lse.  `fragment` selects
 // the partial layout written by the MFMA kernel.
 hipError_t launch_combine(const DecodeArgs& a, bool fragment);
 
 // Constants of the MFMA decode kernel that the planner needs.
-constexpr int kMfmaHeadsPerGroup = 64;   // heads handled by one workgroup
+constexpr int kMfmaHeadsPerGroup = 128;  // heads handled by one workgroup
 constexpr int kMfmaTokenGranule = 32;    // tokens consumed per workgroup iteration
 
 }  // namespace mla
