@@ -19,7 +19,8 @@
 //    staging) through a 4-stage ring.  A 32-token tile is stored column-group
 //    major: the 576-element row is cut into 9 groups of 64 elements (128 B);
 //    group g of token n sits at ((g * 32 + n) * 128), its eight 16-byte chunks
-//    XOR-swizzled by (n & 7) so MFMA operand reads are conflict free.  A load
+//    XOR-swizzled by a key of n (swz_key) so that both MFMA operand reads are
+//    free of bank conflicts on the 64-bank LDS.  A load
 //    instruction fills 8 tokens x one group: each lane owns one token row per
 //    tile and every global access is a whole 128-byte segment.
 //  * Scores are computed transposed, S^T[token, head] = tile . Q^T, with
@@ -126,7 +127,11 @@ __device__ __forceinline__ void mfma_a(f32x16_t& c, const bf16x8_t& a, const bf1
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 // Wait states between the last product writing an accumulator and any other
-// access to it: at least 18 for this product (s_nop n waits n + 1).
+// access to it: at least 18 once the product has started (s_nop n waits
+// n + 1).  An MFMA issued right behind an independent one may start up to a
+// whole product later, so every drain below follows either a dependent chain
+// (which starts each product as soon as it issues) or further MFMAs, or uses
+// the longer drain at the end of the kernel.
 __device__ __forceinline__ void drain_v(f32x16_t& c) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(c));
 }
@@ -137,9 +142,20 @@ __device__ __forceinline__ unsigned lds_address(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS const void*)p));
 }
 
+// XOR key of token n's 128-byte rows.  The LDS has 64 four-byte banks: 16
+// lanes reading one chunk of 16 consecutive tokens (the score operand) and
+// 32 lanes reading four chunks of 4 consecutive tokens (the transposing PV
+// operand read) each cover all 64 banks exactly once.  Rows of tokens of one
+// parity share a bank half, so the key is a bijection of (n / 2) % 8 whose
+// bit 2 differs between n and n + 2 when n % 4 < 2.
+__device__ __forceinline__ int swz_key(int n) {
+  const int j = (n >> 1) & 7;
+  return j ^ ((j & 1) << 2);
+}
+
 // LDS byte offset (within a tile) of 16-byte chunk `chunk` (0..71) of token `n`.
 __device__ __forceinline__ int swz(int n, int chunk) {
-  return (((chunk >> 3) * kTile + n) << 7) + (((chunk & 7) ^ (n & 7)) << 4);
+  return (((chunk >> 3) * kTile + n) << 7) + (((chunk & 7) ^ swz_key(n)) << 4);
 }
 
 template <bool kPaged>
@@ -186,11 +202,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
 
   // Loader: wave w fills token octet w of every column group.  This lane's
   // token is w*8 + lane/8 and it fills LDS position lane%8 of that token's
-  // group, which holds logical chunk (lane%8) ^ (token & 7).  Rows past the
+  // group, which holds logical chunk (lane%8) ^ swz_key(token).  Rows past the
   // partition are clamped to t1 - 1: never read past the request, and their
   // probabilities are forced to 0.
   const int n_load = wave * 8 + (lane >> 3);
-  const int chunk_off = ((lane & 7) ^ (n_load & 7)) * 16;
+  const int chunk_off = ((lane & 7) ^ swz_key(n_load)) * 16;
   const uint8_t* req_base =
       kPaged ? p.cache.data
              : p.cache.data + static_cast<size_t>(b) * p.cache.max_len * kRowBytes;
@@ -227,19 +243,19 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
 
   // Per-lane LDS offsets within a tile.  Score operand of K-step ks:
   // swz(l32, 2 ks + half) = qoff[ks % 4] + (ks / 4) * 4096.  PV operand of
-  // latent block cb, K-step kk, read lo/hi: voff[cb % 2] + (cb / 2) * 4096 +
-  // kk * 2048 + hi * 1024.  The transposing read of lane (16-lane group G,
+  // latent block cb, K-step kk, read lo/hi (tokens 8 apart, which have
+  // different XOR keys): voff[hi * 2 + cb % 2] + (cb / 2) * 4096 + kk * 2048.  The transposing read of lane (16-lane group G,
   // index r) addresses token {0,8} + (G/2)*4 + r/4 at latent column
   // 16*(G%2) + 4*(r%4) of its block.
   const int tr_tok = (half << 2) + ((lane >> 2) & 3);
   const int tr_col = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
-  int qoff0[4], voff0[2];
+  int qoff0[4], voff0[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) qoff0[q] = lds_address(lds) + swz(l32, q * 2 + half);
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = q * 32 + tr_col;
-    voff0[q] = lds_address(lds) + swz(tr_tok, c >> 3) + (c & 7) * 2;
+  for (int q = 0; q < 4; ++q) {
+    const int c = (q & 1) * 32 + tr_col;
+    voff0[q] = lds_address(lds) + swz(tr_tok + (q >> 1) * 8, c >> 3) + (c & 7) * 2;
   }
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
 
@@ -249,12 +265,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   auto read_k = [&](const int (&qoff)[4], int ks) {
     return *(MLA_LDS const bf16x8_t*)(uintptr_t)(qoff[ks & 3] + (ks >> 2) * 4096);
   };
-  auto read_v = [&](const int (&voff)[2], int i) {
+  auto read_v = [&](const int (&voff)[4], int i) {
     const int kk = i >> 4, cb = i & 15;
-    const unsigned a = voff[cb & 1] + (cb >> 1) * 4096 + kk * 2048;
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4_t*)(uintptr_t)a);
-    const i16x4_t hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4_t*)(uintptr_t)(a + 1024));
+    const unsigned a = (cb >> 1) * 4096 + kk * 2048;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MLA_LDS i16x4_t*)(uintptr_t)(voff[cb & 1] + a));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MLA_LDS i16x4_t*)(uintptr_t)(voff[2 + (cb & 1)] + a));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // Operand offsets of ring stages; the empty asm keeps the compiler from
@@ -264,10 +281,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     for (int q = 0; q < 4; ++q) qoff[q] = qoff0[q] + stage * kTileBytes;
     asm volatile("" : "+v"(qoff[0]), "+v"(qoff[1]), "+v"(qoff[2]), "+v"(qoff[3]));
   };
-  auto v_offsets = [&](int stage, int (&voff)[2]) {
+  auto v_offsets = [&](int stage, int (&voff)[4]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) voff[q] = voff0[q] + stage * kTileBytes;
-    asm volatile("" : "+v"(voff[0]), "+v"(voff[1]));
+    for (int q = 0; q < 4; ++q) voff[q] = voff0[q] + stage * kTileBytes;
+    asm volatile("" : "+v"(voff[0]), "+v"(voff[1]), "+v"(voff[2]), "+v"(voff[3]));
   };
 
   // Scores S^T accumulate in one chain; inside a step its MFMAs alternate
@@ -324,7 +341,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     issue_tile((t + 3) & (kStages - 1), t0 + (t + 3) * kTile);
 
     const int nvalid = t1 - (t0 + t * kTile);
-    int qoff[4], voff[2];
+    int qoff[4], voff[4];
     k_offsets((t + 1) & (kStages - 1), qoff);
     v_offsets(t & (kStages - 1), voff);
 
@@ -430,7 +447,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // The trailing loads must land before the workgroup's LDS is released, and
   // the last PV products before the accumulators are read.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
   for (int cb = 0; cb < kCBlocks; ++cb) asm volatile("" : "+a"(acc[cb]));
 
