@@ -2,8 +2,9 @@
 """Benchmark: MLA absorbed decode on one MI355X, DeepSeek-V2 shape B=16, T=4096.
 
 A step is one whole decode step of one layer on one batch of synthetic input:
-    mla_absorb_q -> mla_decode_partials -> mla_decode_combine -> mla_out_uv
-(the last two together are mla_decode_attn).  Inputs are resident in HBM
+    mla_absorb_q -> mla_decode_partials -> mla_decode_combine_out
+(the last merges the split partials and applies W^UV in one kernel; it does
+exactly what mla_decode_combine followed by mla_out_uv does).  Inputs are resident in HBM
 before the timed region.  Every step uses the next entry of a rotating pool of
 independently seeded (cache, W^UK, W^UV, q) sets totalling > 512 MB, twice the
 256 MB Infinity Cache, so the cache bytes really come from HBM.
@@ -171,12 +172,9 @@ def main():
         mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
         if ev is not None:
             ev[2].record(stream)
-        mla.decode_combine(e.cache, nh, plan, ws, o_lat, lse)
+        mla.decode_combine_out(e.cache, plan, ws, e.w_uv, o_lat, lse, out=o)
         if ev is not None:
             ev[3].record(stream)
-        mla.out_uv(o_lat, e.w_uv, out=o)
-        if ev is not None:
-            ev[4].record(stream)
 
     for i in range(args.warmup):
         step(pool[i % n_pool])
@@ -194,28 +192,32 @@ def main():
     ms_per_step = e_start.elapsed_time(e_end) / args.steps
 
     # Same steps again with HIP events between the kernels (per-kernel times).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(pool[i % n_pool], evs[i])
     torch.cuda.synchronize()
-    phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(4)] for ev in evs])
+    phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(3)] for ev in evs])
     phase_us = phase.mean(axis=0) * 1e3
-    absorb_us, partials_us, combine_us, out_uv_us = (float(x) for x in phase_us)
-    attn_us = partials_us + combine_us
+    absorb_us, partials_us, tail_us = (float(x) for x in phase_us)
     log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, partials "
-        f"{partials_us:.1f}, combine {combine_us:.1f}, out_uv {out_uv_us:.1f}")
+        f"{partials_us:.1f}, combine+out_uv {tail_us:.1f}")
 
     # Algorithmic work (split partials excluded).
     tokens = int(sum(int(x) for x in pool[0].case.seq_lens))
     cache_bytes = tokens * row * 2
     q_bytes = B * nh * row * 2
-    olat_bytes = B * nh * cfg.d_latent * 2 + B * nh * 4
     flops = 2.0 * nh * (row + cfg.d_latent) * tokens
     k2_bytes = cache_bytes + q_bytes
     k2_gbps = k2_bytes / (partials_us * 1e-6) / 1e9
-    attn_bytes = cache_bytes + q_bytes + olat_bytes
-    t_roof_us = max(attn_bytes / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    # Whole step: the cache, both up-projection weights, the query in and the
+    # output out, each moved once.
+    w_bytes = 2 * nh * cfg.d_head * cfg.d_latent * 2
+    io_bytes = B * nh * (cfg.d_head + cfg.d_rope) * 2 + B * nh * cfg.d_head * 2
+    step_bytes = cache_bytes + w_bytes + io_bytes
+    step_flops = flops + 2.0 * 2 * B * nh * cfg.d_head * cfg.d_latent
+    t_roof_us = max(step_bytes / (HBM_PEAK_GBPS * 1e9),
+                    step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
     sha = kernel_sha()
 
     result = {
@@ -238,11 +240,11 @@ def main():
             "rotating_pool_mb": round(pool_mb), "split_tokens": plan.split_tokens,
             "num_splits": plan.num_splits, "parallelism": "single-gpu",
         },
-        "latent_cache_GBps": cache_bytes / (attn_us * 1e-6) / 1e9,
-        "decode_attn_us": attn_us,
-        "decode_attn_pct_roofline": 100.0 * t_roof_us / attn_us,
+        "latent_cache_GBps": cache_bytes / (partials_us * 1e-6) / 1e9,
+        "step_roofline_us": t_roof_us,
+        "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
         "kernels_us": {"absorb_q": absorb_us, "decode_partials": partials_us,
-                       "decode_combine": combine_us, "out_uv": out_uv_us},
+                       "decode_combine_out": tail_us},
         "roofline": {
             "kernel": "decode_mfma_kernel (mla_decode_partials)",
             "bound": "hbm",

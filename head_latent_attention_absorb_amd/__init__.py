@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_combine.restype = ctypes.c_int
     L.mla_decode_combine.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(CacheDesc),
                                      ctypes.POINTER(Plan), vp, sz, vp, vp, vp]
+    L.mla_decode_combine_out.restype = ctypes.c_int
+    L.mla_decode_combine_out.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(CacheDesc),
+                                         ctypes.POINTER(Plan), vp, sz, vp, vp, vp, vp, vp]
     L.mla_out_uv.restype = ctypes.c_int
     L.mla_out_uv.argtypes = [ctypes.POINTER(Dims), i32, vp, vp, vp, vp]
     _lib = L
@@ -257,6 +260,28 @@ def decode_combine(cache: LatentCache, n_heads: int, plan: Plan, workspace: torc
     _check("mla_decode_combine", lib().mla_decode_combine(
         ctypes.byref(dims), B, ctypes.byref(desc), ctypes.byref(plan), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def decode_combine_out(cache: LatentCache, plan: Plan, workspace: torch.Tensor,
+                       w_uv: torch.Tensor, out_lat: torch.Tensor,
+                       lse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """decode_combine then out_uv in one call: merges the partials into out_lat
+    (and lse) and returns o[b,i,h] = sum_c o_lat[b,i,c] W^UV[i,c,h]."""
+    B = cache.batch()
+    nh, dc, dh = w_uv.shape
+    d_rope = int(cache.d_rope)
+    dims = make_dims(nh, dh, d_rope, dc, _dtype_code(out_lat))
+    _require(out_lat, "out_lat", (B, nh, dc), w_uv.dtype, w_uv.device)
+    if out is None:
+        out = torch.empty((B, nh, dh), dtype=w_uv.dtype, device=w_uv.device)
+    _require(out, "out", (B, nh, dh), w_uv.dtype, w_uv.device)
+    desc = cache.desc()
+    _check("mla_decode_combine_out", lib().mla_decode_combine_out(
+        ctypes.byref(dims), B, ctypes.byref(desc), ctypes.byref(plan), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(w_uv), _ptr(out), _ptr(out_lat),
+        _ptr(lse), _stream(stream)))
+    return out
 
 
 def out_uv(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None,

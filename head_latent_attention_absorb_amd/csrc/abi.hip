@@ -297,6 +297,35 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* 
   return run_combine(a, p);
 }
 
+mla_status_t mla_decode_combine_out(const mla_dims_t* dims, int32_t batch,
+                                    const mla_cache_t* cache, const mla_decode_plan_t* plan,
+                                    const void* workspace, size_t workspace_bytes,
+                                    const void* w_uv, void* out, void* out_lat, float* lse,
+                                    void* stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch < 0) return MLA_ERR_DIMS;
+  if (batch > 0) {
+    if (w_uv == nullptr || out == nullptr) return MLA_ERR_NULL;
+    if (!aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  }
+  mla_decode_plan_t p;
+  DecodeArgs a;
+  st = prepare_decode(dims, batch, nullptr, cache, 0.f, plan, out_lat, lse, workspace,
+                      workspace_bytes, stream, kCombine, &p, &a);
+  if (st != MLA_OK || batch == 0) return st;
+  (void)hipGetLastError();
+  if (p.kernel == 1 && mla::combine_out_fusable(dims->d_latent, dims->d_head)) {
+    const hipError_t e = mla::launch_combine_rows(a, w_uv, out, dims->d_head);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+  }
+  if ((st = run_combine(a, p)) != MLA_OK) return st;
+  const hipError_t e = mla::launch_out_uv(dims->dtype, batch, dims->n_heads, dims->d_head,
+                                          dims->d_latent, out_lat, w_uv, out, a.stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
 mla_status_t mla_out_uv(const mla_dims_t* dims, int32_t batch, const void* out_lat,
                         const void* w_uv, void* out, void* stream) {
   mla_status_t st = check_dims(dims);

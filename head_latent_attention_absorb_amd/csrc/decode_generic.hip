@@ -145,78 +145,6 @@ __global__ __launch_bounds__(kThreads) void combine_rowmajor_kernel(
 }  // namespace
 
 // Combine for fragment-order partials written by the MFMA decode kernel.
-// Fragment layout of the MFMA kernel's bf16 partials, per (request b, split
-// s, 32-head block hb, 32-column latent block cb), 16 contiguous values per
-// lane:
-//   part_o[((((b * S + s) * NHB + hb) * 16 + cb) * 64 + lane) * 16 + v]
-//     = O[head hb*32 + lane%32][latent cb*32 + (v/4)*8 + (lane/32)*4 + v%4]
-// One wave per (request, hb, cb): grid x = (NHB * 16) / 4, y = request.  The
-// splits are consumed kCombineBatch at a time with all their loads issued
-// together, so HBM latency is paid once per batch rather than once per split.
-constexpr int kCombineBatch = 8;
-__global__ __launch_bounds__(kThreads) void combine_fragment_kernel(
-    const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ seq_lens, int n_heads, int split_tokens, int num_splits,
-    __bf16* __restrict__ out_lat, float* __restrict__ lse_out) {
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int unit = blockIdx.x * 4 + wave;
-  const int hb = unit >> 4, cb = unit & 15;
-  const int nhb = n_heads / 32;
-  const int head = hb * 32 + (lane & 31), half = lane >> 5;
-  const int ns = used_splits(seq_lens[b], split_tokens);
-  const size_t lbase = static_cast<size_t>(b) * num_splits * n_heads + head;
-  float L = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += kCombineBatch) {
-    float x[kCombineBatch];
-#pragma unroll
-    for (int j = 0; j < kCombineBatch; ++j)
-      x[j] = part_lse[lbase + static_cast<size_t>(min(s0 + j, ns - 1)) * n_heads];
-#pragma unroll
-    for (int j = 0; j < kCombineBatch; ++j) L = fmaxf(L, x[j]);
-  }
-
-  const size_t split_stride = static_cast<size_t>(nhb) * 16 * 64 * 16;
-  const uint16_t* frag = part_o + ((static_cast<size_t>(b) * num_splits * nhb + hb) * 16 + cb) * 1024 +
-                         lane * 16;
-  float acc[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-  float W = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kCombineBatch) {
-    bf16x8_t lo[kCombineBatch], hi[kCombineBatch];
-    float w[kCombineBatch];
-#pragma unroll
-    for (int j = 0; j < kCombineBatch; ++j) {
-      const int s = min(s0 + j, ns - 1);
-      const uint16_t* f = frag + static_cast<size_t>(s) * split_stride;
-      lo[j] = *reinterpret_cast<const bf16x8_t*>(f);
-      hi[j] = *reinterpret_cast<const bf16x8_t*>(f + 8);
-      w[j] = s0 + j < ns ? expf(part_lse[lbase + static_cast<size_t>(s) * n_heads] - L) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < kCombineBatch; ++j) {
-      W += w[j];
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        acc[v] = fmaf(w[j], static_cast<float>(lo[j][v]), acc[v]);
-        acc[v + 8] = fmaf(w[j], static_cast<float>(hi[j][v]), acc[v + 8]);
-      }
-    }
-  }
-  const float invW = ns > 0 ? 1.f / W : 0.f;
-  __bf16* orow = out_lat + static_cast<size_t>(b * n_heads + head) * 512;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    bf16x4_t pk;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pk[r] = static_cast<__bf16>(acc[g * 4 + r] * invW);
-    *reinterpret_cast<bf16x4_t*>(orow + cb * 32 + g * 8 + half * 4) = pk;
-  }
-  if (lse_out != nullptr && cb == 0 && half == 0)
-    lse_out[static_cast<size_t>(b) * n_heads + head] = ns > 0 ? L + logf(W) : -INFINITY;
-}
-
 hipError_t launch_partials_generic(const DecodeArgs& a) {
   if (a.batch == 0) return hipSuccess;
   const int row = a.d_latent + a.d_rope;
@@ -236,12 +164,7 @@ hipError_t launch_partials_generic(const DecodeArgs& a) {
 
 hipError_t launch_combine(const DecodeArgs& a, bool fragment) {
   if (a.batch == 0) return hipSuccess;
-  if (fragment) {
-    combine_fragment_kernel<<<dim3(a.n_heads / 32 * 16 / 4, a.batch), kThreads, 0, a.stream>>>(
-        static_cast<const uint16_t*>(a.part_o), a.part_lse, a.cache.seq_lens, a.n_heads,
-        a.split_tokens, a.num_splits, static_cast<__bf16*>(a.out_lat), a.lse);
-    return hipGetLastError();
-  }
+  if (fragment) return launch_combine_rows(a, nullptr, nullptr, 0);
   const dim3 cgrid(a.n_heads, a.batch);
   if (a.dtype == 0) {
     combine_rowmajor_kernel<float><<<cgrid, kThreads, 0, a.stream>>>(

@@ -454,22 +454,32 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // Softmax sum over both lane halves (each half saw half of the tokens).
   l = halves_sum(l);
   const float inv = 1.f / l;
-  // bf16 partial, 16 contiguous values per lane and latent block:
-  // part_o[((((b * S + s) * NHB + hblock) * 16 + cb) * 64 + lane) * 16 + v].
-  uint16_t* dst = p.part_o +
-                  ((static_cast<size_t>(b) * p.num_splits + s) * (p.n_heads / 32) + hblock) * 16384 +
-                  lane * 16;
+  // bf16 partial, row-major per (request, split, head):
+  // part_o[((b * S + s) * n_heads + head) * 512 + c].  Register v of latent
+  // block cb holds column cb*32 + (v/4)*8 + half*4 + v%4.  The rows pass
+  // through LDS (free once every wave is past its last step) so that each
+  // global store writes a whole 1 KiB row: wave w owns rows w*32 .. w*32+31,
+  // kOutStride bytes apart.
+  constexpr int kOutStride = 1024 + 16;
+  static_assert(4 * 32 * kOutStride <= kLdsBytes, "epilogue rows fit in the ring");
+  __syncthreads();
+  uint8_t* rows = lds + wave * 32 * kOutStride;
 #pragma unroll
-  for (int cb = 0; cb < kCBlocks; ++cb) {
-    bf16x8_t lo, hi;
+  for (int cb = 0; cb < kCBlocks; ++cb)
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      lo[v] = static_cast<__bf16>(acc[cb][v] * inv);
-      hi[v] = static_cast<__bf16>(acc[cb][v + 8] * inv);
+    for (int g = 0; g < 4; ++g) {
+      bf16x4_t v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][g * 4 + e] * inv);
+      *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride + (cb * 32 + g * 8 + half * 4) * 2) = v4;
     }
-    *reinterpret_cast<bf16x8_t*>(dst + cb * 1024) = lo;
-    *reinterpret_cast<bf16x8_t*>(dst + cb * 1024 + 8) = hi;
-  }
+  uint16_t* dst = p.part_o +
+                  ((static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + hblock * 32) * 512 +
+                  lane * 8;
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r)
+    *reinterpret_cast<bf16x8_t*>(dst + r * 512) =
+        *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
   if (half == 0)
     p.part_lse[(static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + head] =
         (m + __log2f(l)) * kLn2;

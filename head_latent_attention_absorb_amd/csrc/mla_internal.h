@@ -54,8 +54,13 @@ hipError_t launch_partials_generic(const DecodeArgs& a);
 // n_heads % 128 == 0, fragment-order partial layout.
 hipError_t launch_partials_mfma(const DecodeArgs& a);
 // Merge the partials of each request into out_lat / lse.  `fragment` selects
-// the partial layout written by the MFMA kernel.
+// the bf16 row-major partials written by the MFMA kernel.
 hipError_t launch_combine(const DecodeArgs& a, bool fragment);
+// Merge of the MFMA kernel's partials into out_lat / lse and, when w_uv is
+// not null, the W^UV product of the merged rows into out in the same kernel
+// (requires combine_out_fusable(d_latent, d_head)).
+bool combine_out_fusable(int d_latent, int d_head);
+hipError_t launch_combine_rows(const DecodeArgs& a, const void* w_uv, void* out, int d_head);
 
 // Constants of the MFMA decode kernel that the planner needs.
 constexpr int kMfmaHeadsPerGroup = 128;  // heads handled by one workgroup

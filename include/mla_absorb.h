@@ -168,6 +168,25 @@ mla_status_t mla_decode_combine(const mla_dims_t* dims, int32_t batch, const mla
                                 size_t workspace_bytes, void* out_lat, float* lse,
                                 void* stream);
 
+/* The tail of a decode step in one pass: mla_decode_combine followed by
+ * mla_out_uv on its result, without a separate launch for the projection.
+ * The merged latent output is the softmax-weighted latent sum of every cached
+ * row; W^UV is applied to it afterwards (V2 read-through section 2.3):
+ *   out_lat[b, i, :] = merged partials of mla_decode_partials (as
+ *                      mla_decode_combine; required)
+ *   lse[b, i]        = merged log-sum-exp (fp32; may be NULL)
+ *   out[b, i, h]     = sum_c out_lat[b, i, c] * w_uv[i, c, h]
+ * w_uv [n_heads, d_latent, d_head] and out [batch, n_heads, d_head] as in
+ * mla_out_uv; dims->d_head must be set.  The projection reads out_lat as
+ * rounded to dims->dtype, exactly as the two separate calls would.  Plan,
+ * workspace, cache and error rules are those of mla_decode_combine; a NULL
+ * w_uv or out returns MLA_ERR_NULL, a misaligned one MLA_ERR_ALIGN. */
+mla_status_t mla_decode_combine_out(const mla_dims_t* dims, int32_t batch,
+                                    const mla_cache_t* cache, const mla_decode_plan_t* plan,
+                                    const void* workspace, size_t workspace_bytes,
+                                    const void* w_uv, void* out, void* out_lat, float* lse,
+                                    void* stream);
+
 /* Apply W^UV after the latent-space sum (V2 read-through section 2.3):
  *   out[b, i, h] = sum_c out_lat[b, i, c] * w_uv[i, c, h]
  * out_lat [batch, n_heads, d_latent], w_uv [n_heads, d_latent, d_head]

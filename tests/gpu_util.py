@@ -58,6 +58,23 @@ class DevCase:
         torch.cuda.synchronize()
         return q_cat, o_lat, lse, o
 
+    def run_fused(self, split_tokens: int = 0):
+        """absorb -> decode partials -> combine fused with W^UV; returns device
+        tensors (q_cat, o_lat, lse, o)."""
+        cfg = self.case.cfg
+        B = cfg.batch
+        q_cat = mla.absorb_q(self.q_c, self.q_r, self.w_uk)
+        plan = mla.decode_plan(cfg.n_heads, cfg.d_latent, cfg.d_rope, q_cat.dtype, self.cache,
+                               split_tokens=split_tokens, d_head=cfg.d_head)
+        ws = mla.workspace_for(plan, q_cat.device)
+        mla.decode_partials(q_cat, self.cache, cfg.scale, plan, ws)
+        o_lat = torch.empty((B, cfg.n_heads, cfg.d_latent), dtype=q_cat.dtype,
+                            device=q_cat.device)
+        lse = torch.empty((B, cfg.n_heads), dtype=torch.float32, device=q_cat.device)
+        o = mla.decode_combine_out(self.cache, plan, ws, self.w_uv, o_lat, lse)
+        torch.cuda.synchronize()
+        return q_cat, o_lat, lse, o
+
 
 def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)

@@ -78,6 +78,16 @@ def test_null_and_bad_dims_rejected_on_host():
     cache = mla.CacheDesc(0x1000, 0x2000, None, 0, 64, 0)
     assert L.mla_decode_attn(ctypes.byref(_dims()), 1, None, ctypes.byref(cache), 1.0, None,
                              fake, None, fake, 1 << 20, None) == 1
+    # Fused combine + W^UV: NULL or misaligned projection operands.
+    assert L.mla_decode_combine_out(ctypes.byref(_dims()), 1, ctypes.byref(cache), None, fake,
+                                    1 << 20, None, fake, fake, None, None) == 1
+    assert L.mla_decode_combine_out(ctypes.byref(_dims()), 1, ctypes.byref(cache), None, fake,
+                                    1 << 20, fake, None, fake, None, None) == 1
+    assert L.mla_decode_combine_out(ctypes.byref(_dims()), 1, ctypes.byref(cache), None, fake,
+                                    1 << 20, ctypes.c_void_p(0x1002), fake, fake, None,
+                                    None) == 5
+    assert L.mla_decode_combine_out(ctypes.byref(_dims()), 0, ctypes.byref(cache), None, None,
+                                    0, None, None, None, None, None) == 0
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")

@@ -132,6 +132,63 @@ def test_chain_small_bf16(cfg):
                  "q_cat")
 
 
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_PAGED], ids=["contiguous", "paged"])
+def test_chain_small_bf16_fused(cfg):
+    """absorb -> partials -> combine fused with W^UV against the oracle."""
+    case = make_case(cfg, 5)
+    _log(f"[chain small fused] {cfg.name} lens={case.seq_lens.tolist()}")
+    _, o_lat, lse, o = DevCase(case).run_fused()
+    o_ref, lse_ref = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
+                                                 case.w_uk, case.w_uv, cfg.scale,
+                                                 case.page_table, cfg.page_size)
+    assert_close(from_dev(o), o_ref, "bf16", "o")
+    assert_close(from_dev(lse), lse_ref, "bf16", "lse")
+
+
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_PAGED], ids=["contiguous", "paged"])
+@pytest.mark.parametrize("split", [0, 64])
+def test_combine_out_matches_separate_calls(cfg, split):
+    """The fused tail writes exactly mla_decode_combine's o_lat and lse, and an
+    o that differs from mla_out_uv(o_lat) only by fp32 summation order."""
+    case = make_case(cfg, 15)
+    _log(f"[combine_out] {cfg.name} split={split}")
+    dc = DevCase(case)
+    q_np = draw_latent_query(cfg, 15)
+    q_dev = _bf16_dev(q_np)
+    plan = mla.decode_plan(cfg.n_heads, cfg.d_latent, cfg.d_rope, torch.bfloat16, dc.cache,
+                           split_tokens=split, d_head=cfg.d_head)
+    ws = mla.workspace_for(plan, "cuda")
+    mla.decode_partials(q_dev, dc.cache, cfg.scale, plan, ws)
+    shape = (cfg.batch, cfg.n_heads, cfg.d_latent)
+    o_lat1 = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse1 = torch.empty(shape[:2], dtype=torch.float32, device="cuda")
+    mla.decode_combine(dc.cache, cfg.n_heads, plan, ws, o_lat1, lse1)
+    o1 = mla.out_uv(o_lat1, dc.w_uv)
+    o_lat2 = torch.empty_like(o_lat1)
+    lse2 = torch.empty_like(lse1)
+    o2 = mla.decode_combine_out(dc.cache, plan, ws, dc.w_uv, o_lat2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(o_lat1, o_lat2) and torch.equal(lse1, lse2)
+    a, b = from_dev(o1), from_dev(o2)
+    # Both round an fp32 sum of the same bf16 products to bf16: at most one
+    # bf16 step apart (2^-8 relative).
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-6)
+    o_ref, _ = _latent_ref(case, q_np)
+    assert_close(from_dev(o_lat2), o_ref, "bf16", "o_lat")
+
+
+@pytest.mark.parametrize("seed", [0, 4])
+def test_tiny_f32_combine_out(seed):
+    """fp32 storage takes the generic merge and projection behind the same call."""
+    cfg = CONFIGS["tiny_f32"]
+    case = make_case(cfg, seed)
+    _, o_lat, lse, o = DevCase(case).run_fused(split_tokens=16)
+    o_ref, lse_ref = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache,
+                                                 case.seq_lens, case.w_uk, case.w_uv, cfg.scale)
+    assert_close(from_dev(o), o_ref, "f32", "o")
+    assert_close(from_dev(lse), lse_ref, "f32", "lse")
+
+
 def test_absorb_q_bf16_b16():
     cfg = DSV2.replace(len_lo=1, len_hi=1, max_len=1)
     case = make_case(cfg, 2)
@@ -166,6 +223,19 @@ def test_zero_length_requests():
     assert np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2]))
     o_ref, lse_ref = _latent_ref(case, q_np, requests=[1])
     assert_close(o_lat[1], o_ref[1], "bf16", "o_lat[1]")
+
+
+def test_zero_length_requests_fused():
+    cfg = SMALL
+    lens = np.array([0, 40, 0], np.int32)
+    case = make_case(cfg, 6, seq_lens=lens, pad_value=np.nan)
+    _, o_lat, lse, o = DevCase(case).run_fused()
+    o = from_dev(o)
+    assert np.all(o[0] == 0) and np.all(o[2] == 0)
+    assert np.all(np.isneginf(from_dev(lse)[[0, 2]]))
+    o_ref, _ = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
+                                           case.w_uk, case.w_uv, cfg.scale, requests=[1])
+    assert_close(o[1], o_ref[1], "bf16", "o[1]")
 
 
 def test_single_token_request_equals_row():
@@ -291,6 +361,21 @@ def test_dsv2_b16_t4096_seed1_chain_sampled():
     _, o_lat, lse, o = DevCase(case).run()
     heads = [3, 100]
     reqs = [4, 11]
+    o_ref, lse_ref = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
+                                                 case.w_uk, case.w_uv, cfg.scale,
+                                                 requests=reqs, heads=heads)
+    assert_close(from_dev(o)[np.ix_(reqs, heads)], o_ref[np.ix_(reqs, heads)], "bf16", "o")
+    assert_close(from_dev(lse)[np.ix_(reqs, heads)], lse_ref[np.ix_(reqs, heads)], "bf16",
+                 "lse")
+
+
+def test_dsv2_b16_t4096_fused_chain_sampled():
+    cfg = DSV2
+    case = make_case(cfg, 0)
+    _log("[dsv2_b16_t4096 fused] running")
+    _, o_lat, lse, o = DevCase(case).run_fused()
+    heads = [1, 64, 126]
+    reqs = [0, 7, 15]
     o_ref, lse_ref = oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens,
                                                  case.w_uk, case.w_uv, cfg.scale,
                                                  requests=reqs, heads=heads)
