@@ -203,13 +203,28 @@ def main():
     log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, partials "
         f"{partials_us:.1f}, combine+out_uv {tail_us:.1f}")
 
+    # The decode kernel alone, launched back to back on the same stream over the
+    # same rotating inputs: its average launch duration, free of the event
+    # records that split the phases above.  This is the roofline's time.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        e = pool[i % n_pool]
+        mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    decode_us = e0.elapsed_time(e1) / args.steps * 1e3
+    log(f"[bench] decode kernel back to back: {decode_us:.1f} us per launch")
+
     # Algorithmic work (split partials excluded).
     tokens = int(sum(int(x) for x in pool[0].case.seq_lens))
     cache_bytes = tokens * row * 2
     q_bytes = B * nh * row * 2
     flops = 2.0 * nh * (row + cfg.d_latent) * tokens
     k2_bytes = cache_bytes + q_bytes
-    k2_gbps = k2_bytes / (partials_us * 1e-6) / 1e9
+    k2_gbps = k2_bytes / (decode_us * 1e-6) / 1e9
     # Whole step: the cache, both up-projection weights, the query in and the
     # output out, each moved once.
     w_bytes = 2 * nh * cfg.d_head * cfg.d_latent * 2
@@ -240,11 +255,12 @@ def main():
             "rotating_pool_mb": round(pool_mb), "split_tokens": plan.split_tokens,
             "num_splits": plan.num_splits, "parallelism": "single-gpu",
         },
-        "latent_cache_GBps": cache_bytes / (partials_us * 1e-6) / 1e9,
+        "latent_cache_GBps": cache_bytes / (decode_us * 1e-6) / 1e9,
         "step_roofline_us": t_roof_us,
         "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
         "kernels_us": {"absorb_q": absorb_us, "decode_partials": partials_us,
-                       "decode_combine_out": tail_us},
+                       "decode_combine_out": tail_us,
+                       "decode_partials_back_to_back": decode_us},
         "roofline": {
             "kernel": "decode_mfma_kernel (mla_decode_partials)",
             "bound": "hbm",
@@ -254,7 +270,8 @@ def main():
             "frac": k2_gbps / HBM_PEAK_GBPS,
             "traffic": traffic_from_counters(sha),
             "alg_bytes_per_launch": k2_bytes,
-            "mfma_tflops": flops / (partials_us * 1e-6) / 1e12,
+            "launch_us": decode_us,
+            "mfma_tflops": flops / (decode_us * 1e-6) / 1e12,
             "kernel_source_sha": sha,
         },
     }

@@ -476,10 +476,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   uint16_t* dst = p.part_o +
                   ((static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + hblock * 32) * 512 +
                   lane * 8;
+  // The partials are read once, by the combine: stream them past the caches.
 #pragma unroll 8
   for (int r = 0; r < 32; ++r)
-    *reinterpret_cast<bf16x8_t*>(dst + r * 512) =
-        *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
+    __builtin_nontemporal_store(*reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16),
+                                reinterpret_cast<bf16x8_t*>(dst + r * 512));
   if (half == 0)
     p.part_lse[(static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + head] =
         (m + __log2f(l)) * kLn2;
