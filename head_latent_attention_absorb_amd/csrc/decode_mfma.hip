@@ -58,7 +58,7 @@ constexpr int kCBlocks = 512 / 32;    // 16 latent blocks
 constexpr int kPv = 2 * kCBlocks;     // 32 PV MFMAs per tile
 constexpr int kKWindow = 3;           // score operand reads in flight
 constexpr int kVWindow = 4;           // PV operands (two reads each) in flight
-constexpr int kQkLead = 8;            // score MFMAs issued between the softmax pieces
+constexpr int kSoftSlots = 17;        // score MFMAs the softmax arithmetic is spread over
 constexpr int kLdsBytes = kStages * kTileBytes;
 constexpr float kRescaleThreshold = 8.f;             // log2 units
 
@@ -107,6 +107,16 @@ __device__ __forceinline__ void load_row_groups(const void* src, unsigned dst,
   (load_to_lds16<gi * 128>(src, dst + gi * 4096), ...);
 }
 
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // The two products are issued through inline asm so that they keep the
 // order written below: the compiler may not sink the softmax arithmetic
 // behind them or regroup them, which would serialise the matrix pipe behind
@@ -135,8 +145,28 @@ __device__ __forceinline__ void mfma_a(f32x16_t& c, const bf16x8_t& a, const bf1
 __device__ __forceinline__ void drain_v(f32x16_t& c) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(c));
 }
+// Copies the score accumulator out with VALU moves issued right here (an
+// asm statement keeps its place among the asm products): a copy the compiler
+// placed itself could land right behind the product that writes `c`.
+__device__ __forceinline__ void take_scores(float (&dst)[16], const f32x16_t& c) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const f32x2_t in = {c[2 * k], c[2 * k + 1]};
+    f32x2_t out;
+    asm volatile("v_mov_b64 %0, %1" : "=v"(out) : "v"(in));
+    dst[2 * k] = out[0];
+    dst[2 * k + 1] = out[1];
+  }
+}
+
 // Pins the computation of x before this point of the instruction stream.
 __device__ __forceinline__ void anchor(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void anchor(float x, float y) { asm volatile("" ::"v"(x), "v"(y)); }
+// Keeps every computation on x after this point of the instruction stream.
+__device__ __forceinline__ void launder(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void launder(int& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 __device__ __forceinline__ unsigned lds_address(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS const void*)p));
@@ -192,6 +222,16 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     for (int ks = 0; ks < kKSteps; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
   }
+  // The softmax takes its max on raw scores and folds the scale into the
+  // exponent, which needs a scale >= 0: a negative scale moves onto the query
+  // (an exact sign flip of every element).
+  const float scale = fabsf(p.scale_log2);
+  if (p.scale_log2 < 0.f) {
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, qf[ks]) ^ 0x80008000u);
+  }
 
   f32x16_t acc[kCBlocks];
 #pragma unroll
@@ -224,7 +264,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       page_of_lane = p.cache.page_table[static_cast<size_t>(b) * p.cache.max_pages +
                                         first_page + lane];
   }
-  auto issue_tile = [&](int stage, int tile_t0) {
+  // This lane's source address for the tile starting at token tile_t0, and
+  // this wave's LDS destination in a ring stage.
+  auto tile_src = [&](int tile_t0) {
     const int t = min(tile_t0 + n_load, t1 - 1);
     const uint8_t* src;
     if constexpr (kPaged) {
@@ -236,9 +278,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     } else {
       src = req_base + static_cast<size_t>(t) * kRowBytes;
     }
-    src += chunk_off;
-    const unsigned dst = lds_address(lds + stage * kTileBytes) + wave * 1024;
-    load_row_groups(src, dst, std::make_integer_sequence<int, kGroups>{});
+    return src + chunk_off;
+  };
+  auto tile_dst = [&](int stage) { return lds_address(lds + stage * kTileBytes) + wave * 1024; };
+  auto issue_tile = [&](int stage, int tile_t0) {
+    load_row_groups(tile_src(tile_t0), tile_dst(stage), std::make_integer_sequence<int, kGroups>{});
   };
 
   // Per-lane LDS offsets within a tile.  Score operand of K-step ks:
@@ -298,19 +342,21 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       mfma_v(sc, ta[ks], qf[ks]);
   };
 
-  // Prologue: tiles 0..2 in flight, then one wait (visible to the compiler)
-  // for tile 0 and the query fragments.  From here on the compiler sees no
-  // outstanding loads, and the tile loads are governed only by the waits
-  // below.  Every step issues exactly one tile (past the last tile they
-  // re-read the partition's last row into a stage that is never read
-  // again), so "this wave's loads of tile t have landed" while two younger
-  // tiles may stay in flight is always vmcnt(2 * kGroups).
+  // Prologue: tile 0 alone first, and one wait (visible to the compiler) for
+  // it and the query fragments; only then tiles 1 and 2.  When every
+  // workgroup starts at once, tile 0 lands sooner if it does not share the
+  // memory system with two more tiles per workgroup.  From here on the
+  // compiler sees no outstanding loads, and the tile loads are governed only
+  // by the waits below.  Every step issues exactly one tile (past the last
+  // tile they re-read the partition's last row into a stage that is never
+  // read again), so at step t "this wave's loads of tile t+1 have landed"
+  // while those of tile t+2 may stay in flight is always vmcnt(kGroups).
   issue_tile(0, t0);
-  issue_tile(1, t0 + kTile);
-  issue_tile(2, t0 + 2 * kTile);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGroups));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  issue_tile(1, t0 + kTile);
+  issue_tile(2, t0 + 2 * kTile);
 
   // Scores of tile 0.
   {
@@ -323,12 +369,23 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     for (int ks = 0; ks < kKSteps; ++ks) qk(ta, qoff, ks);
     drain_v(sc);
   }
+  float s_next[16];
+  take_scores(s_next, sc);
 
-  // One step: the softmax of tile t (stage t % 4) is issued between the first
-  // score MFMAs of tile t+1 (stage (t+1) % 4); then every PV MFMA of tile t
-  // is paired with a score MFMA of tile t+1.
+  // One step.  The softmax arithmetic of tile t (stage t % 4) is spread over
+  // the first kSoftSlots score MFMAs of tile t+1 (stage (t+1) % 4), a few VALU
+  // instructions behind each product, where they issue while the matrix pipe
+  // works; then the PV products of tile t, the first ones paired with the
+  // remaining score MFMAs, and between them the loads of tile t+3, one column
+  // group every second PV product (issued in a burst, the four waves' loads
+  // queue behind each other in the CU's address unit).
   auto step = [&](int t, auto has_next) {
     constexpr bool kNext = decltype(has_next)::value;
+    // The scores of tile t, taken out of the accumulator at the end of the
+    // previous step (or after the prologue).
+    float sv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sv[v] = s_next[v];
     // Wait for this wave's loads of tile t+1 (tile t+2 may stay in flight),
     // then for everyone's.  A raw s_barrier, not __syncthreads(): the latter
     // also waits for every outstanding global load and would drain the
@@ -338,65 +395,95 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroups));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_tile((t + 3) & (kStages - 1), t0 + (t + 3) * kTile);
 
     const int nvalid = t1 - (t0 + t * kTile);
     int qoff[4], voff[4];
     k_offsets((t + 1) & (kStages - 1), qoff);
     v_offsets(t & (kStages - 1), voff);
-
-    // The scores of tile t leave the accumulators.
-    float sv[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sv[v] = sc[v];
+    const uint8_t* next_src = tile_src(t0 + (t + 3) * kTile);
+    const unsigned next_dst = tile_dst((t + 3) & (kStages - 1));
 
     bf16x8_t ta[kKSteps];
     if constexpr (kNext) {
 #pragma unroll
       for (int ks = 0; ks < kKWindow; ++ks) ta[ks] = read_k(qoff, ks);
     }
+    auto qk_at = [&](int ks) {
+      if constexpr (kNext) qk(ta, qoff, ks);
+    };
 
-    // Softmax of tile t, without branches: the new running max is decided
-    // here, the (rare) accumulator rescale it implies runs after the lead-in.
     // Accumulator row of register v in this lane: token (v/4)*8 + half*4 +
-    // v%4, valid while (v/4)*8 + v%4 < nvalid - half*4.
+    // v%4, valid while (v/4)*8 + v%4 < nvalid - half*4.  Only a partition's
+    // last tile can be partial; its invalid scores are excluded from the max
+    // here and their probabilities zeroed below.
+    // (The limit is laundered inside each branch so that the compiler does
+    // not hoist its comparisons into every full tile.)
+    const bool partial = nvalid < kTile;
     const int lim = nvalid - half * 4;
-    float tmax = -INFINITY;
+    if (partial) {
+      int lim_p = lim;
+      launder(lim_p);
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      sv[v] = (v >> 2) * 8 + (v & 3) < lim ? sv[v] * p.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[v]);
+      for (int v = 0; v < 16; ++v)
+        if ((v >> 2) * 8 + (v & 3) >= lim_p) sv[v] = -INFINITY;
     }
+
+    // Tile max of the raw scores (the scale is >= 0 here, so it commutes with
+    // the max), over both lane halves, then scaled to exp2 units.
+    qk_at(0);
+#pragma unroll
+    for (int v = 0; v < 12; ++v) launder(sv[v]);
+    const float a0 = fmax3(sv[0], sv[1], sv[2]), a1 = fmax3(sv[3], sv[4], sv[5]);
+    const float a2 = fmax3(sv[6], sv[7], sv[8]), a3 = fmax3(sv[9], sv[10], sv[11]);
+    anchor(a0, a1);
+    anchor(a2, a3);
+    qk_at(1);
+#pragma unroll
+    for (int v = 12; v < 16; ++v) launder(sv[v]);
+    float tmax = fmaxf(fmax3(a0, a1, sv[15]), fmax3(a2, a3, fmax3(sv[12], sv[13], sv[14])));
     anchor(tmax);
-    if constexpr (kNext) { qk(ta, qoff, 0); qk(ta, qoff, 1); }
-#pragma unroll
-    for (int v = 8; v < 16; ++v) {
-      sv[v] = (v >> 2) * 8 + (v & 3) < lim ? sv[v] * p.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[v]);
-    }
-    tmax = halves_max(tmax);
+    qk_at(2);
+    tmax = halves_max(tmax) * scale;
+    anchor(tmax);
+    qk_at(3);
+    // The new running max is decided here; the (rare) accumulator rescale it
+    // implies runs after the softmax.
     const bool rescale = __builtin_amdgcn_ballot_w64(tmax > m + kRescaleThreshold) != 0;
     const float m_new = rescale ? fmaxf(m, tmax) : m;
     anchor(m_new);
-    if constexpr (kNext) { qk(ta, qoff, 2); qk(ta, qoff, 3); }
+
+    // p = exp2(scale * s - m_new), two per product.
+    float pv[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qk_at(4 + j);
+      launder(sv[2 * j]);
+      launder(sv[2 * j + 1]);
+      pv[2 * j] = __builtin_amdgcn_exp2f(fmaf(sv[2 * j], scale, -m_new));
+      pv[2 * j + 1] = __builtin_amdgcn_exp2f(fmaf(sv[2 * j + 1], scale, -m_new));
+      anchor(pv[2 * j], pv[2 * j + 1]);
+    }
+    if (partial) {
+      int lim_p = lim;
+      launder(lim_p);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if ((v >> 2) * 8 + (v & 3) >= lim_p) pv[v] = 0.f;
+    }
+    // bf16 probabilities (the PV B operand) and their sum, four per product.
     bf16x8_t pb[2];
-    float psum = 0.f;
+    float s4[4];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const float pv = __builtin_amdgcn_exp2f(sv[v] - m_new);
-      psum += pv;
-      pb[0][v] = static_cast<__bf16>(pv);
-    }
-    anchor(psum);
-    if constexpr (kNext) { qk(ta, qoff, 4); qk(ta, qoff, 5); }
+    for (int k = 0; k < 4; ++k) {
+      qk_at(12 + k);
 #pragma unroll
-    for (int v = 8; v < 16; ++v) {
-      const float pv = __builtin_amdgcn_exp2f(sv[v] - m_new);
-      psum += pv;
-      pb[1][v - 8] = static_cast<__bf16>(pv);
+      for (int e = 0; e < 4; ++e) pb[k >> 1][(k & 1) * 4 + e] = static_cast<__bf16>(pv[4 * k + e]);
+      s4[k] = (pv[4 * k] + pv[4 * k + 1]) + (pv[4 * k + 2] + pv[4 * k + 3]);
+      anchor(s4[k]);
     }
-    anchor(psum);
-    if constexpr (kNext) { qk(ta, qoff, 6); qk(ta, qoff, 7); }
+    qk_at(16);
+    const float psum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    static_assert(kSoftSlots == 17, "the softmax above occupies score products 0..16");
 
     bf16x8_t va[kPv];
 #pragma unroll
@@ -426,20 +513,23 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     l += psum;
     m = m_new;
 
-    // PV of tile t, each MFMA paired with the next score MFMA of tile t+1.
-#pragma unroll
-    for (int i = 0; i < kPv; ++i) {
-      if (i + kVWindow < kPv) va[i + kVWindow] = read_v(voff, i + kVWindow);
+    // PV of tile t; the first ones paired with the remaining score MFMAs of
+    // tile t+1, every second one followed by one column group of tile t+3.
+    static_for<kPv>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i + kVWindow < kPv) va[i + kVWindow] = read_v(voff, i + kVWindow);
       mfma_a(acc[i & 15], va[i], pb[i >> 4]);
-      if constexpr (kNext) {
-        if (kQkLead + i < kKSteps) qk(ta, qoff, kQkLead + i);
-      }
-    }
-    if constexpr (kNext) {
-#pragma unroll
-      for (int ks = kQkLead + kPv; ks < kKSteps; ++ks) qk(ta, qoff, ks);
-      drain_v(sc);
-    }
+      if constexpr (kNext && kSoftSlots + i < kKSteps) qk(ta, qoff, kSoftSlots + i);
+      if constexpr (i % 2 == 0 && i / 2 < kGroups)
+        load_to_lds16<(i / 2) * 128>(next_src, next_dst + (i / 2) * 4096);
+    });
+    static_assert(kKSteps - kSoftSlots <= kPv, "every score MFMA is paired");
+    // The scores of tile t+1 leave the accumulator behind the last PV
+    // products, which issue after the last score product: it has retired by
+    // then, with far more than the 18 wait states a VALU read of an MFMA
+    // result needs.
+    static_assert(kPv - (kKSteps - kSoftSlots) >= 4, "PV products behind the last score product");
+    if constexpr (kNext) take_scores(s_next, sc);
   };
 
   for (int t = 0; t + 1 < ntiles; ++t) step(t, std::true_type{});

@@ -301,6 +301,28 @@ def test_request_independence_and_determinism():
     assert np.array_equal(from_dev(o_lat)[0], o1[0])
 
 
+@pytest.mark.parametrize("scale", [-0.0722, 0.0], ids=["negative", "zero"])
+def test_scale_sign_and_zero(scale):
+    """The softmax scale is a free parameter of the call.  A negative scale
+    reverses the score order (the kernel's max must follow it) and zero gives
+    uniform weights over every valid token, including a partial last tile."""
+    cfg = SMALL.replace(softmax_scale=scale)
+    lens = np.array([1, 45, 300], np.int32)
+    case = make_case(cfg, 21, seq_lens=lens, pad_value=np.nan)
+    _log(f"[scale] scale={scale} lens={lens.tolist()}")
+    dc = DevCase(case)
+    q_np, o_lat, lse = _decode_only(case, dc, 21, split_tokens=96)
+    o_ref, lse_ref = _latent_ref(case, q_np)
+    assert np.isfinite(o_lat).all() and np.isfinite(lse).all()
+    assert_close(o_lat, o_ref, "bf16", "o_lat")
+    assert_close(lse, lse_ref, "bf16", "lse")
+    if scale == 0.0:
+        for b, n in enumerate(lens):
+            mean = case.cache[b, :n, :cfg.d_latent].astype(np.float64).mean(axis=0)
+            assert max_abs(o_lat[b], np.broadcast_to(mean, o_lat[b].shape)) <= 2e-2
+            assert np.allclose(lse[b], np.log(n), atol=1e-5)
+
+
 def test_large_scores_rescale_path():
     """Scores that keep growing along the sequence (by ~30 in natural-log units
     over 300 tokens) push later tiles far past the running max, exercising the
