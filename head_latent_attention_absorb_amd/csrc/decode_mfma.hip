@@ -213,26 +213,6 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   const int hblock = g * 4 + wave;
   const int head = hblock * 32 + l32;
 
-  // Query as the B operand: lane holds head `head`, K slots half*8..+7 of
-  // each of the 36 K-steps.
-  bf16x8_t qf[kKSteps];
-  {
-    const uint16_t* qrow = p.q_cat + (static_cast<size_t>(b) * p.n_heads + head) * kRow + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
-  }
-  // The softmax takes its max on raw scores and folds the scale into the
-  // exponent, which needs a scale >= 0: a negative scale moves onto the query
-  // (an exact sign flip of every element).
-  const float scale = fabsf(p.scale_log2);
-  if (p.scale_log2 < 0.f) {
-    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, qf[ks]) ^ 0x80008000u);
-  }
-
   f32x16_t acc[kCBlocks];
 #pragma unroll
   for (int cb = 0; cb < kCBlocks; ++cb)
@@ -331,8 +311,47 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     asm volatile("" : "+v"(voff[0]), "+v"(voff[1]), "+v"(voff[2]), "+v"(voff[3]));
   };
 
-  // Scores S^T accumulate in one chain; inside a step its MFMAs alternate
-  // with independent PV MFMAs, which covers the chain's dependency latency.
+  // Query as the B operand: lane holds head `head`, K slots half*8..+7 of
+  // each of the 36 K-steps.  The workgroup's 128 query rows have the shape of
+  // four tiles and go through the ring first, with the tile loader (head
+  // block j into stage j): every load reads whole 128-byte lines, where
+  // loading the fragments straight into registers would touch 32 lines per
+  // instruction.  Each wave then reads its fragments with the (bank-conflict
+  // free) score-operand reads of its stage.
+  static_assert(kStages == 4 && kMfmaHeadsPerGroup == kStages * kTile, "query fills the ring");
+  bf16x8_t qf[kKSteps];
+  {
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(p.q_cat) +
+                          (static_cast<size_t>(b) * p.n_heads + g * kMfmaHeadsPerGroup + n_load) *
+                              kRowBytes + chunk_off;
+#pragma unroll
+    for (int j = 0; j < kStages; ++j)
+      load_row_groups(qsrc + j * kTile * kRowBytes, tile_dst(j),
+                      std::make_integer_sequence<int, kGroups>{});
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    int qo[4];
+    k_offsets(wave, qo);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = read_k(qo, ks);
+    // Every wave's reads are done before the ring is refilled with tiles.
+    __syncthreads();
+  }
+  // The softmax takes its max on raw scores and folds the scale into the
+  // exponent, which needs a scale >= 0: a negative scale moves onto the query
+  // (an exact sign flip of every element).
+  const float scale = fabsf(p.scale_log2);
+  if (p.scale_log2 < 0.f) {
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, qf[ks]) ^ 0x80008000u);
+  }
+
+  // Scores S^T accumulate in one chain of dependent products (on gfx950 a
+  // 32x32x16 product that accumulates onto the previous one's result still
+  // issues every 32 cycles).
   f32x16_t sc;
   auto qk = [&](bf16x8_t (&ta)[kKSteps], const int (&qoff)[4], int ks) {
     if (ks + kKWindow < kKSteps) ta[ks + kKWindow] = read_k(qoff, ks + kKWindow);
