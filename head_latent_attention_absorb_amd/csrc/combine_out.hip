@@ -87,26 +87,34 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   const int r = tid / kSegs, seg = tid % kSegs;
   const int b = b0 + r;
   const bool live = b < batch;
-  const int ns = live ? used_splits(seq_lens[b], split_tokens) : 0;
+  const int len = live ? seq_lens[b] : 0;
   const size_t lbase = static_cast<size_t>(live ? b : 0) * num_splits * n_heads + i;
-  // Single pass with a running max: each batch of kBatch splits loads its
-  // log-sum-exps and rows together, so a merge of S splits costs
-  // ceil(S / kBatch) memory round trips.
+  // Single pass with a running max over batches of kBatch splits.  The loads
+  // of a batch (rows and log-sum-exps) are issued together with the length
+  // load, without waiting for it: every split's row lies in the workspace,
+  // and the splits past the request's length (never written: any bits) are
+  // dropped with selects afterwards.  A merge of S splits costs ceil(S /
+  // kBatch) memory round trips.
   float L = -INFINITY, W = 0.f;
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
   const uint16_t* row = part_o + lbase * kLat + seg * 8;
   const size_t split_stride = static_cast<size_t>(n_heads) * kLat;
-  for (int s0 = 0; s0 < ns; s0 += kBatch) {
+  int ns = 0;
+  for (int s0 = 0; s0 < num_splits; s0 += kBatch) {
     bf16x8_t v[kBatch];
     float x[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int s = min(s0 + j, ns - 1);
+      const int s = min(s0 + j, num_splits - 1);
       v[j] = *reinterpret_cast<const bf16x8_t*>(row + static_cast<size_t>(s) * split_stride);
-      x[j] = s0 + j < ns ? part_lse[lbase + static_cast<size_t>(s) * n_heads] : -INFINITY;
+      x[j] = part_lse[lbase + static_cast<size_t>(s) * n_heads];
     }
+    ns = used_splits(len, split_tokens);
+    if (s0 >= ns) break;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) x[j] = s0 + j < ns ? x[j] : -INFINITY;
     float Ln = L;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) Ln = fmaxf(Ln, x[j]);
@@ -116,10 +124,12 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
     for (int k = 0; k < 8; ++k) acc[k] *= alpha;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const float w = expf(x[j] - Ln);
-      W += w;
+      if (s0 + j < ns) {
+        const float w = expf(x[j] - Ln);
+        W += w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, static_cast<float>(v[j][e]), acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, static_cast<float>(v[j][e]), acc[e]);
+      }
     }
     L = Ln;
   }

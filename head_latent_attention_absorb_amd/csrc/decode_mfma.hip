@@ -374,18 +374,26 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  issue_tile(1, t0 + kTile);
-  issue_tile(2, t0 + 2 * kTile);
 
-  // Scores of tile 0.
+  // Scores of tile 0, with the loads of tiles 1 and 2 (in that order), one
+  // column group behind each of the first 18 score products.
   {
     int qoff[4];
     k_offsets(0, qoff);
     bf16x8_t ta[kKSteps];
 #pragma unroll
     for (int ks = 0; ks < kKWindow; ++ks) ta[ks] = read_k(qoff, ks);
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qk(ta, qoff, ks);
+    const uint8_t* src1 = tile_src(t0 + kTile);
+    const uint8_t* src2 = tile_src(t0 + 2 * kTile);
+    const unsigned dst1 = tile_dst(1), dst2 = tile_dst(2);
+    static_for<kKSteps>([&](auto K) {
+      constexpr int ks = decltype(K)::value;
+      qk(ta, qoff, ks);
+      if constexpr (ks < kGroups)
+        load_to_lds16<ks * 128>(src1, dst1 + ks * 4096);
+      else if constexpr (ks < 2 * kGroups)
+        load_to_lds16<(ks - kGroups) * 128>(src2, dst2 + (ks - kGroups) * 4096);
+    });
     drain_v(sc);
   }
   float s_next[16];
@@ -585,11 +593,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   uint16_t* dst = p.part_o +
                   ((static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + hblock * 32) * 512 +
                   lane * 8;
-  // The partials are read once, by the combine: stream them past the caches.
+  // Plain stores: the combine that reads the partials right after this
+  // kernel finds them in the last-level cache (non-temporal stores make this
+  // kernel slightly faster but the whole step slower).
 #pragma unroll 8
   for (int r = 0; r < 32; ++r)
-    __builtin_nontemporal_store(*reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16),
-                                reinterpret_cast<bf16x8_t*>(dst + r * 512));
+    *reinterpret_cast<bf16x8_t*>(dst + r * 512) =
+        *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
   if (half == 0)
     p.part_lse[(static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + head] =
         (m + __log2f(l)) * kLn2;
