@@ -70,6 +70,9 @@ static_assert(kMfmaHeadsPerGroup == 4 * 32 && kMfmaTokenGranule == kTile, "");
 // s_waitcnt immediate: wait until at most `n` vector-memory loads are
 // outstanding; expcnt and lgkmcnt are left at their maxima (no wait).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt immediate: wait until no LDS access is outstanding; vmcnt and
+// expcnt are left at their maxima (no wait).
+constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
 struct MfmaParams {
   const uint16_t* q_cat;  // [B, n_heads, 576] bf16
@@ -313,30 +316,49 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
 
   // Query as the B operand: lane holds head `head`, K slots half*8..+7 of
   // each of the 36 K-steps.  The workgroup's 128 query rows have the shape of
-  // four tiles and go through the ring first, with the tile loader (head
-  // block j into stage j): every load reads whole 128-byte lines, where
-  // loading the fragments straight into registers would touch 32 lines per
-  // instruction.  Each wave then reads its fragments with the (bank-conflict
-  // free) score-operand reads of its stage.
+  // four tiles (head block j = rows 32j..32j+31) and go through the ring with
+  // the tile loader: every load reads whole 128-byte lines, where loading the
+  // fragments straight into registers would touch 32 lines per instruction.
+  // Each wave then reads its fragments with the (bank-conflict free)
+  // score-operand reads.  Two rounds through stages 2 and 3, so that tiles 0
+  // and 1 stream into stages 0 and 1 meanwhile: round 0 carries head blocks
+  // 2 and 3 (read by waves 2 and 3), round 1 head blocks 0 and 1.  The
+  // barrier closing each round waits for LDS reads only, never for the tile
+  // loads still in flight.
   static_assert(kStages == 4 && kMfmaHeadsPerGroup == kStages * kTile, "query fills the ring");
   bf16x8_t qf[kKSteps];
   {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(p.q_cat) +
                           (static_cast<size_t>(b) * p.n_heads + g * kMfmaHeadsPerGroup + n_load) *
                               kRowBytes + chunk_off;
-#pragma unroll
-    for (int j = 0; j < kStages; ++j)
-      load_row_groups(qsrc + j * kTile * kRowBytes, tile_dst(j),
+    for (int round = 0; round < 2; ++round) {
+      const int hb0 = 2 - 2 * round;  // first head block of this round
+      load_row_groups(qsrc + hb0 * kTile * kRowBytes, tile_dst(2),
                       std::make_integer_sequence<int, kGroups>{});
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    int qo[4];
-    k_offsets(wave, qo);
+      load_row_groups(qsrc + (hb0 + 1) * kTile * kRowBytes, tile_dst(3),
+                      std::make_integer_sequence<int, kGroups>{});
+      if (round == 0) {
+        issue_tile(0, t0);
+        issue_tile(1, t0 + kTile);
+        // This round's query blocks landed; tiles 0 and 1 may stay in flight.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGroups));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if ((wave & 2) == hb0) {
+        int qo[4];
+        k_offsets(2 + (wave & 1), qo);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = read_k(qo, ks);
-    // Every wave's reads are done before the ring is refilled with tiles.
-    __syncthreads();
+        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = read_k(qo, ks);
+      }
+      // Every wave's reads of stages 2 and 3 are done before they are
+      // refilled.
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
   }
   // The softmax takes its max on raw scores and folds the scale into the
   // exponent, which needs a scale >= 0: a negative scale moves onto the query
@@ -361,38 +383,28 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       mfma_v(sc, ta[ks], qf[ks]);
   };
 
-  // Prologue: tile 0 alone first, and one wait (visible to the compiler) for
-  // it and the query fragments; only then tiles 1 and 2.  When every
-  // workgroup starts at once, tile 0 lands sooner if it does not share the
-  // memory system with two more tiles per workgroup.  From here on the
-  // compiler sees no outstanding loads, and the tile loads are governed only
-  // by the waits below.  Every step issues exactly one tile (past the last
-  // tile they re-read the partition's last row into a stage that is never
-  // read again), so at step t "this wave's loads of tile t+1 have landed"
-  // while those of tile t+2 may stay in flight is always vmcnt(kGroups).
-  issue_tile(0, t0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-
-  // Scores of tile 0, with the loads of tiles 1 and 2 (in that order), one
-  // column group behind each of the first 18 score products.
+  // Prologue: tiles 0 and 1 landed with the query (their wait is the
+  // vmcnt(0) of the second query round).  From here on the compiler sees no
+  // outstanding loads, and the tile loads are governed only by the waits
+  // below.  Every step issues exactly one tile (past the last tile they
+  // re-read the partition's last row into a stage that is never read
+  // again), so at step t "this wave's loads of tile t+1 have landed" while
+  // those of tile t+2 may stay in flight is always vmcnt(kGroups).
+  //
+  // Scores of tile 0, with the loads of tile 2 one column group behind each
+  // of the first 9 score products.
   {
     int qoff[4];
     k_offsets(0, qoff);
     bf16x8_t ta[kKSteps];
 #pragma unroll
     for (int ks = 0; ks < kKWindow; ++ks) ta[ks] = read_k(qoff, ks);
-    const uint8_t* src1 = tile_src(t0 + kTile);
     const uint8_t* src2 = tile_src(t0 + 2 * kTile);
-    const unsigned dst1 = tile_dst(1), dst2 = tile_dst(2);
+    const unsigned dst2 = tile_dst(2);
     static_for<kKSteps>([&](auto K) {
       constexpr int ks = decltype(K)::value;
       qk(ta, qoff, ks);
-      if constexpr (ks < kGroups)
-        load_to_lds16<ks * 128>(src1, dst1 + ks * 4096);
-      else if constexpr (ks < 2 * kGroups)
-        load_to_lds16<(ks - kGroups) * 128>(src2, dst2 + (ks - kGroups) * 4096);
+      if constexpr (ks < kGroups) load_to_lds16<ks * 128>(src2, dst2 + ks * 4096);
     });
     drain_v(sc);
   }
