@@ -1,13 +1,19 @@
 #!/usr/bin/env python3
-"""Benchmark: MLA absorbed decode on one MI355X, DeepSeek-V2 shape B=16, T=4096.
+"""Benchmark: MLA absorbed decode on one MI355X (default: DeepSeek-V2 shape B=16, T=4096).
 
 A step is one whole decode step of one layer on one batch of synthetic input:
     mla_absorb_q -> mla_decode_partials -> mla_decode_combine_out
 (the last merges the split partials and applies W^UV in one kernel; it does
-exactly what mla_decode_combine followed by mla_out_uv does).  Inputs are resident in HBM
-before the timed region.  Every step uses the next entry of a rotating pool of
-independently seeded (cache, W^UK, W^UV, q) sets totalling > 512 MB, twice the
-256 MB Infinity Cache, so the cache bytes really come from HBM.
+exactly what mla_decode_combine followed by mla_out_uv does).  For the
+60-layer workload a step is the 60 layers back to back, each with its own
+weights and cache.  Inputs are resident in HBM before the timed region.  A
+single-layer step uses the next entry of a rotating pool of independently
+seeded (cache, W^UK, W^UV, q) sets totalling > 512 MB, twice the 256 MB
+Infinity Cache, so the cache bytes really come from HBM.
+
+Beside the step, the attention alone (mla_decode_partials followed by
+mla_decode_combine, i.e. mla_decode_attn) is timed back to back over the same
+inputs and set against its roofline.
 
 Prints ONE JSON line on stdout (everything else goes to stderr).
 """
@@ -33,6 +39,7 @@ from workload import CONFIGS, f32_to_bf16_bits, make_case  # noqa: E402
 
 METRIC = "MLA decode tokens/s and latent-cache HBM GB/s (% roofline), B=16 T=4096"
 WORKLOAD = "dsv2_b16_t4096"
+WORKLOADS = ("dsv2_b16_t4096", "ragged_b4_16k_32k", "paged_b128_t2048", "ctx128k_b2_60l")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partials_dsv2_b16_t4096_counters.json")
@@ -48,7 +55,8 @@ def to_dev(x: np.ndarray) -> torch.Tensor:
 
 
 class Entry:
-    """One pool entry: a seeded decode input resident on the GPU."""
+    """One input set (one layer of one batch) resident on the GPU, drawn with
+    the same seeded generator as the parity tests."""
 
     def __init__(self, cfg, seed):
         case = make_case(cfg, seed)
@@ -58,8 +66,41 @@ class Entry:
         self.w_uk = to_dev(case.w_uk)
         self.w_uv = to_dev(case.w_uv)
         self.cache_t = to_dev(case.cache)
-        self.lens = torch.from_numpy(case.seq_lens).cuda()
+        self.lens = torch.from_numpy(case.seq_lens.astype(np.int32)).cuda()
+        self.page_table = (torch.from_numpy(case.page_table).cuda()
+                           if case.page_table is not None else None)
+        self.cache = mla.latent_cache(self.cache_t, self.lens, cfg.d_rope, self.page_table,
+                                      cfg.page_size, cfg.max_len if cfg.paged else None)
+        self.tokens = int(case.seq_lens.sum())
+        self.nbytes = sum(t.numel() * t.element_size()
+                          for t in (self.q_c, self.q_r, self.w_uk, self.w_uv, self.cache_t))
+
+
+class DeviceEntry:
+    """The same distributions drawn on the GPU from a seeded torch generator
+    (contiguous caches only): used for the 60-layer 128K workload, whose
+    18 GB of cache would take minutes to draw on the host.  Timing only."""
+
+    def __init__(self, cfg, seed):
+        assert not cfg.paged and cfg.len_lo == cfg.len_hi
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        B, nh, dh, dr, dc = cfg.batch, cfg.n_heads, cfg.d_head, cfg.d_rope, cfg.d_latent
+
+        def randn(shape, std=1.0):
+            return (torch.randn(shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+        self.q_c = randn((B, nh, dh))
+        self.q_r = randn((B, nh, dr))
+        self.w_uk = randn((nh, dh, dc), dc ** -0.5)
+        self.w_uv = randn((nh, dc, dh), dc ** -0.5)
+        self.cache_t = torch.empty((B, cfg.max_len, dc + dr), dtype=torch.bfloat16,
+                                   device="cuda")
+        for b in range(B):  # one request at a time bounds the fp32 temporary
+            self.cache_t[b] = randn((cfg.max_len, dc + dr))
+        self.lens = torch.full((B,), cfg.len_lo, dtype=torch.int32, device="cuda")
         self.cache = mla.latent_cache(self.cache_t, self.lens, cfg.d_rope)
+        self.tokens = B * cfg.len_lo
         self.nbytes = sum(t.numel() * t.element_size()
                           for t in (self.q_c, self.q_r, self.w_uk, self.w_uv, self.cache_t))
 
@@ -125,15 +166,22 @@ def copy_calibration(n_bytes: int = 256 << 20, copies: int = 6):
     print(json.dumps({"copy_calibration_bytes": n_bytes, "copies": copies}), flush=True)
 
 
+def percentiles(x):
+    x = np.asarray(x)
+    return {"p10": float(np.percentile(x, 10)), "p50": float(np.percentile(x, 50)),
+            "p90": float(np.percentile(x, 90))}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=WORKLOAD, choices=WORKLOADS)
     ap.add_argument("--pool-mb", type=int, default=640,
                     help="total bytes of the rotating input pool (>= 512 MB defeats the MALL)")
     ap.add_argument("--cpu-requests", type=int, default=16,
-                    help="requests in the CPU oracle sample (0 skips it)")
+                    help="requests in the CPU oracle sample (0 skips it; default workload only)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device copies (a known-size kernel that scales "
@@ -149,15 +197,22 @@ def main():
               "(sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    cfg = CONFIGS[WORKLOAD]
+    name = args.workload
+    cfg = CONFIGS[name]
     B, nh, row = cfg.batch, cfg.n_heads, cfg.row
-    log(f"[bench] generating pool for {WORKLOAD}")
-    pool = [Entry(cfg, 0)]
-    n_pool = max(1, math.ceil(args.pool_mb * 1e6 / pool[0].nbytes))
-    for i in range(1, n_pool):
-        pool.append(Entry(cfg, i))
+    layered = cfg.layers > 1
+    log(f"[bench] generating inputs for {name}")
+    if layered:
+        # One step = every layer once, each with its own weights and cache.
+        pool = [DeviceEntry(cfg, 1000 + l) for l in range(cfg.layers)]
+    else:
+        pool = [Entry(cfg, 0)]
+        n_pool = max(1, math.ceil(args.pool_mb * 1e6 / pool[0].nbytes))
+        for i in range(1, n_pool):
+            pool.append(Entry(cfg, i))
+    n_pool = len(pool)
     pool_mb = sum(e.nbytes for e in pool) / 1e6
-    log(f"[bench] pool: {n_pool} entries, {pool_mb:.0f} MB")
+    log(f"[bench] {'layers' if layered else 'pool'}: {n_pool} entries, {pool_mb:.0f} MB")
 
     dev = "cuda"
     plan = mla.decode_plan(nh, cfg.d_latent, cfg.d_rope, torch.bfloat16, pool[0].cache,
@@ -170,7 +225,7 @@ def main():
     o = torch.empty((B, nh, cfg.d_head), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(e: Entry, ev=None):
+    def layer(e: Entry, ev=None):
         if ev is not None:
             ev[0].record(stream)
         mla.absorb_q(e.q_c, e.q_r, e.w_uk, out=q_cat)
@@ -183,67 +238,112 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    def entries(i):
+        return pool if layered else [pool[i % n_pool]]
+
+    def step(i):
+        for e in entries(i):
+            layer(e)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us per call
+
     for i in range(args.warmup):
-        step(pool[i % n_pool])
+        step(i)
     torch.cuda.synchronize()
 
-    # Timed region: exactly --steps whole steps.
+    # Timed region: exactly --steps whole steps, between device synchronisations.
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e_start.record(stream)
     for i in range(args.steps):
-        step(pool[i % n_pool])
+        step(i)
     e_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e_start.elapsed_time(e_end) / args.steps
 
-    # Same steps again with HIP events between the kernels (per-kernel times).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The same steps again with an event between steps: the spread of step
+    # times.
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
+    bounds[0].record(stream)
     for i in range(args.steps):
-        step(pool[i % n_pool], evs[i])
+        step(i)
+        bounds[i + 1].record(stream)
     torch.cuda.synchronize()
-    phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(3)] for ev in evs])
-    phase_us = phase.mean(axis=0) * 1e3
-    absorb_us, partials_us, tail_us = (float(x) for x in phase_us)
-    log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, partials "
-        f"{partials_us:.1f}, combine+out_uv {tail_us:.1f}")
+    step_us = [bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(args.steps)]
+    kernels_us = {}
+    if not layered:
+        # And once more with events between the kernels: per-kernel times (the
+        # event records add a little to each).
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            layer(pool[i % n_pool], evs[i])
+        torch.cuda.synchronize()
+        phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(3)] for ev in evs])
+        absorb_us, partials_us, tail_us = (float(x) for x in phase.mean(axis=0) * 1e3)
+        kernels_us = {"absorb_q": absorb_us, "decode_partials": partials_us,
+                      "decode_combine_out": tail_us}
+        log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, partials "
+            f"{partials_us:.1f}, combine+out_uv {tail_us:.1f}")
+    else:
+        log(f"[bench] step ({cfg.layers} layers) {ms_per_step*1e3:.1f} us")
 
-    # The decode kernel alone, launched back to back on the same stream over the
-    # same rotating inputs: its average launch duration, free of the event
-    # records that split the phases above.  This is the roofline's time.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        e = pool[i % n_pool]
-        mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    decode_us = e0.elapsed_time(e1) / args.steps * 1e3
+    # The decode kernel alone, launched back to back on the same stream over
+    # the same inputs: its average launch duration, free of the event records
+    # that split the phases above.  This is the roofline's time.
+    n_dec = args.steps * (cfg.layers if layered else 1)
+    decode_us = timed(lambda i: mla.decode_partials(
+        q_cat, pool[i % n_pool].cache, cfg.scale, plan, ws), n_dec)
     log(f"[bench] decode kernel back to back: {decode_us:.1f} us per launch")
 
-    # Algorithmic work (split partials excluded).
-    tokens = int(sum(int(x) for x in pool[0].case.seq_lens))
+    # mla_decode_attn (partials + split combine), back to back, per step.
+    def attn(i):
+        for e in entries(i):
+            mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
+            mla.decode_combine(e.cache, nh, plan, ws, o_lat, lse)
+    attn_us = timed(attn, args.steps)
+    log(f"[bench] mla_decode_attn (partials + combine) back to back: {attn_us:.1f} us per step")
+
+    # Algorithmic work per step (split partials excluded), averaged over the
+    # entries the timed steps used.
+    layers_per_step = cfg.layers if layered else 1
+    tokens = (sum(e.tokens for e in pool) if layered
+              else sum(pool[i % n_pool].tokens for i in range(args.steps)) / args.steps)
+    tokens_layer = tokens / layers_per_step
     cache_bytes = tokens * row * 2
-    q_bytes = B * nh * row * 2
+    q_bytes = layers_per_step * B * nh * row * 2
+    olat_bytes = layers_per_step * B * nh * (cfg.d_latent * 2 + 4)
     flops = 2.0 * nh * (row + cfg.d_latent) * tokens
-    k2_bytes = cache_bytes + q_bytes
+    attn_bytes = cache_bytes + q_bytes + olat_bytes
+    t_roof_attn_us = max(attn_bytes / (HBM_PEAK_GBPS * 1e9),
+                         flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    k2_bytes = (cache_bytes + q_bytes) / layers_per_step
     k2_gbps = k2_bytes / (decode_us * 1e-6) / 1e9
     # Whole step: the cache, both up-projection weights, the query in and the
     # output out, each moved once.
-    w_bytes = 2 * nh * cfg.d_head * cfg.d_latent * 2
-    io_bytes = B * nh * (cfg.d_head + cfg.d_rope) * 2 + B * nh * cfg.d_head * 2
+    w_bytes = layers_per_step * 2 * nh * cfg.d_head * cfg.d_latent * 2
+    io_bytes = layers_per_step * (B * nh * (cfg.d_head + cfg.d_rope) * 2 + B * nh * cfg.d_head * 2)
     step_bytes = cache_bytes + w_bytes + io_bytes
-    step_flops = flops + 2.0 * 2 * B * nh * cfg.d_head * cfg.d_latent
+    step_flops = flops + layers_per_step * 2.0 * 2 * B * nh * cfg.d_head * cfg.d_latent
     t_roof_us = max(step_bytes / (HBM_PEAK_GBPS * 1e9),
                     step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
     sha = kernel_sha()
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if name == WORKLOAD else
+                  f"MLA decode tokens/s and latent-cache HBM GB/s (% roofline), {name}",
         "value": B / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -256,18 +356,28 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD, "batch": B, "seq_len": cfg.max_len, "n_heads": nh,
+            "workload": name, "batch": B, "seq_len": cfg.max_len,
+            "seq_len_range": [cfg.len_lo, cfg.len_hi], "n_heads": nh,
             "d_head": cfg.d_head, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope,
-            "cache": "contiguous", "layers_per_step": 1,
+            "cache": f"paged, {cfg.page_size}-token pages" if cfg.paged else "contiguous",
+            "layers_per_step": layers_per_step,
             "rotating_pool_mb": round(pool_mb), "split_tokens": plan.split_tokens,
             "num_splits": plan.num_splits, "parallelism": "single-gpu",
         },
-        "latent_cache_GBps": cache_bytes / (decode_us * 1e-6) / 1e9,
+        "step_us": percentiles(step_us),
         "step_roofline_us": t_roof_us,
         "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
-        "kernels_us": {"absorb_q": absorb_us, "decode_partials": partials_us,
-                       "decode_combine_out": tail_us,
-                       "decode_partials_back_to_back": decode_us},
+        "attn": {
+            "what": "mla_decode_attn = decode partials + split combine, back to back",
+            "us_per_step": attn_us,
+            "roofline_us": t_roof_attn_us,
+            "pct_roofline": 100.0 * t_roof_attn_us / attn_us,
+            "alg_bytes": attn_bytes,
+            "latent_cache_GBps": cache_bytes / (attn_us * 1e-6) / 1e9,
+        },
+        "latent_cache_GBps": cache_bytes / layers_per_step / (decode_us * 1e-6) / 1e9,
+        "tokens_per_layer": tokens_layer,
+        "kernels_us": dict(kernels_us, decode_partials_back_to_back=decode_us),
         "roofline": {
             "kernel": "decode_mfma_kernel (mla_decode_partials)",
             "bound": "hbm",
@@ -275,14 +385,14 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": k2_gbps / HBM_PEAK_GBPS,
-            "traffic": traffic_from_counters(sha),
+            "traffic": traffic_from_counters(sha) if name == WORKLOAD else None,
             "alg_bytes_per_launch": k2_bytes,
             "launch_us": decode_us,
-            "mfma_tflops": flops / (decode_us * 1e-6) / 1e12,
+            "mfma_tflops": flops / layers_per_step / (decode_us * 1e-6) / 1e12,
             "kernel_source_sha": sha,
         },
     }
-    if args.cpu_requests > 0:
+    if args.cpu_requests > 0 and name == WORKLOAD:
         log(f"[bench] cpu baseline: oracle on {args.cpu_requests} requests")
         result["cpu_baseline"] = cpu_baseline(pool[0], cfg, args.cpu_requests)
     print(json.dumps(result), flush=True)

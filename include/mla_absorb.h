@@ -178,7 +178,9 @@ mla_status_t mla_decode_combine(const mla_dims_t* dims, int32_t batch, const mla
  *   out[b, i, h]     = sum_c out_lat[b, i, c] * w_uv[i, c, h]
  * w_uv [n_heads, d_latent, d_head] and out [batch, n_heads, d_head] as in
  * mla_out_uv; dims->d_head must be set.  The projection reads out_lat as
- * rounded to dims->dtype, exactly as the two separate calls would.  Plan,
+ * rounded to dims->dtype, exactly as the two separate calls would.  Up to
+ * 32 requests (MFMA plan) this is one kernel; beyond, where that kernel would
+ * re-read W^UV once per 8 requests, it is the two calls in sequence.  Plan,
  * workspace, cache and error rules are those of mla_decode_combine; a NULL
  * w_uv or out returns MLA_ERR_NULL, a misaligned one MLA_ERR_ALIGN. */
 mla_status_t mla_decode_combine_out(const mla_dims_t* dims, int32_t batch,

@@ -145,11 +145,16 @@ def test_chain_small_bf16_fused(cfg):
     assert_close(from_dev(lse), lse_ref, "bf16", "lse")
 
 
-@pytest.mark.parametrize("cfg", [SMALL, SMALL_PAGED], ids=["contiguous", "paged"])
+# 40 requests: past the batch where mla_decode_combine_out stops fusing.
+MID_B40 = DSV2.replace(name="dsv2_b40_short", batch=40, len_lo=1, len_hi=160, max_len=160)
+
+
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_PAGED, MID_B40], ids=["contiguous", "paged", "b40"])
 @pytest.mark.parametrize("split", [0, 64])
 def test_combine_out_matches_separate_calls(cfg, split):
-    """The fused tail writes exactly mla_decode_combine's o_lat and lse, and an
-    o that differs from mla_out_uv(o_lat) only by fp32 summation order."""
+    """The tail in one call writes exactly mla_decode_combine's o_lat and lse,
+    and an o that differs from mla_out_uv(o_lat) only by fp32 summation order
+    (fused kernel up to 32 requests, the two calls beyond)."""
     case = make_case(cfg, 15)
     _log(f"[combine_out] {cfg.name} split={split}")
     dc = DevCase(case)
