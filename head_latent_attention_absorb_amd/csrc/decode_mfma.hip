@@ -125,19 +125,22 @@ __device__ __forceinline__ void static_for(F&& f) {
 // behind them or regroup them, which would serialise the matrix pipe behind
 // LDS latency.  Scores accumulate in ordinary VGPRs (the O accumulators fill
 // the whole accumulation register file), O in accumulation registers.  The
-// compiler does not see these as MFMAs, so the wait states it would insert
-// are spelled out: two before each product (an operand may have just been
-// written by a VALU instruction), none between back-to-back products
-// accumulating into the same registers, and an explicit drain after the last
-// product into an accumulator before any other instruction reads it.
+// compiler does not see these as MFMAs, so it inserts none of the wait
+// states the hardware needs around them.  In this kernel every product's
+// operands come from LDS reads (covered by s_waitcnt), from the previous
+// product accumulating into the same registers (no wait states needed), or
+// from VALU results written long before; mfma_first, used outside the loop,
+// keeps two wait states in front of it.  After the last product into an
+// accumulator an explicit drain precedes any other access.  A test compiles
+// the kernel and checks these rules on the generated code.
 __device__ __forceinline__ void mfma_first(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_v(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_a(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 // Wait states between the last product writing an accumulator and any other
 // access to it: at least 18 once the product has started (s_nop n waits
