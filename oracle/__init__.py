@@ -21,9 +21,14 @@ pages is partly garbled; each reading taken is stated where it is used):
   2kiu.com/news/6340724 -- sections 2.2 (what is cached), 2.3 (absorption,
   k = [k_c; k_r]), 2.4.
 
+* [zeeklog] also: the YaRN paragraph (s = 40, alpha = 1, beta = 32, sqrt(t))
+  and the d = 5120 hidden width of the worked example.
+* [ai-library] also: "Model configuration" (RMSNorm after the compressed
+  latent) and "Long-Context Extension" (YaRN only on k^R).
+
 Parity status: every function below is pinned by a test in
-``tests/test_oracle_pins.py`` except where its docstring says "parity
-unpinned".
+``tests/test_oracle_pins.py`` (decode) or ``tests/test_oracle_append.py``
+(cache append) except where its docstring says "parity unpinned".
 """
 
 from .mla_ref import (  # noqa: F401
@@ -39,4 +44,12 @@ from .mla_ref import (  # noqa: F401
     project_out,
     softmax_attention,
     up_project,
+)
+from .append_ref import (  # noqa: F401
+    append_into,
+    append_rows,
+    down_project,
+    rms_norm,
+    rope,
+    rope_frequencies,
 )

@@ -8,12 +8,14 @@ the attention arithmetic.
 
 from .gen import (  # noqa: F401
     CONFIGS,
+    AppendCase,
     Case,
     WorkloadConfig,
     bf16_bits_to_f32,
     draw_latent_output,
     draw_latent_query,
     f32_to_bf16_bits,
+    make_append_case,
     make_case,
     round_to_bf16,
 )

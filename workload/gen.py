@@ -74,6 +74,7 @@ class WorkloadConfig:
     page_size: int = 0       # 0 => contiguous cache
     layers: int = 1
     softmax_scale: Optional[float] = None   # None => 1/sqrt(d_head + d_rope)
+    d_model: int = 0         # hidden width d of the cache append; 0 => n_heads * d_head
 
     @property
     def row(self) -> int:
@@ -94,11 +95,16 @@ class WorkloadConfig:
             return float(self.softmax_scale)
         return 1.0 / math.sqrt(self.d_head + self.d_rope)
 
+    @property
+    def hidden(self) -> int:
+        return self.d_model if self.d_model > 0 else self.n_heads * self.d_head
+
     def replace(self, **kw) -> "WorkloadConfig":
         return dataclasses.replace(self, **kw)
 
 
-_DSV2 = dict(n_heads=128, d_head=128, d_rope=64, d_latent=512)
+# d = 5120: the hidden width in the zeeklog page's worked cache example.
+_DSV2 = dict(n_heads=128, d_head=128, d_rope=64, d_latent=512, d_model=5120)
 
 CONFIGS: Dict[str, WorkloadConfig] = {
     # Tiny fp32 decode: B=1, n_h=4, d_h=16, d_h^R=8, d_c=32, T=64.
@@ -244,3 +250,36 @@ def draw_latent_output(cfg: WorkloadConfig, seed: int, batch: Optional[int] = No
     rng = np.random.Generator(np.random.PCG64(seed ^ 0x5EED0002))
     B = cfg.batch if batch is None else batch
     return _draw(rng, (B, cfg.n_heads, cfg.d_latent), 1.0, cfg.dtype)
+
+
+@dataclasses.dataclass
+class AppendCase:
+    """Inputs of one cache append: the new token's hidden state per request
+    and the projections that make its cached row."""
+    cfg: WorkloadConfig
+    seed: int
+    h: np.ndarray           # [B, d_model]
+    w_dkv: np.ndarray       # [d_c, d_model]
+    w_kr: np.ndarray        # [d_h^R, d_model]
+    rms_weight: np.ndarray  # [d_c]
+    positions: np.ndarray   # int32 [B], in [0, max_len)
+
+
+def make_append_case(cfg: WorkloadConfig, seed: int) -> AppendCase:
+    """Draw one append case from PCG64(seed ^ 0x5EED0003).
+
+    Draw order: positions, h, W^DKV, W^KR, RMSNorm weight.  h is N(0, 1) (the
+    normalised attention input); W^DKV and W^KR are N(0, 1/d); the RMSNorm
+    weight is N(1, 0.1^2); positions are uniform in [0, max_len).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed ^ 0x5EED0003))
+    B, d = cfg.batch, cfg.hidden
+    positions = rng.integers(0, cfg.max_len, size=B).astype(np.int32)
+    h = _draw(rng, (B, d), 1.0, cfg.dtype)
+    w_std = 1.0 / math.sqrt(d)
+    w_dkv = _draw(rng, (cfg.d_latent, d), w_std, cfg.dtype)
+    w_kr = _draw(rng, (cfg.d_rope, d), w_std, cfg.dtype)
+    g = rng.standard_normal(cfg.d_latent) * 0.1 + 1.0
+    rms_weight = round_to_bf16(g.astype(np.float32)) if cfg.dtype == "bf16" else \
+        g.astype(np.float32)
+    return AppendCase(cfg, seed, h, w_dkv, w_kr, rms_weight, positions)
