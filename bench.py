@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import head_latent_attention_absorb_amd as mla  # noqa: E402
-from workload import CONFIGS, f32_to_bf16_bits, make_case  # noqa: E402
+from workload import CONFIGS, f32_to_bf16_bits, make_append_case, make_case  # noqa: E402
 
 METRIC = "MLA decode tokens/s and latent-cache HBM GB/s (% roofline), B=16 T=4096"
 WORKLOAD = "dsv2_b16_t4096"
@@ -74,6 +74,14 @@ class Entry:
         self.tokens = int(case.seq_lens.sum())
         self.nbytes = sum(t.numel() * t.element_size()
                           for t in (self.q_c, self.q_r, self.w_uk, self.w_uv, self.cache_t))
+        # Inputs of the cache append (the step before the decode path): the new
+        # token's hidden state, W^DKV, W^KR and the RMSNorm weight.
+        ac = make_append_case(cfg, seed)
+        self.h = to_dev(ac.h)
+        self.w_dkv = to_dev(ac.w_dkv)
+        self.w_kr = to_dev(ac.w_kr)
+        self.rms_weight = to_dev(ac.rms_weight)
+        self.positions = torch.from_numpy(ac.positions).cuda()
 
 
 class DeviceEntry:
@@ -219,6 +227,9 @@ def main():
                            split_tokens=args.split_tokens, d_head=cfg.d_head)
     log(f"[bench] {plan}")
     ws = mla.workspace_for(plan, dev)
+    append_ws = torch.empty(max(256, int(mla.lib().mla_cache_append_workspace_bytes(
+        mla.make_dims(1, 1, cfg.d_rope, cfg.d_latent, torch.bfloat16), B, cfg.hidden))),
+        dtype=torch.uint8, device=dev)
     q_cat = torch.empty((B, nh, row), dtype=torch.bfloat16, device=dev)
     o_lat = torch.empty((B, nh, cfg.d_latent), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, nh), dtype=torch.float32, device=dev)
@@ -284,17 +295,24 @@ def main():
     kernels_us = {}
     if not layered:
         # And once more with events between the kernels: per-kernel times (the
-        # event records add a little to each).
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        # event records add a little to each).  This pass also runs the cache
+        # append of the step's new token first (the step before the decode
+        # path, not part of the step timed above); the step's ~100 MB between
+        # two appends keep its weights out of the last-level cache.
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
                for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
-            layer(pool[i % n_pool], evs[i])
+            e = pool[i % n_pool]
+            evs[i][0].record(stream)
+            mla.cache_append(e.cache, e.h, e.w_dkv, e.w_kr, e.rms_weight, e.positions,
+                             workspace=append_ws)
+            layer(e, evs[i][1:])
         torch.cuda.synchronize()
-        phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(3)] for ev in evs])
-        absorb_us, partials_us, tail_us = (float(x) for x in phase.mean(axis=0) * 1e3)
+        phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(4)] for ev in evs])
+        append_us, absorb_us, partials_us, tail_us = (float(x) for x in phase.mean(axis=0) * 1e3)
         kernels_us = {"absorb_q": absorb_us, "decode_partials": partials_us,
-                      "decode_combine_out": tail_us}
+                      "decode_combine_out": tail_us, "cache_append": append_us}
         log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, partials "
             f"{partials_us:.1f}, combine+out_uv {tail_us:.1f}")
     else:
@@ -392,6 +410,18 @@ def main():
             "kernel_source_sha": sha,
         },
     }
+    if not layered:
+        # The cache append: every weight element of [W^DKV; W^KR] read once,
+        # plus h, the RMSNorm weight and the written rows.
+        ap_bytes = (row * cfg.hidden + B * cfg.hidden + cfg.d_latent + B * row) * 2 + B * 4
+        result["cache_append"] = {
+            "what": "mla_cache_append (projection + RMSNorm + RoPE + row write), per step",
+            "us": kernels_us["cache_append"],
+            "alg_bytes": ap_bytes,
+            "roofline_us": ap_bytes / (HBM_PEAK_GBPS * 1e9) * 1e6,
+            "achieved_GBps": ap_bytes / (kernels_us["cache_append"] * 1e-6) / 1e9,
+            "timing": "events around the call inside the per-kernel pass",
+        }
     if args.cpu_requests > 0 and name == WORKLOAD:
         log(f"[bench] cpu baseline: oracle on {args.cpu_requests} requests")
         result["cpu_baseline"] = cpu_baseline(pool[0], cfg, args.cpu_requests)

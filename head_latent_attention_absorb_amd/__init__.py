@@ -50,6 +50,13 @@ class Plan(ctypes.Structure):
                 f"head_groups={self.head_groups}, workspace_bytes={self.workspace_bytes})")
 
 
+class Rope(ctypes.Structure):
+    """mla_rope_t: RoPE base and optional YaRN interpolation of the key."""
+    _fields_ = [("base", ctypes.c_float), ("yarn_scale", ctypes.c_float),
+                ("yarn_alpha", ctypes.c_float), ("yarn_beta", ctypes.c_float),
+                ("yarn_original_len", ctypes.c_int32)]
+
+
 class MLAError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn} failed: {msg} (status {status})")
@@ -91,6 +98,12 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(Plan), vp, sz, vp, vp, vp, vp, vp]
     L.mla_out_uv.restype = ctypes.c_int
     L.mla_out_uv.argtypes = [ctypes.POINTER(Dims), i32, vp, vp, vp, vp]
+    L.mla_cache_append_workspace_bytes.restype = sz
+    L.mla_cache_append_workspace_bytes.argtypes = [ctypes.POINTER(Dims), i32, i32]
+    L.mla_cache_append.restype = ctypes.c_int
+    L.mla_cache_append.argtypes = [ctypes.POINTER(Dims), i32, i32, vp, vp, vp, vp,
+                                   ctypes.c_float, ctypes.POINTER(Rope), vp,
+                                   ctypes.POINTER(CacheDesc), vp, sz, vp]
     _lib = L
     return L
 
@@ -307,3 +320,34 @@ def latent_cache(data: torch.Tensor, seq_lens: torch.Tensor, d_rope: int,
         return LatentCache(data, seq_lens, int(d_rope), None, 0, int(data.shape[1]))
     ml = int(max_len) if max_len is not None else int(page_table.shape[1]) * page_size
     return LatentCache(data, seq_lens, int(d_rope), page_table, page_size, ml)
+
+
+def cache_append(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,
+                 rms_weight: torch.Tensor, positions: torch.Tensor, rms_eps: float = 1e-6,
+                 rope_base: float = 10000.0, yarn_scale: float = 1.0, yarn_alpha: float = 1.0,
+                 yarn_beta: float = 32.0, yarn_original_len: int = 4096,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write row positions[b] of request b of `cache`:
+    [RMSNorm(W^DKV h[b]) | RoPE(W^KR h[b], positions[b])] (see mla_cache_append)."""
+    B, d_model = h.shape
+    d_c = w_dkv.shape[0]
+    d_r = w_kr.shape[0]
+    dev = h.device
+    _require(w_dkv, "w_dkv", (d_c, d_model), h.dtype, dev)
+    _require(w_kr, "w_kr", (d_r, d_model), h.dtype, dev)
+    _require(rms_weight, "rms_weight", (d_c,), h.dtype, dev)
+    _require(positions, "positions", (B,), torch.int32, dev)
+    _require(h, "h", (B, d_model), h.dtype, dev)
+    if cache.data.dtype != h.dtype or cache.data.shape[2] != d_c + d_r:
+        raise ValueError("cache row must be [d_latent + d_rope] of h's dtype")
+    dims = make_dims(1, 1, d_r, d_c, _dtype_code(h))
+    need = int(lib().mla_cache_append_workspace_bytes(ctypes.byref(dims), B, d_model))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    rope = Rope(float(rope_base), float(yarn_scale), float(yarn_alpha), float(yarn_beta),
+                int(yarn_original_len))
+    desc = cache.desc()
+    _check("mla_cache_append", lib().mla_cache_append(
+        ctypes.byref(dims), B, d_model, _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(rms_weight),
+        float(rms_eps), ctypes.byref(rope), _ptr(positions), ctypes.byref(desc),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -1,6 +1,7 @@
 // C ABI of the MLA absorbed-decode library: argument checks, split-KV
 // planning and kernel dispatch.  Declared in include/mla_absorb.h.
 
+#include <cmath>
 #include <mutex>
 #include <string.h>
 
@@ -352,3 +353,72 @@ mla_status_t mla_out_uv(const mla_dims_t* dims, int32_t batch, const void* out_l
 }
 
 }  // extern "C"
+
+// ----------------------------------------------------------------------------
+// Cache append
+// ----------------------------------------------------------------------------
+
+namespace {
+
+mla_status_t check_append(const mla_dims_t* dims, int32_t batch, int32_t d_model, float eps,
+                          const mla_rope_t* rope) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (rope == nullptr) return MLA_ERR_NULL;
+  if (batch < 0 || d_model < 1 || d_model > (1 << 20) || (dims->d_rope & 1) != 0 ||
+      !(eps >= 0.f) || !std::isfinite(eps))
+    return MLA_ERR_DIMS;
+  if (!(rope->base > 0.f) || !std::isfinite(rope->base) || !(rope->yarn_scale > 0.f) ||
+      !std::isfinite(rope->yarn_scale))
+    return MLA_ERR_DIMS;
+  if (rope->yarn_scale != 1.f &&
+      (rope->yarn_original_len < 1 || !(rope->yarn_beta > rope->yarn_alpha) ||
+       !std::isfinite(rope->yarn_alpha) || !std::isfinite(rope->yarn_beta)))
+    return MLA_ERR_DIMS;
+  return MLA_OK;
+}
+
+}  // namespace
+
+size_t mla_cache_append_workspace_bytes(const mla_dims_t* dims, int32_t batch, int32_t d_model) {
+  if (check_dims(dims) != MLA_OK || batch < 0 || d_model < 1) return 0;
+  return round256(mla::append_workspace_bytes(dims->dtype, batch, d_model, dims->d_latent,
+                                              dims->d_rope));
+}
+
+mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t batch, int32_t d_model,
+                              const void* h, const void* w_dkv, const void* w_kr,
+                              const void* rms_weight, float rms_eps, const mla_rope_t* rope,
+                              const int32_t* positions, const mla_cache_t* cache,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status_t st = check_append(dims, batch, d_model, rms_eps, rope);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
+  if (h == nullptr || w_dkv == nullptr || (dims->d_rope > 0 && w_kr == nullptr) ||
+      rms_weight == nullptr || positions == nullptr || cache->data == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(h) || !aligned16(w_dkv) || (dims->d_rope > 0 && !aligned16(w_kr)) ||
+      !aligned16(cache->data))
+    return MLA_ERR_ALIGN;
+  const size_t need = mla::append_workspace_bytes(dims->dtype, batch, d_model, dims->d_latent,
+                                                  dims->d_rope);
+  if (workspace == nullptr || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return MLA_ERR_ALIGN;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != MLA_OK) return st;
+  mla::CacheView view;
+  view.data = static_cast<const uint8_t*>(cache->data);
+  view.seq_lens = cache->seq_lens;
+  view.page_table = cache->page_table;
+  view.page_size = cache->page_table ? cache->page_size : 0;
+  view.max_len = cache->max_len;
+  view.max_pages = cache->page_table ? cache->max_len / cache->page_size : 0;
+  (void)hipGetLastError();
+  const hipError_t e = mla::launch_cache_append(
+      dims->dtype, batch, d_model, dims->d_latent, dims->d_rope, h, w_dkv, w_kr, rms_weight,
+      rms_eps, rope->base, rope->yarn_scale, rope->yarn_alpha, rope->yarn_beta,
+      static_cast<double>(rope->yarn_original_len), positions, view,
+      const_cast<void*>(cache->data), workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}

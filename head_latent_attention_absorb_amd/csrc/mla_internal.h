@@ -9,12 +9,10 @@
 namespace mla {
 
 // Split-KV partial results of the decode kernels live in the caller's
-// workspace: partial outputs normalised by their own softmax sum (fp32 from
-// the generic kernel, bf16 from the MFMA kernel) and the fp32 natural-log
-// sum-exp per (request, split, head).
-struct PartialLayout {
-  enum Kind { kRowMajor = 0, kFragment = 1 };
-};
+// workspace: row-major partial outputs [request, split, head, d_latent]
+// normalised by their own softmax sum (fp32 from the generic kernel, bf16
+// from the MFMA kernel) and the fp32 natural-log sum-exp per (request,
+// split, head).
 
 struct CacheView {
   const uint8_t* data;      // cache rows, (d_latent + d_rope) elements each
@@ -51,16 +49,28 @@ hipError_t launch_out_uv(int dtype, int batch, int n_heads, int d_head, int d_la
 // storage), row-major partial layout.
 hipError_t launch_partials_generic(const DecodeArgs& a);
 // bf16 MFMA split-KV partials for d_latent = 512, d_rope = 64,
-// n_heads % 128 == 0, fragment-order partial layout.
+// n_heads % 128 == 0.
 hipError_t launch_partials_mfma(const DecodeArgs& a);
 // Merge the partials of each request into out_lat / lse.  `fragment` selects
-// the bf16 row-major partials written by the MFMA kernel.
+// the bf16 partials written by the MFMA kernel (else fp32).
 hipError_t launch_combine(const DecodeArgs& a, bool fragment);
 // Merge of the MFMA kernel's partials into out_lat / lse and, when w_uv is
 // not null, the W^UV product of the merged rows into out in the same kernel
 // (requires combine_out_fusable(d_latent, d_head)).
 bool combine_out_fusable(int d_latent, int d_head);
 hipError_t launch_combine_rows(const DecodeArgs& a, const void* w_uv, void* out, int d_head);
+
+// Cache append: projections of the new token's hidden state, RMSNorm of the
+// latent, RoPE (optionally YaRN) of the key, row written at `positions[b]`
+// of request b through `cache_data` (the layout of `cache`).  The workspace
+// holds fp32 partial sums, append_workspace_bytes() of them.
+size_t append_workspace_bytes(int dtype, int batch, int d_model, int d_c, int d_r);
+hipError_t launch_cache_append(int dtype, int batch, int d_model, int d_c, int d_r,
+                               const void* h, const void* w_dkv, const void* w_kr,
+                               const void* gamma, float eps, double base, double yarn_scale,
+                               double yarn_alpha, double yarn_beta, double yarn_len,
+                               const int32_t* positions, const CacheView& cache,
+                               void* cache_data, void* workspace, hipStream_t stream);
 
 // Constants of the MFMA decode kernel that the planner needs.
 constexpr int kMfmaHeadsPerGroup = 128;  // heads handled by one workgroup

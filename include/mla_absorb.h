@@ -197,6 +197,52 @@ mla_status_t mla_decode_combine_out(const mla_dims_t* dims, int32_t batch,
 mla_status_t mla_out_uv(const mla_dims_t* dims, int32_t batch, const void* out_lat,
                         const void* w_uv, void* out, void* stream);
 
+/* Rotary position encoding of the decoupled key k^R.  Pairs (x[2i], x[2i+1])
+ * turn by pos * f_i, f_i = base^(-2i/d_rope).  With yarn_scale s != 1 the
+ * frequencies follow YaRN's interpolation (Peng et al. 2023), which the
+ * DeepSeek-V2 long-context extension applies to k^R only (ai-library
+ * "DeepSeek-V2" notes, "Long-Context Extension"; zeeklog notes: s = 40,
+ * alpha = 1, beta = 32, from a 4K context): with r_i = L f_i / (2 pi) the
+ * number of turns pair i makes over the original context L, f_i is kept for
+ * r_i >= beta, divided by s for r_i <= alpha and blended linearly in r
+ * between.  YaRN's attention-temperature factor is not applied here: it
+ * belongs to the decode step's softmax_scale. */
+typedef struct {
+  float base;                 /* > 0 (10000 is the usual value)                */
+  float yarn_scale;           /* s > 0; 1 = plain RoPE                         */
+  float yarn_alpha;           /* ramp start, in turns over the original context */
+  float yarn_beta;            /* ramp end, > yarn_alpha (when yarn_scale != 1)  */
+  int32_t yarn_original_len;  /* L > 0 (when yarn_scale != 1)                  */
+} mla_rope_t;
+
+/* Device bytes of workspace mla_cache_append needs for these sizes. */
+size_t mla_cache_append_workspace_bytes(const mla_dims_t* dims, int32_t batch, int32_t d_model);
+
+/* Append the new token of each request to the latent cache (V3 read-through
+ * section 2.2: the KV-side listing and cache.append((c_kv, k_r)); section
+ * 2.3: k_r = RoPE(W_kr h_t); ai-library "DeepSeek-V2" notes, "Model
+ * configuration": RMSNorm after the compressed latent):
+ *   c     = W^DKV h[b]                       (d_latent values)
+ *   c'    = c / sqrt(mean(c^2) + rms_eps) * rms_weight
+ *   k     = RoPE(W^KR h[b], positions[b])    (d_rope values, see mla_rope_t)
+ *   row positions[b] of request b := [c' | k]
+ * h [batch, d_model], w_dkv [d_latent, d_model], w_kr [d_rope, d_model],
+ * rms_weight [d_latent], all in dims->dtype; positions device int32 [batch].
+ * The row is written through cache->data (contiguous or paged exactly as
+ * mla_decode_attn reads it); positions outside [0, max_len) write nothing.
+ * Updating seq_lens is the caller's.  Accumulates in fp32 (angles in fp64),
+ * rounds once to dims->dtype.  Uses dims->d_latent, d_rope and dtype;
+ * d_rope must be even.  Errors: NULL pointers (with batch > 0) ->
+ * MLA_ERR_NULL; d_model < 1, odd d_rope, rms_eps < 0 or not finite, a bad
+ * rope description -> MLA_ERR_DIMS; h, the weights or cache->data not
+ * 16-byte aligned -> MLA_ERR_ALIGN; workspace NULL or smaller than
+ * mla_cache_append_workspace_bytes -> MLA_ERR_WORKSPACE. */
+mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t batch, int32_t d_model,
+                              const void* h, const void* w_dkv, const void* w_kr,
+                              const void* rms_weight, float rms_eps, const mla_rope_t* rope,
+                              const int32_t* positions, const mla_cache_t* cache,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,8 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(mla.Dims) == 20
     assert ctypes.sizeof(mla.CacheDesc) == 40
     assert ctypes.sizeof(mla.Plan) == 24
+    # mla_rope_t: 4 floats and an int32.
+    assert ctypes.sizeof(mla.Rope) == 20
 
 
 def _dims(**kw):
@@ -88,6 +90,45 @@ def test_null_and_bad_dims_rejected_on_host():
                                     None) == 5
     assert L.mla_decode_combine_out(ctypes.byref(_dims()), 0, ctypes.byref(cache), None, None,
                                     0, None, None, None, None, None) == 0
+
+
+def test_cache_append_host_checks():
+    L = mla.lib()
+    fake = ctypes.c_void_p(0x1000)
+    rope = mla.Rope(10000.0, 1.0, 1.0, 32.0, 4096)
+    cache = mla.CacheDesc(0x1000, 0x2000, None, 0, 64, 0)
+    d = _dims()
+    ws = 1 << 20
+    # Workspace size: 16 slices of fp32 sums per request on the MFMA path.
+    assert L.mla_cache_append_workspace_bytes(ctypes.byref(d), 16, 5120) >= 16 * 16 * 576 * 4
+    assert L.mla_cache_append_workspace_bytes(None, 16, 5120) == 0
+
+    def call(**kw):
+        a = dict(dims=ctypes.byref(d), batch=2, d_model=5120, h=fake, w_dkv=fake, w_kr=fake,
+                 g=fake, eps=1e-6, rope=ctypes.byref(rope), pos=fake,
+                 cache=ctypes.byref(cache), ws=fake, ws_bytes=ws)
+        a.update(kw)
+        return L.mla_cache_append(a["dims"], a["batch"], a["d_model"], a["h"], a["w_dkv"],
+                                  a["w_kr"], a["g"], a["eps"], a["rope"], a["pos"], a["cache"],
+                                  a["ws"], a["ws_bytes"], None)
+
+    assert call(batch=0, h=None, w_dkv=None, w_kr=None, g=None, pos=None) == 0
+    assert call(h=None) == 1
+    assert call(pos=None) == 1
+    assert call(rope=None) == 1
+    assert call(d_model=0) == 2
+    assert call(eps=-1.0) == 2
+    assert call(eps=float("nan")) == 2
+    assert call(dims=ctypes.byref(_dims(d_rope=63))) == 2
+    bad_rope = mla.Rope(0.0, 1.0, 1.0, 32.0, 4096)
+    assert call(rope=ctypes.byref(bad_rope)) == 2
+    bad_yarn = mla.Rope(10000.0, 40.0, 32.0, 1.0, 4096)  # beta <= alpha
+    assert call(rope=ctypes.byref(bad_yarn)) == 2
+    no_len = mla.Rope(10000.0, 40.0, 1.0, 32.0, 0)
+    assert call(rope=ctypes.byref(no_len)) == 2
+    assert call(h=ctypes.c_void_p(0x1008)) == 5
+    assert call(ws_bytes=16) == 4
+    assert call(ws=None) == 4
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
