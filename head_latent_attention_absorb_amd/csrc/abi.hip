@@ -75,9 +75,14 @@ size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // Bytes of one partial output element: the MFMA kernel stores bf16 partials.
 size_t partial_elem_bytes(bool mfma) { return mfma ? 2 : sizeof(float); }
 
+// Per (request, split, head) the generic kernel keeps its log-sum-exp, the
+// MFMA kernel the pair (log-sum-exp, reference max) of its unnormalised sum.
+size_t partial_stat_bytes(bool mfma) { return mfma ? 2 * sizeof(float) : sizeof(float); }
+
 size_t workspace_for(const mla_dims_t* d, int batch, int num_splits, bool mfma) {
   const size_t parts = static_cast<size_t>(batch) * num_splits * d->n_heads;
-  return round256(parts * d->d_latent * partial_elem_bytes(mfma)) + round256(parts * sizeof(float));
+  return round256(parts * d->d_latent * partial_elem_bytes(mfma)) +
+         round256(parts * partial_stat_bytes(mfma));
 }
 
 mla_status_t make_plan(const mla_dims_t* d, int batch, const mla_cache_t* c, int split_req,

@@ -1,23 +1,30 @@
 // K3 (split-KV combine) for the bf16 MFMA partials, alone or fused with K4
 // (the W^UV output projection).
 //
-// Combine: the splits s of request b each hold a latent partial O_s
-// normalised by its own softmax sum and its log-sum-exp lse_s; the merged
-// latent output is
-//   o_lat = sum_s exp(lse_s - L) O_s / sum_s exp(lse_s - L),  L = max_s lse_s,
-// and its log-sum-exp is L + ln sum_s exp(lse_s - L) (computed in one pass
-// with a running max, rescaling the sums whenever it grows).  This is the softmax of
+// Combine: split s of request b holds the latent sum U_s = sum_j 2^(x_j - m_s)
+// row_j over its tokens (x_j the scores scaled to log2 units, m_s a reference
+// value of the split, U_s not divided by its softmax sum), its base-2
+// log-sum-exp lse_s = log2 sum_j 2^(x_j) and m_s.  The merged latent output is
+//   o_lat = sum_s 2^(m_s - L) U_s / sum_s 2^(lse_s - L),  L = max_s lse_s
+// (2^(m_s - L) U_s = 2^(lse_s - L) times the split's normalised sum), and its
+// natural-log sum-exp is ln 2 * (L + log2 sum_s 2^(lse_s - L)) (computed in one
+// pass with a running max, rescaling the sums whenever it grows).  This is the softmax of
 // the concatenated scores regrouped by partition, so it equals the single-pass
 // latent weighted sum of the DeepSeek-V2 read-through (2kiu.com/news/6085339),
 // section 2.3.
 // Output projection, applied after the latent-space sum (same section):
 //   out[b, i, h] = sum_c o_lat[b, i, c] W^UV[i, c, h].
 //
-// One workgroup = one head i and up to 8 requests (8 waves).  The MFMA
-// partials are row-major bf16, part_o[((b * S + s) * n_heads + i) * 512 + c],
-// so every (request, split) contributes one contiguous 1 KiB row.  Wave r
-// merges request r, 8 latents per lane, with the loads of kBatch splits (rows
-// and log-sum-exps) in flight at once.  In the fused form the workgroup first starts W^UV[i]
+// One workgroup = one head i and R = 8 / P requests (8 waves, P waves per
+// request).  The MFMA partials are row-major bf16,
+// part_o[((b * S + s) * n_heads + i) * 512 + c], so every (request, split)
+// contributes one contiguous 1 KiB row; (lse_s, m_s) are an fp32 pair per
+// (request, split, head).  Wave p of a request merges splits p, p + P,
+// p + 2P, ..., 8 latents per lane, with the loads of up to kBatch splits
+// (rows and statistics) in flight at once; with P > 1 the waves of a request
+// then merge their results through LDS.  P grows with the split count, so
+// that a request with many splits (few long requests) is not merged by one
+// wave in many dependent memory round trips.  In the fused form the workgroup first starts W^UV[i]
 // (d_latent x d_head bf16, 128 KiB for DeepSeek-V2) streaming into LDS with
 // direct-to-LDS loads, merges the partials while it lands, writes o_lat, and
 // multiplies the bf16 o_lat rows by W^UV[i] with v_mfma_f32_32x32x16_bf16
@@ -32,9 +39,10 @@ namespace {
 
 constexpr int kLat = 512;          // d_latent of the MFMA path
 constexpr int kThreads = 512;      // 8 waves
-constexpr int kRowsPerGroup = 8;   // requests per workgroup
-constexpr int kSegs = kThreads / kRowsPerGroup;  // 64 threads per request, 8 latents each
-constexpr int kBatch = 16;         // splits whose loads are in flight together
+constexpr int kWaves = kThreads / 64;
+constexpr int kRowsPerGroup = 8;   // o_lat rows of the fused product (requests, zero-padded)
+constexpr int kSegs = 64;          // lanes per wave, 8 latents each
+constexpr int kBatch = 16;         // most splits a wave has in flight at once
 constexpr int kMaxHead = 128;      // d_head handled by the fused kernel
 constexpr int kWBytes = kLat * kMaxHead * 2;
 constexpr int kOStride = kLat + 8;  // o_lat rows in LDS, padded against bank conflicts
@@ -54,21 +62,29 @@ __device__ __forceinline__ void load_to_lds16(const void* src, unsigned lds_base
                : "memory", "m0");
 }
 
-template <bool kOut>
+// kB: splits per batch of loads (at most kBatch), sized on the host to the
+// splits a wave merges.
+template <bool kOut, int kB>
 __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
-    const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
+    const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, int batch, int n_heads, int split_tokens,
-    int num_splits, __bf16* __restrict__ out_lat, float* __restrict__ lse_out,
+    int num_splits, int p_log2, __bf16* __restrict__ out_lat, float* __restrict__ lse_out,
     const __bf16* __restrict__ w_uv, __bf16* __restrict__ out, int d_head) {
   __shared__ __attribute__((aligned(16))) uint8_t w_s[kOut ? kWBytes : 16];
   __shared__ __attribute__((aligned(16))) __bf16 o_s[kOut ? kRowsPerGroup * kOStride : 8];
-  __shared__ float red[kOut ? 4 * 16 * 64 : 1];
+  // Per-wave partial sums of the cross-wave merge, later (fused form) the
+  // reduction buffer of the two contraction halves.
+  __shared__ __attribute__((aligned(16))) float red[kWaves * kLat];
+  __shared__ float2 stat_s[kWaves];
+  static_assert(4 * 16 * 64 <= kWaves * kLat, "");
 
   // Workgroups (i, g) and (i, g') are n_heads apart in launch order, so with
   // n_heads % 8 == 0 they land on the same XCD and share W^UV[i] through its
   // L2.
   const int i = blockIdx.x;
-  const int b0 = blockIdx.y * kRowsPerGroup;
+  const int P = 1 << p_log2;                 // waves per request
+  const int R = kWaves >> p_log2;            // requests per workgroup
+  const int b0 = blockIdx.y * R;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
   if constexpr (kOut) {
@@ -83,18 +99,22 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
       load_to_lds16(src + j * 1024, base + j * 1024);
   }
 
-  // Merge: this thread's request (a whole wave per request) and 8 latents.
-  const int r = tid / kSegs, seg = tid % kSegs;
+  // Merge: this wave's request r and split subset p, 8 latents per lane.
+  const int r = wave >> p_log2, p = wave & (P - 1), seg = lane;
   const int b = b0 + r;
   const bool live = b < batch;
   const int len = live ? seq_lens[b] : 0;
   const size_t lbase = static_cast<size_t>(live ? b : 0) * num_splits * n_heads + i;
-  // Single pass with a running max over batches of kBatch splits.  The loads
-  // of a batch (rows and log-sum-exps) are issued together with the length
-  // load, without waiting for it: every split's row lies in the workspace,
-  // and the splits past the request's length (never written: any bits) are
-  // dropped with selects afterwards.  A merge of S splits costs ceil(S /
-  // kBatch) memory round trips.
+  // This wave's splits are p + k * P, k < nk.  Single pass with a running max
+  // over batches of kB of them.  The loads of a batch (rows and statistics)
+  // are issued together with the length load, without waiting for it and
+  // without branches (a branch around a load makes the compiler wait for it
+  // before the branches join): every split's row lies in the workspace,
+  // indexes past the wave's last split are clamped to it, and the splits past
+  // the request's length (never written: any bits) are dropped with selects
+  // afterwards.  A wave's merge of its splits costs ceil(nk / kB) memory round
+  // trips.
+  const int nk = (num_splits - p + P - 1) >> p_log2;
   float L = -INFINITY, W = 0.f;
   float acc[8];
 #pragma unroll
@@ -102,51 +122,108 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   const uint16_t* row = part_o + lbase * kLat + seg * 8;
   const size_t split_stride = static_cast<size_t>(n_heads) * kLat;
   int ns = 0;
-  for (int s0 = 0; s0 < num_splits; s0 += kBatch) {
-    bf16x8_t v[kBatch];
-    float x[kBatch];
+  // One batch: returns false once the batch starts past the used splits.
+  auto merge_batch = [&](int k0) {
+    bf16x8_t v[kB];
+    float x[kB], y[kB];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int s = min(s0 + j, num_splits - 1);
-      v[j] = *reinterpret_cast<const bf16x8_t*>(row + static_cast<size_t>(s) * split_stride);
-      x[j] = part_lse[lbase + static_cast<size_t>(s) * n_heads];
+    for (int j = 0; j < kB; ++j) {
+      const size_t sidx = static_cast<size_t>(p + (min(k0 + j, nk - 1) << p_log2));
+      v[j] = *reinterpret_cast<const bf16x8_t*>(row + sidx * split_stride);
+      const float2 ml = part_ml[lbase + sidx * n_heads];
+      x[j] = ml.x;
+      y[j] = ml.y;
     }
-    ns = used_splits(len, split_tokens);
-    if (s0 >= ns) break;
+    // The length is used only here, behind the loads (laundered so that the
+    // compiler does not hoist its wait in front of them).
+    int len_k = len;
+    asm volatile("" : "+v"(len_k));
+    ns = used_splits(len_k, split_tokens);
+    if (p + (k0 << p_log2) >= ns) return false;
+    bool use[kB];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) x[j] = s0 + j < ns ? x[j] : -INFINITY;
+    for (int j = 0; j < kB; ++j) {
+      use[j] = k0 + j < nk && p + ((k0 + j) << p_log2) < ns;
+      x[j] = use[j] ? x[j] : -INFINITY;
+    }
     float Ln = L;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) Ln = fmaxf(Ln, x[j]);
-    const float alpha = expf(L - Ln);  // 0 on the first batch (L = -inf)
+    for (int j = 0; j < kB; ++j) Ln = fmaxf(Ln, x[j]);
+    const float alpha = __builtin_amdgcn_exp2f(L - Ln);  // 0 on the first batch (L = -inf)
     W *= alpha;
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] *= alpha;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (s0 + j < ns) {
-        const float w = expf(x[j] - Ln);
-        W += w;
+    for (int j = 0; j < kB; ++j) {
+      if (use[j]) {
+        W += __builtin_amdgcn_exp2f(x[j] - Ln);
+        const float w = __builtin_amdgcn_exp2f(y[j] - Ln);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, static_cast<float>(v[j][e]), acc[e]);
       }
     }
     L = Ln;
+    return true;
+  };
+  // The first batch is peeled off the loop: at a loop header the compiler
+  // waits for every outstanding load, the length load included, which would
+  // add a memory round trip in front of the row loads.
+  if (nk > 0 && merge_batch(0))
+    for (int k0 = kB; k0 < nk; k0 += kB)
+      if (!merge_batch(k0)) break;
+  if (P > 1) {
+    // The P waves of a request publish (L, W) and their sums; the first of
+    // them rescales all of them to the common max and adds them up.  A wave
+    // whose splits were all unused has L = -inf and weight 0.
+    *reinterpret_cast<f32x4_t*>(red + wave * kLat + seg * 8) = {acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4_t*>(red + wave * kLat + seg * 8 + 4) = {acc[4], acc[5], acc[6], acc[7]};
+    if (seg == 0) stat_s[wave] = make_float2(L, W);
+    __syncthreads();
+    if (p == 0) {
+      float Lm = -INFINITY;
+      for (int q = 0; q < P; ++q) Lm = fmaxf(Lm, stat_s[wave + q].x);
+      W = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+      for (int q = 0; q < P; ++q) {
+        const float2 st = stat_s[wave + q];
+        const float w = st.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.x - Lm);
+        W += w * st.y;
+        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(red + (wave + q) * kLat + seg * 8);
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(red + (wave + q) * kLat + seg * 8 + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[k] = fmaf(w, a0[k], acc[k]);
+          acc[k + 4] = fmaf(w, a1[k], acc[k + 4]);
+        }
+      }
+      L = Lm;
+    }
+    // red is reused by the fused product below.
+    __syncthreads();
   }
   const float invW = ns > 0 ? 1.f / W : 0.f;
   bf16x8_t ob;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ob[e] = static_cast<__bf16>(acc[e] * invW);
-  if (live) {
+  if (live && p == 0) {
     *reinterpret_cast<bf16x8_t*>(out_lat + (static_cast<size_t>(b) * n_heads + i) * kLat +
                                  seg * 8) = ob;
     if (lse_out != nullptr && seg == 0)
-      lse_out[static_cast<size_t>(b) * n_heads + i] = ns > 0 ? L + logf(W) : -INFINITY;
+      lse_out[static_cast<size_t>(b) * n_heads + i] =
+          ns > 0 ? (L + __log2f(W)) * kLn2 : -INFINITY;
   }
   if constexpr (kOut) {
-    // Fused W^UV product.  o_lat rows (zero past the batch) go to LDS; the
-    // weight stream must have landed before the barrier publishes w_s.
-    *reinterpret_cast<bf16x8_t*>(o_s + r * kOStride + seg * 8) = ob;
+    // Fused W^UV product.  o_lat rows (zero past the batch and past the
+    // workgroup's R requests) go to LDS; the weight stream must have landed
+    // before the barrier publishes w_s.
+    if (p == 0) *reinterpret_cast<bf16x8_t*>(o_s + r * kOStride + seg * 8) = ob;
+    if (wave >= R) {
+      bf16x8_t z;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = static_cast<__bf16>(0.f);
+      *reinterpret_cast<bf16x8_t*>(o_s + wave * kOStride + seg * 8) = z;
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -205,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
         for (int e = 0; e < 4; ++e) {
           const int rr = half * 4 + e;
           const float y = acc2[e] + red[(nb0 * 4 + e) * 64 + lane];
-          if (b0 + rr < batch)
+          if (rr < R && b0 + rr < batch)
             out[(static_cast<size_t>(b0 + rr) * n_heads + i) * d_head + nb * 32 + l32] =
                 static_cast<__bf16>(y);
         }
@@ -213,6 +290,30 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
       __syncthreads();
     }
   }
+}
+
+template <bool kOut, int kB>
+void launch_rows(const DecodeArgs& a, int p_log2, const dim3& grid, const void* w_uv, void* out,
+                 int d_head) {
+  combine_rows_kernel<kOut, kB><<<grid, kThreads, 0, a.stream>>>(
+      static_cast<const uint16_t*>(a.part_o), reinterpret_cast<const float2*>(a.part_lse),
+      a.cache.seq_lens, a.batch, a.n_heads, a.split_tokens, a.num_splits, p_log2,
+      static_cast<__bf16*>(a.out_lat), a.lse, static_cast<const __bf16*>(w_uv),
+      static_cast<__bf16*>(out), d_head);
+}
+
+template <bool kOut>
+void launch_rows_sized(const DecodeArgs& a, int p_log2, const dim3& grid, const void* w_uv,
+                       void* out, int d_head) {
+  const int nk = (a.num_splits + (1 << p_log2) - 1) >> p_log2;  // splits of wave 0
+  if (nk <= 2)
+    launch_rows<kOut, 2>(a, p_log2, grid, w_uv, out, d_head);
+  else if (nk <= 4)
+    launch_rows<kOut, 4>(a, p_log2, grid, w_uv, out, d_head);
+  else if (nk <= 8)
+    launch_rows<kOut, 8>(a, p_log2, grid, w_uv, out, d_head);
+  else
+    launch_rows<kOut, kBatch>(a, p_log2, grid, w_uv, out, d_head);
 }
 
 }  // namespace
@@ -223,18 +324,20 @@ bool combine_out_fusable(int d_latent, int d_head) {
 
 hipError_t launch_combine_rows(const DecodeArgs& a, const void* w_uv, void* out, int d_head) {
   if (a.batch == 0) return hipSuccess;
-  const dim3 grid(a.n_heads, (a.batch + kRowsPerGroup - 1) / kRowsPerGroup);
-  if (w_uv != nullptr) {
-    combine_rows_kernel<true><<<grid, kThreads, 0, a.stream>>>(
-        static_cast<const uint16_t*>(a.part_o), a.part_lse, a.cache.seq_lens, a.batch,
-        a.n_heads, a.split_tokens, a.num_splits, static_cast<__bf16*>(a.out_lat), a.lse,
-        static_cast<const __bf16*>(w_uv), static_cast<__bf16*>(out), d_head);
-  } else {
-    combine_rows_kernel<false><<<grid, kThreads, 0, a.stream>>>(
-        static_cast<const uint16_t*>(a.part_o), a.part_lse, a.cache.seq_lens, a.batch,
-        a.n_heads, a.split_tokens, a.num_splits, static_cast<__bf16*>(a.out_lat), a.lse,
-        nullptr, nullptr, 0);
-  }
+  // Waves per request: the fewest (a power of two up to 8) that leave every
+  // wave at most kBatch splits, so each wave's merge is one memory round
+  // trip.  The fused form stops earlier, at no more than four workgroups per
+  // head: each of them streams its own copy of W^UV[i] into LDS.
+  int p_log2 = 0;
+  while (p_log2 < 3 && (a.num_splits + (1 << p_log2) - 1) >> p_log2 > kBatch) ++p_log2;
+  if (w_uv != nullptr)
+    while (p_log2 > 0 && (a.batch + (kWaves >> p_log2) - 1) / (kWaves >> p_log2) > 4) --p_log2;
+  const int rows = kWaves >> p_log2;
+  const dim3 grid(a.n_heads, (a.batch + rows - 1) / rows);
+  if (w_uv != nullptr)
+    launch_rows_sized<true>(a, p_log2, grid, w_uv, out, d_head);
+  else
+    launch_rows_sized<false>(a, p_log2, grid, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -144,7 +144,6 @@ __global__ __launch_bounds__(kThreads) void combine_rowmajor_kernel(
 
 }  // namespace
 
-// Combine for fragment-order partials written by the MFMA decode kernel.
 hipError_t launch_partials_generic(const DecodeArgs& a) {
   if (a.batch == 0) return hipSuccess;
   const int row = a.d_latent + a.d_rope;
@@ -162,9 +161,9 @@ hipError_t launch_partials_generic(const DecodeArgs& a) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const DecodeArgs& a, bool fragment) {
+hipError_t launch_combine(const DecodeArgs& a, bool mfma_partials) {
   if (a.batch == 0) return hipSuccess;
-  if (fragment) return launch_combine_rows(a, nullptr, nullptr, 0);
+  if (mfma_partials) return launch_combine_rows(a, nullptr, nullptr, 0);
   const dim3 cgrid(a.n_heads, a.batch);
   if (a.dtype == 0) {
     combine_rowmajor_kernel<float><<<cgrid, kThreads, 0, a.stream>>>(

@@ -6,8 +6,9 @@
 //           DeepSeek-V2 read-through, 2kiu.com/news/6085339, sections 2.3-2.4)
 //   O_i   = sum_j softmax_j(s) * row_j[0:512]           (weighted sum in latent
 //           space, section 2.3; the cached latent serves as both K and V)
-// written as a bf16 partial normalised by its own softmax sum plus its fp32
-// log-sum-exp.
+// written as a bf16 partial sum_j 2^(scale*log2(e)*s_j - m) row_j (not divided by
+// its softmax sum: the combine folds both factors into one weight) with the
+// fp32 pair (log2 sum_j 2^(scale*log2(e)*s_j), m).
 //
 // Mapping onto CDNA4:
 //  * One workgroup = 4 waves (one per SIMD) = (request, 128 heads, partition).
@@ -80,7 +81,7 @@ struct MfmaParams {
   int n_heads, split_tokens, num_splits, head_groups, work_items;
   float scale_log2;       // softmax scale * log2(e)
   uint16_t* part_o;       // bf16 partials
-  float* part_lse;
+  float2* part_ml;        // per (request, split, head): (base-2 log-sum-exp, m)
 };
 
 // 16-byte direct-to-LDS load: every lane reads 16 bytes at `src` and writes
@@ -340,14 +341,14 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
                       std::make_integer_sequence<int, kGroups>{});
       load_row_groups(qsrc + (hb0 + 1) * kTile * kRowBytes, tile_dst(3),
                       std::make_integer_sequence<int, kGroups>{});
-      if (round == 0) {
-        issue_tile(0, t0);
-        issue_tile(1, t0 + kTile);
-        // This round's query blocks landed; tiles 0 and 1 may stay in flight.
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGroups));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      }
+      // Tile 0 follows the first round's query loads and tile 1 the second
+      // round's, so the second wait need not cover tile 1: when every
+      // workgroup starts at once, the query and tile 0 arrive sooner with
+      // tile 1 not yet competing for the memory system.  Loads complete in
+      // issue order, so vmcnt(kGroups) means: everything but the tile just
+      // issued has landed.
+      issue_tile(round, t0 + round * kTile);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroups));
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       if ((wave & 2) == hb0) {
@@ -386,9 +387,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       mfma_v(sc, ta[ks], qf[ks]);
   };
 
-  // Prologue: tiles 0 and 1 landed with the query (their wait is the
-  // vmcnt(0) of the second query round).  From here on the compiler sees no
-  // outstanding loads, and the tile loads are governed only by the waits
+  // Prologue: tile 0 landed with the query (the wait of the second query
+  // round); tile 1 may still be in flight.  The compiler does not see these
+  // loads (inline asm), and the tile loads are governed only by the waits
   // below.  Every step issues exactly one tile (past the last tile they
   // re-read the partition's last row into a stage that is never read
   // again), so at step t "this wave's loads of tile t+1 have landed" while
@@ -531,8 +532,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
 #pragma unroll
     for (int i = 0; i < kVWindow; ++i) va[i] = read_v(voff, i);
 
-    if (rescale) {
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
+    // On the first tile every lane's running max is -inf and the accumulators
+    // and the sum are still zero: nothing to rescale.  Skipping it saves 768
+    // VALU instructions (about 4000 cycles) at the start of every partition.
+    if (rescale && t != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       // Scale the accumulators in place in the accumulation registers.  The
       // PV MFMAs that last wrote them retired a whole score pass ago; the
       // s_nops cover the MFMA-to-read wait states regardless.
@@ -585,9 +589,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
 
   // Softmax sum over both lane halves (each half saw half of the tokens).
   l = halves_sum(l);
-  const float inv = 1.f / l;
   // bf16 partial, row-major per (request, split, head):
-  // part_o[((b * S + s) * n_heads + head) * 512 + c].  Register v of latent
+  // part_o[((b * S + s) * n_heads + head) * 512 + c], written as accumulated
+  // (relative to the running max m, not divided by l: the combine applies
+  // both factors as one weight, which saves a multiply per element here).
+  // Register v of latent
   // block cb holds column cb*32 + (v/4)*8 + half*4 + v%4.  The rows pass
   // through LDS (free once every wave is past its last step) so that each
   // global store writes a whole 1 KiB row: wave w owns rows w*32 .. w*32+31,
@@ -602,7 +608,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     for (int g = 0; g < 4; ++g) {
       bf16x4_t v4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][g * 4 + e] * inv);
+      for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][g * 4 + e]);
       *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride + (cb * 32 + g * 8 + half * 4) * 2) = v4;
     }
   uint16_t* dst = p.part_o +
@@ -616,8 +622,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     *reinterpret_cast<bf16x8_t*>(dst + r * 512) =
         *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
   if (half == 0)
-    p.part_lse[(static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + head] =
-        (m + __log2f(l)) * kLn2;
+    p.part_ml[(static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + head] =
+        make_float2(m + __log2f(l), m);
 }
 
 }  // namespace
@@ -634,7 +640,7 @@ hipError_t launch_partials_mfma(const DecodeArgs& a) {
   p.work_items = a.batch * a.num_splits * a.head_groups;
   p.scale_log2 = a.softmax_scale * kLog2e;
   p.part_o = static_cast<uint16_t*>(a.part_o);
-  p.part_lse = a.part_lse;
+  p.part_ml = reinterpret_cast<float2*>(a.part_lse);
   const int grid = (p.work_items + 7) / 8 * 8;  // multiple of the 8 XCDs
   if (a.cache.page_table != nullptr)
     decode_mfma_kernel<true><<<grid, 256, 0, a.stream>>>(p);

@@ -9,10 +9,12 @@
 namespace mla {
 
 // Split-KV partial results of the decode kernels live in the caller's
-// workspace: row-major partial outputs [request, split, head, d_latent]
-// normalised by their own softmax sum (fp32 from the generic kernel, bf16
-// from the MFMA kernel) and the fp32 natural-log sum-exp per (request,
-// split, head).
+// workspace: row-major partial outputs [request, split, head, d_latent] and
+// per (request, split, head) statistics behind them.  The generic kernel
+// writes fp32 sums normalised by their own softmax sum and the fp32
+// natural-log sum-exp; the MFMA kernel writes bf16 sums relative to a
+// reference max m (not normalised) and the fp32 pair (log-sum-exp, m), both
+// in base-2 log units.
 
 struct CacheView {
   const uint8_t* data;      // cache rows, (d_latent + d_rope) elements each
@@ -32,7 +34,7 @@ struct DecodeArgs {
   void* out_lat;
   float* lse;           // may be nullptr
   void* part_o;         // workspace: fp32 (generic kernel) or bf16 (MFMA kernel)
-  float* part_lse;      // workspace
+  float* part_lse;      // workspace: lse (generic kernel) or (lse, m) pairs (MFMA kernel)
   hipStream_t stream;
 };
 
@@ -51,9 +53,9 @@ hipError_t launch_partials_generic(const DecodeArgs& a);
 // bf16 MFMA split-KV partials for d_latent = 512, d_rope = 64,
 // n_heads % 128 == 0.
 hipError_t launch_partials_mfma(const DecodeArgs& a);
-// Merge the partials of each request into out_lat / lse.  `fragment` selects
-// the bf16 partials written by the MFMA kernel (else fp32).
-hipError_t launch_combine(const DecodeArgs& a, bool fragment);
+// Merge the partials of each request into out_lat / lse.  `mfma_partials`
+// selects the layout written by the MFMA kernel (else the generic one).
+hipError_t launch_combine(const DecodeArgs& a, bool mfma_partials);
 // Merge of the MFMA kernel's partials into out_lat / lse and, when w_uv is
 // not null, the W^UV product of the merged rows into out in the same kernel
 // (requires combine_out_fusable(d_latent, d_head)).

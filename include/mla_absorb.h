@@ -152,12 +152,14 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* 
  *
  * mla_decode_partials: for every request b, split s and head i with tokens in
  *   [s*split_tokens, min((s+1)*split_tokens, seq_lens[b])), writes into the
- *   workspace the split's softmax-normalised latent sum and its natural-log
- *   sum-exp (fp32).  The workspace layout is private to the library and
- *   depends on plan->kernel.  Splits with no tokens are not written.
- * mla_decode_combine: merges the used splits of each request with weights
- *   exp(lse_s - max_s lse_s) into out_lat (dims->dtype) and lse (fp32, may be
- *   NULL); it reads only seq_lens from `cache` (data may be NULL).
+ *   workspace the split's softmax-weighted latent sum and the fp32
+ *   statistics that weight it in the merge (its natural-log sum-exp among
+ *   them).  The workspace layout is private to the library and depends on
+ *   plan->kernel.  Splits with no tokens are not written.
+ * mla_decode_combine: merges the used splits of each request, split s
+ *   weighted by exp(lse_s - max_s lse_s) relative to its normalised sum, into
+ *   out_lat (dims->dtype) and lse (fp32, may be NULL); it reads only seq_lens
+ *   from `cache` (data may be NULL).
  * Arguments, errors and the plan rule are those of mla_decode_attn. */
 mla_status_t mla_decode_partials(const mla_dims_t* dims, int32_t batch, const void* q_cat,
                                  const mla_cache_t* cache, float softmax_scale,

@@ -182,6 +182,41 @@ def test_combine_out_matches_separate_calls(cfg, split):
     assert_close(from_dev(o_lat2), o_ref, "bf16", "o_lat")
 
 
+# Many splits per request: 157 partitions of 32 tokens, so the merge spreads
+# each request over 8 waves (two batches of loads each), and the short
+# requests leave most of those waves without a used split.
+MANY_SPLITS = DSV2.replace(name="dsv2_b3_many_splits", batch=3, len_lo=1, len_hi=5000,
+                           max_len=5024)
+
+
+@pytest.mark.parametrize("lens", [(1, 300, 5000), (5000, 33, 4097)], ids=["short_first", "long_first"])
+def test_combine_many_splits(lens):
+    cfg = MANY_SPLITS
+    case = make_case(cfg, 21, seq_lens=np.array(lens, np.int32), pad_value=np.nan)
+    _log(f"[many_splits] lens={lens}")
+    dc = DevCase(case)
+    q_np = draw_latent_query(cfg, 21)
+    q_dev = _bf16_dev(q_np)
+    plan = mla.decode_plan(cfg.n_heads, cfg.d_latent, cfg.d_rope, torch.bfloat16, dc.cache,
+                           split_tokens=32, d_head=cfg.d_head)
+    assert plan.num_splits == 157
+    ws = mla.workspace_for(plan, "cuda")
+    mla.decode_partials(q_dev, dc.cache, cfg.scale, plan, ws)
+    shape = (cfg.batch, cfg.n_heads, cfg.d_latent)
+    o_lat1 = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse1 = torch.empty(shape[:2], dtype=torch.float32, device="cuda")
+    mla.decode_combine(dc.cache, cfg.n_heads, plan, ws, o_lat1, lse1)
+    o_lat2 = torch.empty_like(o_lat1)
+    lse2 = torch.empty_like(lse1)
+    mla.decode_combine_out(dc.cache, plan, ws, dc.w_uv, o_lat2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(o_lat1, o_lat2) and torch.equal(lse1, lse2)
+    heads = np.arange(0, 128, 9)
+    o_ref, lse_ref = _latent_ref(case, q_np, heads=heads)
+    assert_close(from_dev(o_lat1)[:, heads], o_ref[:, heads], "bf16", "o_lat")
+    assert_close(from_dev(lse1)[:, heads], lse_ref[:, heads], "bf16", "lse")
+
+
 @pytest.mark.parametrize("seed", [0, 4])
 def test_tiny_f32_combine_out(seed):
     """fp32 storage takes the generic merge and projection behind the same call."""
