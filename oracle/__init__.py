@@ -19,7 +19,8 @@ pages is partly garbled; each reading taken is stated where it is used):
   section "Multi-Head Latent Attention" (4.5 d_h l, shared k^R, concatenation).
 * [V3 read-through] "DeepSeek-V3 technical report" read-through,
   2kiu.com/news/6340724 -- sections 2.2 (what is cached), 2.3 (absorption,
-  k = [k_c; k_r]), 2.4.
+  k = [k_c; k_r]), 2.4, 4.1 (multi-token prediction used for speculative
+  decoding, whose verification decodes several new tokens at once).
 
 * [zeeklog] also: the YaRN paragraph (s = 40, alpha = 1, beta = 32, sqrt(t))
   and the d = 5120 hidden width of the worked example.
@@ -39,6 +40,7 @@ from .mla_ref import (  # noqa: F401
     gather_rows,
     kv_cache_bytes,
     latent_attention,
+    latent_attention_causal,
     mla_decode_absorbed,
     mla_decode_reference,
     project_out,

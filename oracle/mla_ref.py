@@ -200,6 +200,32 @@ def latent_attention(q_cat: np.ndarray, rows: np.ndarray, d_latent: int, scale: 
     return o_lat, (m + np.log(z))[:, 0]
 
 
+def latent_attention_causal(q_cat: np.ndarray, rows: np.ndarray, d_latent: int,
+                            scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Several new tokens of one request decoded at once, each attending
+    causally (speculative-decoding verification: the extra prediction depths
+    propose q_len - 1 further tokens and the main model checks all of them in
+    one pass; V3 read-through, section 4.1, and the causal attention over
+    positions 1..t of the zeeklog MHA equation).
+
+    q_cat [q_len, n_h, d_c + d_h^R]: the queries of the request's last q_len
+    positions, whose rows are already among `rows` [T, d_c + d_h^R].  New token
+    j sits at position T - q_len + j and attends to rows 0 .. T - q_len + j,
+    i.e. latent_attention over the first T - q_len + j + 1 rows (none when
+    that count is <= 0).  Returns (o_lat [q_len, n_h, d_c], lse [q_len, n_h]).
+    """
+    q_cat = np.asarray(q_cat, np.float64)
+    q_len, n_h = q_cat.shape[:2]
+    T = np.asarray(rows).shape[0]
+    o_lat = np.zeros((q_len, n_h, d_latent))
+    lse = np.full((q_len, n_h), -np.inf)
+    for j in range(q_len):
+        visible = T - q_len + j + 1
+        o_lat[j], lse[j] = latent_attention(q_cat[j], np.asarray(rows)[:max(visible, 0)],
+                                            d_latent, scale)
+    return o_lat, lse
+
+
 def project_out(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
     """Apply W^UV after the latent-space sum: o_i[h] = sum_c W^UV[i,c,h] o_lat_i[c]
     (V2 read-through section 2.3; zeeklog equation 11 moved past the sum).
