@@ -42,12 +42,13 @@ class CacheDesc(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [("split_tokens", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("kernel", ctypes.c_int32), ("head_groups", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("q_len", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
     def __repr__(self):
         return (f"Plan(split_tokens={self.split_tokens}, num_splits={self.num_splits}, "
                 f"kernel={'mfma' if self.kernel == 1 else 'generic'}, "
-                f"head_groups={self.head_groups}, workspace_bytes={self.workspace_bytes})")
+                f"head_groups={self.head_groups}, q_len={self.q_len}, "
+                f"workspace_bytes={self.workspace_bytes})")
 
 
 class Rope(ctypes.Structure):
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_plan.restype = ctypes.c_int
     L.mla_decode_plan.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(CacheDesc), i32,
                                   ctypes.POINTER(Plan)]
+    L.mla_decode_plan_mq.restype = ctypes.c_int
+    L.mla_decode_plan_mq.argtypes = [ctypes.POINTER(Dims), i32, i32, ctypes.POINTER(CacheDesc),
+                                     i32, ctypes.POINTER(Plan)]
     L.mla_decode_attn.restype = ctypes.c_int
     L.mla_decode_attn.argtypes = [ctypes.POINTER(Dims), i32, vp, ctypes.POINTER(CacheDesc),
                                   ctypes.c_float, ctypes.POINTER(Plan), vp, vp, vp, sz, vp]
@@ -197,14 +201,46 @@ def absorb_q(q_c: torch.Tensor, q_r: torch.Tensor, w_uk: torch.Tensor,
 
 
 def decode_plan(n_heads: int, d_latent: int, d_rope: int, dtype, cache: LatentCache,
-                split_tokens: int = 0, d_head: int = 1) -> Plan:
+                split_tokens: int = 0, d_head: int = 1, q_len: int = 1) -> Plan:
+    """Split-KV plan for `cache`; q_len > 1 plans the causal decode of the last
+    q_len positions of every request at once (mla_decode_plan_mq)."""
     dims = make_dims(n_heads, d_head, d_rope, d_latent, dtype)
     plan = Plan()
     desc = cache.desc()
-    _check("mla_decode_plan", lib().mla_decode_plan(ctypes.byref(dims), cache.batch(),
-                                                    ctypes.byref(desc), split_tokens,
-                                                    ctypes.byref(plan)))
+    if q_len == 1:
+        _check("mla_decode_plan", lib().mla_decode_plan(ctypes.byref(dims), cache.batch(),
+                                                        ctypes.byref(desc), split_tokens,
+                                                        ctypes.byref(plan)))
+    else:
+        _check("mla_decode_plan_mq", lib().mla_decode_plan_mq(
+            ctypes.byref(dims), cache.batch(), int(q_len), ctypes.byref(desc), split_tokens,
+            ctypes.byref(plan)))
     return plan
+
+
+def _query_shape(q_cat: torch.Tensor, plan: Optional[Plan]):
+    """(B, q_len, n_h, row) of a [B, n_h, row] or [B, q_len, n_h, row] query,
+    checked against the plan's q_len."""
+    if q_cat.dim() == 3:
+        B, nh, row = q_cat.shape
+        q_len = 1
+    elif q_cat.dim() == 4:
+        B, q_len, nh, row = q_cat.shape
+    else:
+        raise ValueError(f"q_cat must be [B, n_h, row] or [B, q_len, n_h, row], got "
+                         f"{tuple(q_cat.shape)}")
+    if plan is not None and int(plan.q_len) != q_len:
+        raise ValueError(f"q_cat holds {q_len} query tokens per request, the plan "
+                         f"{int(plan.q_len)}")
+    return B, q_len, nh, row
+
+
+def _lead(B: int, q_len: int, token_axis: bool):
+    """Leading output shape: [B] for a [B, n_h, ...] query, [B, q_len] for a
+    [B, q_len, n_h, ...] one (a token axis is required when q_len > 1)."""
+    if q_len > 1 and not token_axis:
+        raise ValueError(f"the plan has {q_len} query tokens: outputs need a token axis")
+    return (B, q_len) if token_axis else (B,)
 
 
 def workspace_for(plan: Plan, device) -> torch.Tensor:
@@ -217,8 +253,11 @@ def decode_attn(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,
                 plan: Optional[Plan] = None, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                 stream=None, split_tokens: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Latent-space decode attention; returns (o_lat [B,n_h,d_c], lse [B,n_h] fp32)."""
-    B, nh, row = q_cat.shape
+    """Latent-space decode attention; returns (o_lat [B,n_h,d_c], lse [B,n_h] fp32).
+    With a [B, q_len, n_h, row] query (and a plan for q_len), the last q_len
+    positions of each request attend causally: o_lat [B,q_len,n_h,d_c],
+    lse [B,q_len,n_h]."""
+    B, q_len, nh, row = _query_shape(q_cat, plan)
     if cache.data.shape[2] != row:
         raise ValueError(f"cache row width {cache.data.shape[2]} != q_cat width {row}")
     d_rope = int(cache.d_rope)
@@ -230,18 +269,16 @@ def decode_attn(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,
     dims = make_dims(nh, 1, d_rope, d_latent, _dtype_code(q_cat))
     desc = cache.desc()
     if plan is None:
-        plan = Plan()
-        _check("mla_decode_plan", lib().mla_decode_plan(ctypes.byref(dims), B,
-                                                        ctypes.byref(desc), split_tokens,
-                                                        ctypes.byref(plan)))
+        plan = decode_plan(nh, d_latent, d_rope, q_cat.dtype, cache, split_tokens, q_len=q_len)
     if workspace is None:
         workspace = workspace_for(plan, dev)
+    lead = _lead(B, q_len, q_cat.dim() == 4)
     if out is None:
-        out = torch.empty((B, nh, d_latent), dtype=q_cat.dtype, device=dev)
+        out = torch.empty(lead + (nh, d_latent), dtype=q_cat.dtype, device=dev)
     if lse is None:
-        lse = torch.empty((B, nh), dtype=torch.float32, device=dev)
-    _require(out, "out", (B, nh, d_latent), q_cat.dtype, dev)
-    _require(lse, "lse", (B, nh), torch.float32, dev)
+        lse = torch.empty(lead + (nh,), dtype=torch.float32, device=dev)
+    _require(out, "out", lead + (nh, d_latent), q_cat.dtype, dev)
+    _require(lse, "lse", lead + (nh,), torch.float32, dev)
     _check("mla_decode_attn", lib().mla_decode_attn(
         ctypes.byref(dims), B, _ptr(q_cat), ctypes.byref(desc), float(softmax_scale),
         ctypes.byref(plan), _ptr(out), _ptr(lse), _ptr(workspace),
@@ -252,7 +289,7 @@ def decode_attn(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,
 def decode_partials(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,
                     plan: Plan, workspace: torch.Tensor, stream=None) -> None:
     """First phase of decode_attn: per-split partials into `workspace`."""
-    B, nh, row = q_cat.shape
+    B, _, nh, row = _query_shape(q_cat, plan)
     d_rope = int(cache.d_rope)
     dims = make_dims(nh, 1, d_rope, row - d_rope, _dtype_code(q_cat))
     desc = cache.desc()
@@ -264,10 +301,13 @@ def decode_partials(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: floa
 
 def decode_combine(cache: LatentCache, n_heads: int, plan: Plan, workspace: torch.Tensor,
                    out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Second phase of decode_attn: merge the partials into out (and lse)."""
+    """Second phase of decode_attn: merge the partials into out (and lse);
+    out is [B, n_h, d_c], or [B, q_len, n_h, d_c] with a plan for q_len."""
     B = cache.batch()
     d_rope = int(cache.d_rope)
-    d_latent = out.shape[2]
+    d_latent = out.shape[-1]
+    _require(out, "out", _lead(B, int(plan.q_len), out.dim() == 4) + (n_heads, d_latent),
+             out.dtype, out.device)
     dims = make_dims(n_heads, 1, d_rope, d_latent, _dtype_code(out))
     desc = cache.desc()
     _check("mla_decode_combine", lib().mla_decode_combine(
@@ -280,15 +320,17 @@ def decode_combine_out(cache: LatentCache, plan: Plan, workspace: torch.Tensor,
                        lse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                        stream=None) -> torch.Tensor:
     """decode_combine then out_uv in one call: merges the partials into out_lat
-    (and lse) and returns o[b,i,h] = sum_c o_lat[b,i,c] W^UV[i,c,h]."""
+    (and lse) and returns o[b,i,h] = sum_c o_lat[b,i,c] W^UV[i,c,h] (with a
+    leading q_len axis after B when the plan has several query tokens)."""
     B = cache.batch()
     nh, dc, dh = w_uv.shape
     d_rope = int(cache.d_rope)
     dims = make_dims(nh, dh, d_rope, dc, _dtype_code(out_lat))
-    _require(out_lat, "out_lat", (B, nh, dc), w_uv.dtype, w_uv.device)
+    lead = _lead(B, int(plan.q_len), out_lat.dim() == 4)
+    _require(out_lat, "out_lat", lead + (nh, dc), w_uv.dtype, w_uv.device)
     if out is None:
-        out = torch.empty((B, nh, dh), dtype=w_uv.dtype, device=w_uv.device)
-    _require(out, "out", (B, nh, dh), w_uv.dtype, w_uv.device)
+        out = torch.empty(lead + (nh, dh), dtype=w_uv.dtype, device=w_uv.device)
+    _require(out, "out", lead + (nh, dh), w_uv.dtype, w_uv.device)
     desc = cache.desc()
     _check("mla_decode_combine_out", lib().mla_decode_combine_out(
         ctypes.byref(dims), B, ctypes.byref(desc), ctypes.byref(plan), _ptr(workspace),

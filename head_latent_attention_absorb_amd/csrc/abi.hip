@@ -72,6 +72,9 @@ mla_status_t check_cache(const mla_cache_t* c) {
 
 size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Most query tokens per request a plan accepts.
+constexpr int kMaxQueryLen = 16;
+
 // Bytes of one partial output element: the MFMA kernel stores bf16 partials.
 size_t partial_elem_bytes(bool mfma) { return mfma ? 2 : sizeof(float); }
 
@@ -79,17 +82,19 @@ size_t partial_elem_bytes(bool mfma) { return mfma ? 2 : sizeof(float); }
 // MFMA kernel the pair (log-sum-exp, reference max) of its unnormalised sum.
 size_t partial_stat_bytes(bool mfma) { return mfma ? 2 * sizeof(float) : sizeof(float); }
 
-size_t workspace_for(const mla_dims_t* d, int batch, int num_splits, bool mfma) {
-  const size_t parts = static_cast<size_t>(batch) * num_splits * d->n_heads;
+size_t workspace_for(const mla_dims_t* d, int batch, int q_len, int num_splits, bool mfma) {
+  const size_t parts = static_cast<size_t>(batch) * num_splits * q_len * d->n_heads;
   return round256(parts * d->d_latent * partial_elem_bytes(mfma)) +
          round256(parts * partial_stat_bytes(mfma));
 }
 
-mla_status_t make_plan(const mla_dims_t* d, int batch, const mla_cache_t* c, int split_req,
-                       const DeviceInfo& dev, mla_decode_plan_t* plan) {
+mla_status_t make_plan(const mla_dims_t* d, int batch, int q_len, const mla_cache_t* c,
+                       int split_req, const DeviceInfo& dev, mla_decode_plan_t* plan) {
+  if (q_len < 1 || q_len > kMaxQueryLen) return MLA_ERR_DIMS;
   const bool mfma = use_mfma(d, c);
   const int granule = mfma ? mla::kMfmaTokenGranule : 1;
-  const int groups = mfma ? d->n_heads / mla::kMfmaHeadsPerGroup : d->n_heads;
+  // Head groups count the query rows of all q_len tokens of a request.
+  const int groups = mfma ? q_len * d->n_heads / mla::kMfmaHeadsPerGroup : q_len * d->n_heads;
   const int max_len = c->max_len;
   const int len_cap = max_len > 0 ? (max_len + granule - 1) / granule * granule : granule;
   int split;
@@ -118,7 +123,8 @@ mla_status_t make_plan(const mla_dims_t* d, int batch, const mla_cache_t* c, int
   plan->num_splits = num_splits;
   plan->kernel = mfma ? 1 : 0;
   plan->head_groups = groups;
-  plan->workspace_bytes = workspace_for(d, batch, num_splits, mfma);
+  plan->q_len = q_len;
+  plan->workspace_bytes = workspace_for(d, batch, q_len, num_splits, mfma);
   return MLA_OK;
 }
 
@@ -140,7 +146,7 @@ const char* mla_status_str(mla_status_t s) {
   return "MLA_ERR_UNKNOWN";
 }
 
-int32_t mla_abi_version(void) { return 1; }
+int32_t mla_abi_version(void) { return 2; }
 
 mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch, const void* q_c,
                           const void* q_r, const void* w_uk, void* q_cat, void* stream) {
@@ -172,7 +178,20 @@ mla_status_t mla_decode_plan(const mla_dims_t* dims, int32_t batch, const mla_ca
   if (batch < 0) return MLA_ERR_DIMS;
   DeviceInfo dev;
   if ((st = current_device(&dev)) != MLA_OK) return st;
-  return make_plan(dims, batch, cache, split_tokens, dev, plan);
+  return make_plan(dims, batch, 1, cache, split_tokens, dev, plan);
+}
+
+mla_status_t mla_decode_plan_mq(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                const mla_cache_t* cache, int32_t split_tokens,
+                                mla_decode_plan_t* plan) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (plan == nullptr) return MLA_ERR_NULL;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch < 0) return MLA_ERR_DIMS;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != MLA_OK) return st;
+  return make_plan(dims, batch, q_len, cache, split_tokens, dev, plan);
 }
 
 }  // extern "C"
@@ -204,14 +223,15 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
   if ((st = current_device(&dev)) != MLA_OK) return st;
 
   if (plan == nullptr) {
-    if ((st = make_plan(dims, batch, cache, 0, dev, plan_out)) != MLA_OK) return st;
+    if ((st = make_plan(dims, batch, 1, cache, 0, dev, plan_out)) != MLA_OK) return st;
   } else {
     // A caller's plan must be one this library would produce for these sizes.
-    if ((st = make_plan(dims, batch, cache, plan->split_tokens, dev, plan_out)) != MLA_OK)
+    if ((st = make_plan(dims, batch, plan->q_len, cache, plan->split_tokens, dev, plan_out)) !=
+        MLA_OK)
       return st;
     if (plan_out->split_tokens != plan->split_tokens ||
         plan_out->num_splits != plan->num_splits || plan_out->kernel != plan->kernel ||
-        plan_out->head_groups != plan->head_groups ||
+        plan_out->head_groups != plan->head_groups || plan_out->q_len != plan->q_len ||
         plan_out->workspace_bytes != plan->workspace_bytes)
       return MLA_ERR_DIMS;
   }
@@ -219,9 +239,11 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
     return MLA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MLA_ERR_ALIGN;
 
-  const size_t parts_n = static_cast<size_t>(batch) * plan_out->num_splits * dims->n_heads;
+  const size_t parts_n =
+      static_cast<size_t>(batch) * plan_out->num_splits * plan_out->q_len * dims->n_heads;
   a->batch = batch;
   a->n_heads = dims->n_heads;
+  a->q_len = plan_out->q_len;
   a->d_latent = dims->d_latent;
   a->d_rope = dims->d_rope;
   a->dtype = dims->dtype;
@@ -329,14 +351,17 @@ mla_status_t mla_decode_combine_out(const mla_dims_t* dims, int32_t batch,
   // combine and the weight-streaming projection are faster (measured at
   // n_heads 128, d_latent 512: 18.0 vs 18.9 us at 32 requests, 30.0 vs 21.4
   // at 64).
-  if (p.kernel == 1 && batch <= kFusedTailMaxBatch &&
+  if (p.kernel == 1 && batch * p.q_len <= kFusedTailMaxBatch &&
       mla::combine_out_fusable(dims->d_latent, dims->d_head)) {
     const hipError_t e = mla::launch_combine_rows(a, w_uv, out, dims->d_head);
     return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
   }
   if ((st = run_combine(a, p)) != MLA_OK) return st;
-  const hipError_t e = mla::launch_out_uv(dims->dtype, batch, dims->n_heads, dims->d_head,
-                                          dims->d_latent, out_lat, w_uv, out, a.stream);
+  // o_lat rows are [batch, q_len, n_heads]: the projection sees batch * q_len
+  // requests.
+  const hipError_t e = mla::launch_out_uv(dims->dtype, batch * p.q_len, dims->n_heads,
+                                          dims->d_head, dims->d_latent, out_lat, w_uv, out,
+                                          a.stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 

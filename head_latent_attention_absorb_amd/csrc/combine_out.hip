@@ -17,7 +17,7 @@
 //
 // One workgroup = one head i and R = 8 / P requests (8 waves, P waves per
 // request).  The MFMA partials are row-major bf16,
-// part_o[((b * S + s) * n_heads + i) * 512 + c], so every (request, split)
+// part_o[((b * S + s) * n_rows + i) * 512 + c], so every (request, split)
 // contributes one contiguous 1 KiB row; (lse_s, m_s) are an fp32 pair per
 // (request, split, head).  Wave p of a request merges splits p, p + P,
 // p + 2P, ..., 8 latents per lane, with the loads of up to kBatch splits
@@ -67,7 +67,8 @@ __device__ __forceinline__ void load_to_lds16(const void* src, unsigned lds_base
 template <bool kOut, int kB>
 __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
     const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_lens, int batch, int n_heads, int split_tokens,
+    const int32_t* __restrict__ seq_lens, int batch, int n_rows, int heads_per_token, int q_len,
+    int split_tokens,
     int num_splits, int p_log2, __bf16* __restrict__ out_lat, float* __restrict__ lse_out,
     const __bf16* __restrict__ w_uv, __bf16* __restrict__ out, int d_head) {
   __shared__ __attribute__((aligned(16))) uint8_t w_s[kOut ? kWBytes : 16];
@@ -78,8 +79,10 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   __shared__ float2 stat_s[kWaves];
   static_assert(4 * 16 * 64 <= kWaves * kLat, "");
 
-  // Workgroups (i, g) and (i, g') are n_heads apart in launch order, so with
-  // n_heads % 8 == 0 they land on the same XCD and share W^UV[i] through its
+  // Row i of a request: query token i / heads_per_token, head i % heads_per_token
+  // (one token per request unless several are verified at once).
+  // Workgroups (i, g) and (i, g') are n_rows apart in launch order, so with
+  // n_rows % 8 == 0 they land on the same XCD and share W^UV[i] through its
   // L2.
   const int i = blockIdx.x;
   const int P = 1 << p_log2;                 // waves per request
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
     // Start W^UV[i] streaming into LDS: a linear copy of its d_latent x d_head
     // bf16 elements, 1 KiB per wave instruction.
     const uint8_t* src = reinterpret_cast<const uint8_t*>(w_uv) +
-                         static_cast<size_t>(i) * kLat * d_head * 2 + lane * 16;
+                         static_cast<size_t>(i % heads_per_token) * kLat * d_head * 2 + lane * 16;
     const unsigned base = static_cast<unsigned>(
         reinterpret_cast<uintptr_t>((MLA_LDS uint8_t*)w_s));
     const int chunks = kLat * d_head * 2 / 1024;
@@ -103,8 +106,9 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   const int r = wave >> p_log2, p = wave & (P - 1), seg = lane;
   const int b = b0 + r;
   const bool live = b < batch;
-  const int len = live ? seq_lens[b] : 0;
-  const size_t lbase = static_cast<size_t>(live ? b : 0) * num_splits * n_heads + i;
+  // The rows this query token sees: up to its own position.
+  const int len = live ? seq_lens[b] - (q_len - 1 - i / heads_per_token) : 0;
+  const size_t lbase = static_cast<size_t>(live ? b : 0) * num_splits * n_rows + i;
   // This wave's splits are p + k * P, k < nk.  Single pass with a running max
   // over batches of kB of them.  The loads of a batch (rows and statistics)
   // are issued together with the length load, without waiting for it and
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
   const uint16_t* row = part_o + lbase * kLat + seg * 8;
-  const size_t split_stride = static_cast<size_t>(n_heads) * kLat;
+  const size_t split_stride = static_cast<size_t>(n_rows) * kLat;
   int ns = 0;
   // One batch: returns false once the batch starts past the used splits.
   auto merge_batch = [&](int k0) {
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
     for (int j = 0; j < kB; ++j) {
       const size_t sidx = static_cast<size_t>(p + (min(k0 + j, nk - 1) << p_log2));
       v[j] = *reinterpret_cast<const bf16x8_t*>(row + sidx * split_stride);
-      const float2 ml = part_ml[lbase + sidx * n_heads];
+      const float2 ml = part_ml[lbase + sidx * n_rows];
       x[j] = ml.x;
       y[j] = ml.y;
     }
@@ -207,10 +211,10 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) ob[e] = static_cast<__bf16>(acc[e] * invW);
   if (live && p == 0) {
-    *reinterpret_cast<bf16x8_t*>(out_lat + (static_cast<size_t>(b) * n_heads + i) * kLat +
+    *reinterpret_cast<bf16x8_t*>(out_lat + (static_cast<size_t>(b) * n_rows + i) * kLat +
                                  seg * 8) = ob;
     if (lse_out != nullptr && seg == 0)
-      lse_out[static_cast<size_t>(b) * n_heads + i] =
+      lse_out[static_cast<size_t>(b) * n_rows + i] =
           ns > 0 ? (L + __log2f(W)) * kLn2 : -INFINITY;
   }
   if constexpr (kOut) {
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
           const int rr = half * 4 + e;
           const float y = acc2[e] + red[(nb0 * 4 + e) * 64 + lane];
           if (rr < R && b0 + rr < batch)
-            out[(static_cast<size_t>(b0 + rr) * n_heads + i) * d_head + nb * 32 + l32] =
+            out[(static_cast<size_t>(b0 + rr) * n_rows + i) * d_head + nb * 32 + l32] =
                 static_cast<__bf16>(y);
         }
       }
@@ -297,7 +301,8 @@ void launch_rows(const DecodeArgs& a, int p_log2, const dim3& grid, const void* 
                  int d_head) {
   combine_rows_kernel<kOut, kB><<<grid, kThreads, 0, a.stream>>>(
       static_cast<const uint16_t*>(a.part_o), reinterpret_cast<const float2*>(a.part_lse),
-      a.cache.seq_lens, a.batch, a.n_heads, a.split_tokens, a.num_splits, p_log2,
+      a.cache.seq_lens, a.batch, a.q_len * a.n_heads, a.n_heads, a.q_len, a.split_tokens,
+      a.num_splits, p_log2,
       static_cast<__bf16*>(a.out_lat), a.lse, static_cast<const __bf16*>(w_uv),
       static_cast<__bf16*>(out), d_head);
 }
@@ -327,13 +332,16 @@ hipError_t launch_combine_rows(const DecodeArgs& a, const void* w_uv, void* out,
   // Waves per request: the fewest (a power of two up to 8) that leave every
   // wave at most kBatch splits, so each wave's merge is one memory round
   // trip.  The fused form stops earlier, at no more than four workgroups per
-  // head: each of them streams its own copy of W^UV[i] into LDS.
+  // head (counting every query token's rows): each of them streams its own
+  // copy of W^UV[i] into LDS.
   int p_log2 = 0;
   while (p_log2 < 3 && (a.num_splits + (1 << p_log2) - 1) >> p_log2 > kBatch) ++p_log2;
   if (w_uv != nullptr)
-    while (p_log2 > 0 && (a.batch + (kWaves >> p_log2) - 1) / (kWaves >> p_log2) > 4) --p_log2;
+    while (p_log2 > 0 &&
+           a.q_len * ((a.batch + (kWaves >> p_log2) - 1) / (kWaves >> p_log2)) > 4)
+      --p_log2;
   const int rows = kWaves >> p_log2;
-  const dim3 grid(a.n_heads, (a.batch + rows - 1) / rows);
+  const dim3 grid(a.q_len * a.n_heads, (a.batch + rows - 1) / rows);
   if (w_uv != nullptr)
     launch_rows_sized<true>(a, p_log2, grid, w_uv, out, d_head);
   else

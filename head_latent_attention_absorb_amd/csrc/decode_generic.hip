@@ -12,6 +12,11 @@
 // Partials are normalised by their own softmax sum and stored with their
 // natural-log sum-exp; the combine merges splits s with weights
 // exp(lse_s - max_s lse_s).
+//
+// Rows: n_rows = q_len * heads_per_token query rows per request, token-major;
+// row i belongs to query token j = i / heads_per_token, which sees the
+// request's first seq_len - (q_len - 1 - j) cached rows (the rows up to its
+// own position).
 
 #include "device_common.h"
 
@@ -20,6 +25,16 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxLatentPerThread = 8;  // d_latent <= 2048
+
+// Number of splits that hold tokens of a request of length len.
+__device__ __forceinline__ int used_splits(int len, int split_tokens) {
+  return len > 0 ? (len + split_tokens - 1) / split_tokens : 0;
+}
+
+// Rows visible to query row i of a request holding `len` rows.
+__device__ __forceinline__ int visible_rows(int len, int i, int heads_per_token, int q_len) {
+  return len - (q_len - 1 - i / heads_per_token);
+}
 
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
@@ -39,25 +54,25 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// grid: x = split, y = head, z = request.  Partials row-major:
-// part_o[((b * S + s) * n_heads + i) * d_latent + c], part_lse[(b * S + s) * n_heads + i].
+// grid: x = split, y = query row, z = request.  Partials row-major:
+// part_o[((b * S + s) * n_rows + i) * d_latent + c], part_lse[(b * S + s) * n_rows + i].
 template <typename T>
 __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
-    const T* __restrict__ q_cat, CacheView cache, int n_heads, int d_latent, int d_rope,
-    float scale, int split_tokens, int num_splits, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    const T* __restrict__ q_cat, CacheView cache, int n_rows, int heads_per_token, int q_len,
+    int d_latent, int d_rope, float scale, int split_tokens, int num_splits,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
   extern __shared__ float sm[];
   const int row = d_latent + d_rope;
   float* q_s = sm;                 // [row]
   float* p_s = sm + row;           // [kThreads]
   float* red = p_s + kThreads;     // [4]
   const int s = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-  const int len = cache.seq_lens[b];
+  const int len = visible_rows(cache.seq_lens[b], i, heads_per_token, q_len);
   const int t0 = s * split_tokens;
   const int t1 = min(t0 + split_tokens, len);
   if (t0 >= t1) return;  // the combine never reads splits past the length
 
-  const T* q = q_cat + (static_cast<size_t>(b) * n_heads + i) * row;
+  const T* q = q_cat + (static_cast<size_t>(b) * n_rows + i) * row;
   for (int k = threadIdx.x; k < row; k += kThreads) q_s[k] = ld(q + k);
   __syncthreads();
 
@@ -101,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
   }
 
   const float inv = 1.f / l;
-  const size_t base = (static_cast<size_t>(b) * num_splits + s) * n_heads + i;
+  const size_t base = (static_cast<size_t>(b) * num_splits + s) * n_rows + i;
 #pragma unroll
   for (int r = 0; r < kMaxLatentPerThread; ++r) {
     const int c = threadIdx.x + r * kThreads;
@@ -110,19 +125,18 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
   if (threadIdx.x == 0) part_lse[base] = m + logf(l);
 }
 
-// Number of splits that hold tokens of a request of length len.
-__device__ __forceinline__ int used_splits(int len, int split_tokens) {
-  return len > 0 ? (len + split_tokens - 1) / split_tokens : 0;
-}
 
-// Combine for row-major partials.  grid: x = head, y = request.
+// Combine for row-major partials.  grid: x = query row, y = request.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_rowmajor_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ seq_lens, int n_heads, int d_latent, int split_tokens,
-    int num_splits, T* __restrict__ out_lat, float* __restrict__ lse_out) {
+    const int32_t* __restrict__ seq_lens, int n_rows, int heads_per_token, int q_len,
+    int d_latent, int split_tokens, int num_splits, T* __restrict__ out_lat,
+    float* __restrict__ lse_out) {
   const int i = blockIdx.x, b = blockIdx.y;
-  const int ns = used_splits(seq_lens[b], split_tokens);
+  const int ns =
+      used_splits(visible_rows(seq_lens[b], i, heads_per_token, q_len), split_tokens);
+  const int n_heads = n_rows;  // strides below are per query row
   const size_t obase = (static_cast<size_t>(b) * n_heads + i) * d_latent;
   const size_t pbase = static_cast<size_t>(b) * num_splits * n_heads + i;
   float L = -INFINITY;
@@ -147,16 +161,19 @@ __global__ __launch_bounds__(kThreads) void combine_rowmajor_kernel(
 hipError_t launch_partials_generic(const DecodeArgs& a) {
   if (a.batch == 0) return hipSuccess;
   const int row = a.d_latent + a.d_rope;
+  const int n_rows = a.q_len * a.n_heads;
   const size_t lds = sizeof(float) * (row + kThreads + 4);
-  const dim3 grid(a.num_splits, a.n_heads, a.batch);
+  const dim3 grid(a.num_splits, n_rows, a.batch);
   if (a.dtype == 0) {
     decode_generic_kernel<float><<<grid, kThreads, lds, a.stream>>>(
-        static_cast<const float*>(a.q_cat), a.cache, a.n_heads, a.d_latent, a.d_rope,
-        a.softmax_scale, a.split_tokens, a.num_splits, static_cast<float*>(a.part_o), a.part_lse);
+        static_cast<const float*>(a.q_cat), a.cache, n_rows, a.n_heads, a.q_len, a.d_latent,
+        a.d_rope, a.softmax_scale, a.split_tokens, a.num_splits, static_cast<float*>(a.part_o),
+        a.part_lse);
   } else {
     decode_generic_kernel<__bf16><<<grid, kThreads, lds, a.stream>>>(
-        static_cast<const __bf16*>(a.q_cat), a.cache, a.n_heads, a.d_latent, a.d_rope,
-        a.softmax_scale, a.split_tokens, a.num_splits, static_cast<float*>(a.part_o), a.part_lse);
+        static_cast<const __bf16*>(a.q_cat), a.cache, n_rows, a.n_heads, a.q_len, a.d_latent,
+        a.d_rope, a.softmax_scale, a.split_tokens, a.num_splits, static_cast<float*>(a.part_o),
+        a.part_lse);
   }
   return hipGetLastError();
 }
@@ -164,15 +181,18 @@ hipError_t launch_partials_generic(const DecodeArgs& a) {
 hipError_t launch_combine(const DecodeArgs& a, bool mfma_partials) {
   if (a.batch == 0) return hipSuccess;
   if (mfma_partials) return launch_combine_rows(a, nullptr, nullptr, 0);
-  const dim3 cgrid(a.n_heads, a.batch);
+  const int n_rows = a.q_len * a.n_heads;
+  const dim3 cgrid(n_rows, a.batch);
   if (a.dtype == 0) {
     combine_rowmajor_kernel<float><<<cgrid, kThreads, 0, a.stream>>>(
-        static_cast<const float*>(a.part_o), a.part_lse, a.cache.seq_lens, a.n_heads, a.d_latent,
-        a.split_tokens, a.num_splits, static_cast<float*>(a.out_lat), a.lse);
+        static_cast<const float*>(a.part_o), a.part_lse, a.cache.seq_lens, n_rows, a.n_heads,
+        a.q_len, a.d_latent, a.split_tokens, a.num_splits, static_cast<float*>(a.out_lat),
+        a.lse);
   } else {
     combine_rowmajor_kernel<__bf16><<<cgrid, kThreads, 0, a.stream>>>(
-        static_cast<const float*>(a.part_o), a.part_lse, a.cache.seq_lens, a.n_heads, a.d_latent,
-        a.split_tokens, a.num_splits, static_cast<__bf16*>(a.out_lat), a.lse);
+        static_cast<const float*>(a.part_o), a.part_lse, a.cache.seq_lens, n_rows, a.n_heads,
+        a.q_len, a.d_latent, a.split_tokens, a.num_splits, static_cast<__bf16*>(a.out_lat),
+        a.lse);
   }
   return hipGetLastError();
 }

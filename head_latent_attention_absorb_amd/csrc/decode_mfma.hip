@@ -76,9 +76,11 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4)
 constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
 struct MfmaParams {
-  const uint16_t* q_cat;  // [B, n_heads, 576] bf16
+  const uint16_t* q_cat;  // [B, n_rows, 576] bf16
   CacheView cache;
-  int n_heads, split_tokens, num_splits, head_groups, work_items;
+  // Query rows per request: q_len tokens x heads_per_token heads, token-major.
+  int n_rows, heads_per_token, q_len;
+  int split_tokens, num_splits, head_groups, work_items;
   float scale_log2;       // softmax scale * log2(e)
   uint16_t* part_o;       // bf16 partials
   float2* part_ml;        // per (request, split, head): (base-2 log-sum-exp, m)
@@ -212,7 +214,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   const int s = rest % p.num_splits;
   const int b = rest / p.num_splits;
 
-  const int len = p.cache.seq_lens[b];
+  // Query token j of the request (head group g covers rows g*128 ..) sees
+  // the rows up to its own position: q_len - 1 - j fewer than the request.
+  const int len = p.cache.seq_lens[b] -
+                  (p.q_len - 1 - g * kMfmaHeadsPerGroup / p.heads_per_token);
   const int t0 = s * p.split_tokens;
   const int t1 = min(t0 + p.split_tokens, len);
   if (t0 >= t1) return;  // the combine never reads partitions past the length
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   bf16x8_t qf[kKSteps];
   {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(p.q_cat) +
-                          (static_cast<size_t>(b) * p.n_heads + g * kMfmaHeadsPerGroup + n_load) *
+                          (static_cast<size_t>(b) * p.n_rows + g * kMfmaHeadsPerGroup + n_load) *
                               kRowBytes + chunk_off;
     for (int round = 0; round < 2; ++round) {
       const int hb0 = 2 - 2 * round;  // first head block of this round
@@ -590,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // Softmax sum over both lane halves (each half saw half of the tokens).
   l = halves_sum(l);
   // bf16 partial, row-major per (request, split, head):
-  // part_o[((b * S + s) * n_heads + head) * 512 + c], written as accumulated
+  // part_o[((b * S + s) * n_rows + row) * 512 + c], written as accumulated
   // (relative to the running max m, not divided by l: the combine applies
   // both factors as one weight, which saves a multiply per element here).
   // Register v of latent
@@ -612,7 +617,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride + (cb * 32 + g * 8 + half * 4) * 2) = v4;
     }
   uint16_t* dst = p.part_o +
-                  ((static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + hblock * 32) * 512 +
+                  ((static_cast<size_t>(b) * p.num_splits + s) * p.n_rows + hblock * 32) * 512 +
                   lane * 8;
   // Plain stores: the combine that reads the partials right after this
   // kernel finds them in the last-level cache (non-temporal stores make this
@@ -622,7 +627,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     *reinterpret_cast<bf16x8_t*>(dst + r * 512) =
         *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
   if (half == 0)
-    p.part_ml[(static_cast<size_t>(b) * p.num_splits + s) * p.n_heads + head] =
+    p.part_ml[(static_cast<size_t>(b) * p.num_splits + s) * p.n_rows + head] =
         make_float2(m + __log2f(l), m);
 }
 
@@ -633,7 +638,9 @@ hipError_t launch_partials_mfma(const DecodeArgs& a) {
   MfmaParams p;
   p.q_cat = static_cast<const uint16_t*>(a.q_cat);
   p.cache = a.cache;
-  p.n_heads = a.n_heads;
+  p.n_rows = a.q_len * a.n_heads;
+  p.heads_per_token = a.n_heads;
+  p.q_len = a.q_len;
   p.split_tokens = a.split_tokens;
   p.num_splits = a.num_splits;
   p.head_groups = a.head_groups;

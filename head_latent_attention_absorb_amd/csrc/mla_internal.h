@@ -25,8 +25,14 @@ struct CacheView {
   int32_t max_pages;        // max_len / page_size when paged
 };
 
+// Several query tokens per request (q_len > 1): q_cat, the outputs and the
+// partials hold q_len * n_heads rows per request, token-major ([B, q_len,
+// n_heads, ...]); query token j of request b is the one at position
+// seq_lens[b] - q_len + j and attends to the rows up to its own position,
+// seq_lens[b] - (q_len - 1 - j) of them.
 struct DecodeArgs {
   int32_t batch, n_heads, d_latent, d_rope, dtype;
+  int32_t q_len;        // query tokens per request (1 for plain decode)
   const void* q_cat;
   CacheView cache;
   float softmax_scale;
@@ -60,6 +66,7 @@ hipError_t launch_combine(const DecodeArgs& a, bool mfma_partials);
 // not null, the W^UV product of the merged rows into out in the same kernel
 // (requires combine_out_fusable(d_latent, d_head)).
 bool combine_out_fusable(int d_latent, int d_head);
+// (w_uv is indexed by head, out by row: [B, q_len, n_heads, d_head].)
 hipError_t launch_combine_rows(const DecodeArgs& a, const void* w_uv, void* out, int d_head);
 
 // Cache append: projections of the new token's hidden state, RMSNorm of the

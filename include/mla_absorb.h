@@ -90,19 +90,23 @@ typedef struct {
 
 /* Split-KV plan: each request's tokens are cut into partitions of
  * split_tokens tokens that run on different compute units and are merged by
- * their log-sum-exp weights.  Produced by mla_decode_plan. */
+ * their log-sum-exp weights.  Produced by mla_decode_plan or
+ * mla_decode_plan_mq; every decode call takes its query count from it. */
 typedef struct {
   int32_t split_tokens;   /* tokens per partition                              */
   int32_t num_splits;     /* partitions per request, ceil(max_len/split_tokens) */
   int32_t kernel;         /* 0 = generic fp32-VALU kernel, 1 = bf16 MFMA kernel */
-  int32_t head_groups;    /* heads are processed in this many groups           */
+  int32_t head_groups;    /* query rows (q_len * n_heads) are processed in this
+                             many groups                                      */
+  int32_t q_len;          /* query tokens per request (1 = plain decode)       */
   size_t workspace_bytes; /* device bytes mla_decode_attn needs                */
 } mla_decode_plan_t;
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* mla_status_str(mla_status_t status);
 
-/* Library ABI version (incremented on any signature change). */
+/* Library ABI version (incremented on any signature change; 2 added
+ * mla_decode_plan_t.q_len and mla_decode_plan_mq). */
 int32_t mla_abi_version(void);
 
 /* Absorb W^UK into the query (V2 read-through section 2.3; V3 read-through
@@ -125,6 +129,23 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch, const void* q_c
 mla_status_t mla_decode_plan(const mla_dims_t* dims, int32_t batch, const mla_cache_t* cache,
                              int32_t split_tokens, mla_decode_plan_t* plan);
 
+/* As mla_decode_plan, for q_len query tokens per request (1 <= q_len <= 16):
+ * the verification pass of speculative decoding, where tokens proposed by the
+ * extra prediction depths are checked by the main model in one step (V3
+ * read-through section 4.1).  The last q_len cached rows of request b are the
+ * new tokens; query token j (0-based) is the one at position
+ * seq_lens[b] - q_len + j and attends causally to rows
+ * 0 .. seq_lens[b] - q_len + j (zeeklog MHA equation: attention over
+ * positions 1..t).  With such a plan every decode call takes q_cat as
+ * [batch, q_len, n_heads, d_latent + d_rope] and writes out_lat
+ * [batch, q_len, n_heads, d_latent], lse [batch, q_len, n_heads] and, for
+ * mla_decode_combine_out, out [batch, q_len, n_heads, d_head]; a token with
+ * no visible row gets out_lat = 0 and lse = -inf.  q_len outside 1..16 ->
+ * MLA_ERR_DIMS; other errors as mla_decode_plan. */
+mla_status_t mla_decode_plan_mq(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                const mla_cache_t* cache, int32_t split_tokens,
+                                mla_decode_plan_t* plan);
+
 /* Latent-space decode attention over the cache (V2 read-through section 2.3:
  * scores against the cached latent, weighted sum in latent space; zeeklog MHA
  * equation for the softmax):
@@ -134,9 +155,10 @@ mla_status_t mla_decode_plan(const mla_dims_t* dims, int32_t batch, const mla_ca
  * q_cat [batch, n_heads, d_latent + d_rope]; out_lat [batch, n_heads,
  * d_latent] (dims->dtype); lse [batch, n_heads] fp32, may be NULL.
  * A request with seq_lens[b] == 0 yields out_lat = 0 and lse = -inf.
- * `plan` (host pointer) may be NULL: the library plans with split_tokens = 0.
- * A plan passed in must come from mla_decode_plan with the same dims, batch
- * and cache bounds.  workspace: device, >= plan->workspace_bytes, 256-byte
+ * `plan` (host pointer) may be NULL: the library plans with split_tokens = 0
+ * and one query token.  A plan passed in must come from mla_decode_plan (or
+ * mla_decode_plan_mq, whose q_len then sets the shapes) with the same dims,
+ * batch and cache bounds.  workspace: device, >= plan->workspace_bytes, 256-byte
  * aligned, contents need no initialisation; calls that share a workspace
  * must be ordered on one stream. */
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* q_cat,

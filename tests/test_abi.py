@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_absorb_q", "mla_decode_attn", "mla_out_uv", "mla_decode_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
-    assert L.mla_abi_version() == 1
+    assert L.mla_abi_version() == 2
 
 
 def test_status_strings():
@@ -46,7 +46,7 @@ def test_struct_sizes_match_header():
     # mla_dims_t: 5 x int32; mla_cache_t: 3 pointers, 2 int32, int64; plan: 4 int32 + size_t.
     assert ctypes.sizeof(mla.Dims) == 20
     assert ctypes.sizeof(mla.CacheDesc) == 40
-    assert ctypes.sizeof(mla.Plan) == 24
+    assert ctypes.sizeof(mla.Plan) == 32
     # mla_rope_t: 4 floats and an int32.
     assert ctypes.sizeof(mla.Rope) == 20
 
@@ -170,11 +170,23 @@ def test_plan_shapes_and_workspace_errors():
     assert st == 5
     # A plan whose split count does not match its split length is rejected.
     bad = mla.Plan(plan.split_tokens, plan.num_splits - 1, plan.kernel, plan.head_groups,
-                   plan.workspace_bytes)
+                   plan.q_len, plan.workspace_bytes)
     st = L.mla_decode_attn(ctypes.byref(d), B, q.data_ptr(), ctypes.byref(desc), 0.07,
                            ctypes.byref(bad), out.data_ptr(), None, ws.data_ptr(),
                            plan.workspace_bytes, None)
     assert st == 2
+    # So is a plan whose query count was changed by hand (its head groups and
+    # workspace no longer match), and a query count out of range.
+    bad = mla.Plan(plan.split_tokens, plan.num_splits, plan.kernel, plan.head_groups,
+                   2, plan.workspace_bytes)
+    st = L.mla_decode_attn(ctypes.byref(d), B, q.data_ptr(), ctypes.byref(desc), 0.07,
+                           ctypes.byref(bad), out.data_ptr(), None, ws.data_ptr(),
+                           plan.workspace_bytes, None)
+    assert st == 2
+    p2 = mla.Plan()
+    for q_len in (0, 17):
+        assert L.mla_decode_plan_mq(ctypes.byref(d), B, q_len, ctypes.byref(desc), 0,
+                                    ctypes.byref(p2)) == 2
     torch.cuda.synchronize()
 
 
