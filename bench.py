@@ -39,7 +39,8 @@ from workload import CONFIGS, f32_to_bf16_bits, make_append_case, make_case  # n
 
 METRIC = "MLA decode tokens/s and latent-cache HBM GB/s (% roofline), B=16 T=4096"
 WORKLOAD = "dsv2_b16_t4096"
-WORKLOADS = ("dsv2_b16_t4096", "ragged_b4_16k_32k", "paged_b128_t2048", "ctx128k_b2_60l")
+WORKLOADS = ("dsv2_b16_t4096", "ragged_b4_16k_32k", "paged_b128_t2048", "ctx128k_b2_60l",
+             "mtp2_b16_t4096")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partials_dsv2_b16_t4096_counters.json")
@@ -208,6 +209,11 @@ def main():
     name = args.workload
     cfg = CONFIGS[name]
     B, nh, row = cfg.batch, cfg.n_heads, cfg.row
+    # Query tokens per request: the verification workload decodes the last
+    # q_len positions of every request at once; the absorb and the output
+    # projection then see B * q_len query rows.
+    ql = cfg.q_len
+    lead = (B,) if ql == 1 else (B, ql)
     layered = cfg.layers > 1
     log(f"[bench] generating inputs for {name}")
     if layered:
@@ -224,22 +230,24 @@ def main():
 
     dev = "cuda"
     plan = mla.decode_plan(nh, cfg.d_latent, cfg.d_rope, torch.bfloat16, pool[0].cache,
-                           split_tokens=args.split_tokens, d_head=cfg.d_head)
+                           split_tokens=args.split_tokens, d_head=cfg.d_head, q_len=ql)
     log(f"[bench] {plan}")
     ws = mla.workspace_for(plan, dev)
     append_ws = torch.empty(max(256, int(mla.lib().mla_cache_append_workspace_bytes(
         mla.make_dims(1, 1, cfg.d_rope, cfg.d_latent, torch.bfloat16), B, cfg.hidden))),
         dtype=torch.uint8, device=dev)
-    q_cat = torch.empty((B, nh, row), dtype=torch.bfloat16, device=dev)
-    o_lat = torch.empty((B, nh, cfg.d_latent), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, nh), dtype=torch.float32, device=dev)
-    o = torch.empty((B, nh, cfg.d_head), dtype=torch.bfloat16, device=dev)
+    q_cat = torch.empty(lead + (nh, row), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty(lead + (nh, cfg.d_latent), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(lead + (nh,), dtype=torch.float32, device=dev)
+    o = torch.empty(lead + (nh, cfg.d_head), dtype=torch.bfloat16, device=dev)
+    q_rows = q_cat.view(B * ql, nh, row)
     stream = torch.cuda.current_stream()
 
     def layer(e: Entry, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        mla.absorb_q(e.q_c, e.q_r, e.w_uk, out=q_cat)
+        mla.absorb_q(e.q_c.view(B * ql, nh, cfg.d_head), e.q_r.view(B * ql, nh, cfg.d_rope),
+                     e.w_uk, out=q_rows)
         if ev is not None:
             ev[1].record(stream)
         mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
@@ -341,20 +349,29 @@ def main():
               else sum(pool[i % n_pool].tokens for i in range(args.steps)) / args.steps)
     tokens_layer = tokens / layers_per_step
     cache_bytes = tokens * row * 2
-    q_bytes = layers_per_step * B * nh * row * 2
-    olat_bytes = layers_per_step * B * nh * (cfg.d_latent * 2 + 4)
-    flops = 2.0 * nh * (row + cfg.d_latent) * tokens
+    q_bytes = layers_per_step * B * ql * nh * row * 2
+    olat_bytes = layers_per_step * B * ql * nh * (cfg.d_latent * 2 + 4)
+    # Query token j of a request sees ql - 1 - j rows fewer than the request
+    # holds (causal among the new tokens).
+    visible = ql * tokens - layers_per_step * B * ql * (ql - 1) / 2
+    flops = 2.0 * nh * (row + cfg.d_latent) * visible
     attn_bytes = cache_bytes + q_bytes + olat_bytes
     t_roof_attn_us = max(attn_bytes / (HBM_PEAK_GBPS * 1e9),
                          flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
     k2_bytes = (cache_bytes + q_bytes) / layers_per_step
     k2_gbps = k2_bytes / (decode_us * 1e-6) / 1e9
+    k2_tflops = flops / layers_per_step / (decode_us * 1e-6) / 1e12
+    # The decode kernel's bound: HBM, unless its products take longer at the
+    # MFMA peak (several query tokens per request raise the flops per byte).
+    k2_mfma_bound = (flops / layers_per_step / (MFMA_BF16_PEAK_TFLOPS * 1e12) >
+                     k2_bytes / (HBM_PEAK_GBPS * 1e9))
     # Whole step: the cache, both up-projection weights, the query in and the
     # output out, each moved once.
     w_bytes = layers_per_step * 2 * nh * cfg.d_head * cfg.d_latent * 2
-    io_bytes = layers_per_step * (B * nh * (cfg.d_head + cfg.d_rope) * 2 + B * nh * cfg.d_head * 2)
+    io_bytes = layers_per_step * B * ql * (nh * (cfg.d_head + cfg.d_rope) * 2 +
+                                           nh * cfg.d_head * 2)
     step_bytes = cache_bytes + w_bytes + io_bytes
-    step_flops = flops + layers_per_step * 2.0 * 2 * B * nh * cfg.d_head * cfg.d_latent
+    step_flops = flops + layers_per_step * 2.0 * 2 * B * ql * nh * cfg.d_head * cfg.d_latent
     t_roof_us = max(step_bytes / (HBM_PEAK_GBPS * 1e9),
                     step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
     sha = kernel_sha()
@@ -362,7 +379,9 @@ def main():
     result = {
         "metric": METRIC if name == WORKLOAD else
                   f"MLA decode tokens/s and latent-cache HBM GB/s (% roofline), {name}",
-        "value": B / (ms_per_step * 1e-3),
+        # Tokens decoded per second: every query token of every request (the
+        # verification workload decodes q_len per request and step).
+        "value": B * ql / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -380,7 +399,8 @@ def main():
             "cache": f"paged, {cfg.page_size}-token pages" if cfg.paged else "contiguous",
             "layers_per_step": layers_per_step,
             "rotating_pool_mb": round(pool_mb), "split_tokens": plan.split_tokens,
-            "num_splits": plan.num_splits, "parallelism": "single-gpu",
+            "num_splits": plan.num_splits, "query_tokens_per_request": ql,
+            "parallelism": "single-gpu",
         },
         "step_us": percentiles(step_us),
         "step_roofline_us": t_roof_us,
@@ -398,15 +418,17 @@ def main():
         "kernels_us": dict(kernels_us, decode_partials_back_to_back=decode_us),
         "roofline": {
             "kernel": "decode_mfma_kernel (mla_decode_partials)",
-            "bound": "hbm",
-            "achieved": k2_gbps,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": k2_gbps / HBM_PEAK_GBPS,
+            "bound": "mfma" if k2_mfma_bound else "hbm",
+            "achieved": k2_tflops if k2_mfma_bound else k2_gbps,
+            "peak": MFMA_BF16_PEAK_TFLOPS if k2_mfma_bound else HBM_PEAK_GBPS,
+            "unit": "TFLOP/s" if k2_mfma_bound else "GB/s",
+            "frac": (k2_tflops / MFMA_BF16_PEAK_TFLOPS if k2_mfma_bound
+                     else k2_gbps / HBM_PEAK_GBPS),
+            "achieved_GBps": k2_gbps,
             "traffic": traffic_from_counters(sha) if name == WORKLOAD else None,
             "alg_bytes_per_launch": k2_bytes,
             "launch_us": decode_us,
-            "mfma_tflops": flops / layers_per_step / (decode_us * 1e-6) / 1e12,
+            "mfma_tflops": k2_tflops,
             "kernel_source_sha": sha,
         },
     }
@@ -415,7 +437,8 @@ def main():
         # plus h, the RMSNorm weight and the written rows.
         ap_bytes = (row * cfg.hidden + B * cfg.hidden + cfg.d_latent + B * row) * 2 + B * 4
         result["cache_append"] = {
-            "what": "mla_cache_append (projection + RMSNorm + RoPE + row write), per step",
+            "what": ("mla_cache_append (projection + RMSNorm + RoPE + row write) of one new "
+                     "token per request, per step"),
             "us": kernels_us["cache_append"],
             "alg_bytes": ap_bytes,
             "roofline_us": ap_bytes / (HBM_PEAK_GBPS * 1e9) * 1e6,

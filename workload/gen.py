@@ -75,6 +75,7 @@ class WorkloadConfig:
     layers: int = 1
     softmax_scale: Optional[float] = None   # None => 1/sqrt(d_head + d_rope)
     d_model: int = 0         # hidden width d of the cache append; 0 => n_heads * d_head
+    q_len: int = 1           # query tokens per request (several: speculative verification)
 
     @property
     def row(self) -> int:
@@ -122,6 +123,11 @@ CONFIGS: Dict[str, WorkloadConfig] = {
     "paged_b128_t2048": WorkloadConfig("paged_b128_t2048", batch=128, dtype="bf16",
                                        len_lo=1, len_hi=2048, max_len=2048,
                                        page_size=64, **_DSV2),
+    # Speculative verification: B=16, T=4096, the last 2 positions of every
+    # request decoded at once (causal between them).
+    "mtp2_b16_t4096": WorkloadConfig("mtp2_b16_t4096", batch=16, dtype="bf16",
+                                     len_lo=4096, len_hi=4096, max_len=4096, q_len=2,
+                                     **_DSV2),
     # 128K-context decode: B=2, T=131072, 60 independently seeded layers.
     "ctx128k_b2_60l": WorkloadConfig("ctx128k_b2_60l", batch=2, dtype="bf16",
                                      len_lo=131072, len_hi=131072, max_len=131072,
@@ -147,8 +153,8 @@ class Case:
     seed: int
     seq_lens: np.ndarray            # [B] int32
     page_table: Optional[np.ndarray]  # [B, max_pages] int32, or None
-    q_c: np.ndarray                 # [B, n_h, d_h]
-    q_r: np.ndarray                 # [B, n_h, d_h^R]
+    q_c: np.ndarray                 # [B, n_h, d_h] ([B, q_len, n_h, d_h] if q_len > 1)
+    q_r: np.ndarray                 # [B, n_h, d_h^R] (likewise)
     cache: np.ndarray               # see class docstring
     w_uk: np.ndarray                # [n_h, d_h, d_c]
     w_uv: np.ndarray                # [n_h, d_c, d_h]
@@ -205,8 +211,11 @@ def make_case(cfg: WorkloadConfig, seed: int, *, pad_value: float = 0.0,
         n_pages = B * cfg.max_pages
         page_table = rng.permutation(n_pages).astype(np.int32).reshape(B, cfg.max_pages)
 
-    q_c = _draw(rng, (B, nh, dh), 1.0, cfg.dtype)
-    q_r = _draw(rng, (B, nh, dr), 1.0, cfg.dtype)
+    # With several query tokens per request, q^C and q^R hold them token-major
+    # ([B, q_len, n_h, .]); one token keeps the [B, n_h, .] shape.
+    lead = (B,) if cfg.q_len == 1 else (B, cfg.q_len)
+    q_c = _draw(rng, lead + (nh, dh), 1.0, cfg.dtype)
+    q_r = _draw(rng, lead + (nh, dr), 1.0, cfg.dtype)
     total = int(lens.sum())
     c_kv = _draw(rng, (total, dc), 1.0, cfg.dtype)
     k_r = _draw(rng, (total, dr), 1.0, cfg.dtype)
