@@ -25,11 +25,15 @@ pages is partly garbled; each reading taken is stated where it is used):
 * [zeeklog] also: the YaRN paragraph (s = 40, alpha = 1, beta = 32, sqrt(t))
   and the d = 5120 hidden width of the worked example.
 * [ai-library] also: "Model configuration" (RMSNorm after the compressed
-  latent) and "Long-Context Extension" (YaRN only on k^R).
+  latent), "Long-Context Extension" (YaRN only on k^R) and "Training and
+  Inference Efficiency" / "Inference cost" (the KV cache quantised to about 6
+  bits per element at deployment).
 
 Parity status: every function below is pinned by a test in
-``tests/test_oracle_pins.py`` (decode) or ``tests/test_oracle_append.py``
-(cache append) except where its docstring says "parity unpinned".
+``tests/test_oracle_pins.py`` (decode), ``tests/test_oracle_append.py``
+(cache append), ``tests/test_oracle_causal.py`` (several query tokens) or
+``tests/test_oracle_quant.py`` (low-bit cache) except where its docstring says
+"parity unpinned".
 """
 
 from .mla_ref import (  # noqa: F401
@@ -46,6 +50,13 @@ from .mla_ref import (  # noqa: F401
     project_out,
     softmax_attention,
     up_project,
+)
+from .quant_ref import (  # noqa: F401
+    E4M3_MAX,
+    dequantize_rows,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_rows,
 )
 from .append_ref import (  # noqa: F401
     append_into,
