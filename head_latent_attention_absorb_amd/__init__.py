@@ -25,6 +25,7 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libmla_absorb.so")
 
 MLA_F32, MLA_BF16 = 0, 1
+MLA_ROWS_NATIVE, MLA_ROWS_FP8 = 0, 1
 
 
 class Dims(ctypes.Structure):
@@ -36,7 +37,8 @@ class Dims(ctypes.Structure):
 class CacheDesc(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
                 ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
-                ("max_len", ctypes.c_int32), ("num_pages", ctypes.c_int64)]
+                ("max_len", ctypes.c_int32), ("num_pages", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("row_format", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -100,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_combine_out.restype = ctypes.c_int
     L.mla_decode_combine_out.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(CacheDesc),
                                          ctypes.POINTER(Plan), vp, sz, vp, vp, vp, vp, vp]
+    L.mla_quantize_rows.restype = ctypes.c_int
+    L.mla_quantize_rows.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, vp]
     L.mla_out_uv.restype = ctypes.c_int
     L.mla_out_uv.argtypes = [ctypes.POINTER(Dims), i32, vp, vp, vp, vp]
     L.mla_cache_append_workspace_bytes.restype = sz
@@ -154,6 +158,8 @@ class LatentCache:
     data: contiguous [B, max_len, d_latent + d_rope] or paged
           [num_pages, page_size, d_latent + d_rope]
     seq_lens: int32 [B]; page_table: int32 [B, max_len // page_size] or None.
+    scales: for a low-bit cache, fp32 [B, max_len] or [num_pages, page_size]
+          (one per row) with data holding uint8 E4M3 codes; None otherwise.
     """
 
     data: torch.Tensor
@@ -162,6 +168,7 @@ class LatentCache:
     page_table: Optional[torch.Tensor] = None
     page_size: int = 0
     max_len: int = 0
+    scales: Optional[torch.Tensor] = None
 
     def desc(self) -> CacheDesc:
         d = CacheDesc()
@@ -171,6 +178,9 @@ class LatentCache:
         d.page_size = self.page_size if self.page_table is not None else 0
         d.max_len = self.max_len if self.page_table is not None else self.data.shape[1]
         d.num_pages = self.data.shape[0] if self.page_table is not None else 0
+        if self.scales is not None:
+            d.scales = self.scales.data_ptr()
+            d.row_format = MLA_ROWS_FP8
         return d
 
     def batch(self) -> int:
@@ -264,8 +274,10 @@ def decode_attn(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,
     d_latent = row - d_rope
     dev = q_cat.device
     _require(cache.seq_lens, "seq_lens", (B,), torch.int32, dev)
-    if cache.data.dtype != q_cat.dtype:
+    if cache.scales is None and cache.data.dtype != q_cat.dtype:
         raise TypeError("cache and q_cat dtypes differ")
+    if cache.scales is not None and cache.data.dtype != torch.uint8:
+        raise TypeError("a low-bit cache holds uint8 E4M3 codes")
     dims = make_dims(nh, 1, d_rope, d_latent, _dtype_code(q_cat))
     desc = cache.desc()
     if plan is None:
@@ -356,12 +368,42 @@ def out_uv(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] 
 
 def latent_cache(data: torch.Tensor, seq_lens: torch.Tensor, d_rope: int,
                  page_table: Optional[torch.Tensor] = None, page_size: int = 0,
-                 max_len: Optional[int] = None) -> LatentCache:
-    """Describe a contiguous ([B, max_len, row]) or paged ([pages, page_size, row]) cache."""
+                 max_len: Optional[int] = None,
+                 scales: Optional[torch.Tensor] = None) -> LatentCache:
+    """Describe a contiguous ([B, max_len, row]) or paged ([pages, page_size, row])
+    cache; with `scales` (one fp32 per row) `data` is a low-bit cache of uint8
+    E4M3 codes (see quantize_rows)."""
+    if scales is not None:
+        if data.dtype != torch.uint8 or scales.dtype != torch.float32:
+            raise TypeError("a low-bit cache is uint8 codes with float32 scales")
+        if tuple(scales.shape) != tuple(data.shape[:2]):
+            raise ValueError(f"scales: expected shape {tuple(data.shape[:2])}, got "
+                             f"{tuple(scales.shape)}")
     if page_table is None:
-        return LatentCache(data, seq_lens, int(d_rope), None, 0, int(data.shape[1]))
+        return LatentCache(data, seq_lens, int(d_rope), None, 0, int(data.shape[1]), scales)
     ml = int(max_len) if max_len is not None else int(page_table.shape[1]) * page_size
-    return LatentCache(data, seq_lens, int(d_rope), page_table, page_size, ml)
+    return LatentCache(data, seq_lens, int(d_rope), page_table, page_size, ml, scales)
+
+
+def quantize_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  scales: Optional[torch.Tensor] = None, stream=None):
+    """Low-bit cache rows: x [..., width] (fp32 or bf16) -> (uint8 E4M3 codes
+    [..., width], fp32 scales [...]) with scale = max|row| / 448 and codes
+    E4M3(x / scale) (mla_quantize_rows)."""
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    width = int(x.shape[-1])
+    n_rows = x.numel() // width if width > 0 else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _require(out, "out", tuple(x.shape), torch.uint8, x.device)
+    _require(scales, "scales", tuple(x.shape[:-1]), torch.float32, x.device)
+    _check("mla_quantize_rows", lib().mla_quantize_rows(n_rows, width, _dtype_code(x),
+                                                        _ptr(x), _ptr(out), _ptr(scales),
+                                                        _stream(stream)))
+    return out, scales
 
 
 def cache_append(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,

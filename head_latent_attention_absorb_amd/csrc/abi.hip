@@ -53,13 +53,15 @@ mla_status_t check_dims(const mla_dims_t* d) {
 }
 
 bool use_mfma(const mla_dims_t* d, const mla_cache_t* c) {
-  return d->dtype == MLA_BF16 && d->d_latent == 512 && d->d_rope == 64 &&
+  return d->dtype == MLA_BF16 && c->row_format == MLA_ROWS_NATIVE && d->d_latent == 512 &&
+         d->d_rope == 64 &&
          d->n_heads % mla::kMfmaHeadsPerGroup == 0 &&
          (c->page_table == nullptr || (c->page_size % 8 == 0 && c->page_size >= 8));
 }
 
 mla_status_t check_cache(const mla_cache_t* c) {
   if (c == nullptr) return MLA_ERR_NULL;
+  if (c->row_format != MLA_ROWS_NATIVE && c->row_format != MLA_ROWS_FP8) return MLA_ERR_DTYPE;
   if (c->max_len < 0) return MLA_ERR_DIMS;
   if (c->page_table != nullptr) {
     if (c->page_size < 1 || c->max_len % c->page_size != 0 || c->num_pages < 1)
@@ -146,7 +148,23 @@ const char* mla_status_str(mla_status_t s) {
   return "MLA_ERR_UNKNOWN";
 }
 
-int32_t mla_abi_version(void) { return 2; }
+int32_t mla_abi_version(void) { return 3; }
+
+mla_status_t mla_quantize_rows(int64_t n_rows, int32_t width, int32_t src_dtype, const void* src,
+                               void* dst, float* scales, void* stream) {
+  if (src_dtype != MLA_F32 && src_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (n_rows < 0 || width < 1 || width > 4096) return MLA_ERR_DIMS;
+  if (n_rows == 0) return MLA_OK;
+  if (src == nullptr || dst == nullptr || scales == nullptr) return MLA_ERR_NULL;
+  if (!aligned16(src)) return MLA_ERR_ALIGN;
+  DeviceInfo dev;
+  mla_status_t st = current_device(&dev);
+  if (st != MLA_OK) return st;
+  (void)hipGetLastError();
+  const hipError_t e = mla::launch_quantize_rows(src_dtype, n_rows, width, src, dst, scales,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
 
 mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch, const void* q_c,
                           const void* q_r, const void* w_uk, void* q_cat, void* stream) {
@@ -214,6 +232,8 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
   if (batch == 0) return MLA_OK;  // nothing to do; callers return before launching
   if (cache->seq_lens == nullptr) return MLA_ERR_NULL;
   if ((parts & kPartials) && (q_cat == nullptr || cache->data == nullptr)) return MLA_ERR_NULL;
+  if ((parts & kPartials) && cache->row_format == MLA_ROWS_FP8 && cache->scales == nullptr)
+    return MLA_ERR_NULL;
   if ((parts & kCombine) && out_lat == nullptr) return MLA_ERR_NULL;
   if (((parts & kPartials) && (!aligned16(q_cat) || !aligned16(cache->data))) ||
       ((parts & kCombine) && (!aligned16(out_lat) ||
@@ -249,6 +269,8 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
   a->dtype = dims->dtype;
   a->q_cat = q_cat;
   a->cache.data = static_cast<const uint8_t*>(cache->data);
+  a->cache.scales = cache->scales;
+  a->cache.fp8 = cache->row_format == MLA_ROWS_FP8 ? 1 : 0;
   a->cache.seq_lens = cache->seq_lens;
   a->cache.page_table = cache->page_table;
   a->cache.page_size = cache->page_table ? cache->page_size : 0;
@@ -424,6 +446,8 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t batch, int32_t d_m
   mla_status_t st = check_append(dims, batch, d_model, rms_eps, rope);
   if (st != MLA_OK) return st;
   if ((st = check_cache(cache)) != MLA_OK) return st;
+  // The append writes rows of dims->dtype only.
+  if (cache->row_format != MLA_ROWS_NATIVE) return MLA_ERR_DTYPE;
   if (batch == 0) return MLA_OK;
   if (h == nullptr || w_dkv == nullptr || (dims->d_rope > 0 && w_kr == nullptr) ||
       rms_weight == nullptr || positions == nullptr || cache->data == nullptr)
@@ -439,6 +463,8 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t batch, int32_t d_m
   if ((st = current_device(&dev)) != MLA_OK) return st;
   mla::CacheView view;
   view.data = static_cast<const uint8_t*>(cache->data);
+  view.scales = nullptr;
+  view.fp8 = 0;
   view.seq_lens = cache->seq_lens;
   view.page_table = cache->page_table;
   view.page_size = cache->page_table ? cache->page_size : 0;

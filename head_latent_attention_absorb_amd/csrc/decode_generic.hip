@@ -80,22 +80,33 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
   float o[kMaxLatentPerThread];
 #pragma unroll
   for (int r = 0; r < kMaxLatentPerThread; ++r) o[r] = 0.f;
-  const int row_bytes = row * static_cast<int>(sizeof(T));
+  // Low-bit rows: one E4M3 byte per element times the row's scale; the scale
+  // multiplies the dot product, and the probability in the weighted sum.
+  const bool fp8 = cache.fp8 != 0;
+  const int row_bytes = row * (fp8 ? 1 : static_cast<int>(sizeof(T)));
 
   for (int tile = t0; tile < t1; tile += kThreads) {
     const int j = tile + threadIdx.x;
-    float sj = -INFINITY;
+    float sj = -INFINITY, row_scale = 1.f;
     if (j < t1) {
-      const T* rp = reinterpret_cast<const T*>(cache_row(cache, b, j, row_bytes));
       float dot = 0.f;
-      for (int k = 0; k < row; ++k) dot = fmaf(q_s[k], ld(rp + k), dot);
+      if (fp8) {
+        const size_t idx = cache_row_index(cache, b, j);
+        const uint8_t* rp = cache.data + idx * row_bytes;
+        for (int k = 0; k < row; ++k) dot = fmaf(q_s[k], ld_e4m3(rp + k), dot);
+        row_scale = cache.scales[idx];
+        dot *= row_scale;
+      } else {
+        const T* rp = reinterpret_cast<const T*>(cache_row(cache, b, j, row_bytes));
+        for (int k = 0; k < row; ++k) dot = fmaf(q_s[k], ld(rp + k), dot);
+      }
       sj = dot * scale;
     }
     const float tmax = block_max(sj, red);
     const float m_new = fmaxf(m, tmax);
     const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
     const float pj = (j < t1) ? expf(sj - m_new) : 0.f;
-    p_s[threadIdx.x] = pj;
+    p_s[threadIdx.x] = pj * row_scale;
     const float psum = block_sum(pj, red);  // its barriers also publish p_s
     l = l * alpha + psum;
     m = m_new;
@@ -105,9 +116,14 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
       const int c = threadIdx.x + r * kThreads;
       if (c < d_latent) {
         float acc = o[r] * alpha;
-        for (int jj = 0; jj < nt; ++jj) {
-          const T* rp = reinterpret_cast<const T*>(cache_row(cache, b, tile + jj, row_bytes));
-          acc = fmaf(p_s[jj], ld(rp + c), acc);
+        if (fp8) {
+          for (int jj = 0; jj < nt; ++jj)
+            acc = fmaf(p_s[jj], ld_e4m3(cache_row(cache, b, tile + jj, row_bytes) + c), acc);
+        } else {
+          for (int jj = 0; jj < nt; ++jj) {
+            const T* rp = reinterpret_cast<const T*>(cache_row(cache, b, tile + jj, row_bytes));
+            acc = fmaf(p_s[jj], ld(rp + c), acc);
+          }
         }
         o[r] = acc;
       }

@@ -26,17 +26,22 @@ __device__ __forceinline__ float ld(const __bf16* p) { return static_cast<float>
 __device__ __forceinline__ void st(float* p, float v) { *p = v; }
 __device__ __forceinline__ void st(__bf16* p, float v) { *p = static_cast<__bf16>(v); }
 
+// Physical row index of logical token t of request b.
+__device__ __forceinline__ size_t cache_row_index(const CacheView& c, int b, int t) {
+  if (c.page_table == nullptr) return static_cast<size_t>(b) * c.max_len + t;
+  const int page = c.page_table[static_cast<size_t>(b) * c.max_pages + t / c.page_size];
+  return static_cast<size_t>(page) * c.page_size + (t % c.page_size);
+}
+
 // Byte address of logical token t of request b.
 __device__ __forceinline__ const uint8_t* cache_row(const CacheView& c, int b, int t,
                                                     int row_bytes) {
-  size_t phys;
-  if (c.page_table == nullptr) {
-    phys = static_cast<size_t>(b) * c.max_len + t;
-  } else {
-    const int page = c.page_table[static_cast<size_t>(b) * c.max_pages + t / c.page_size];
-    phys = static_cast<size_t>(page) * c.page_size + (t % c.page_size);
-  }
-  return c.data + phys * row_bytes;
+  return c.data + cache_row_index(c, b, t) * row_bytes;
+}
+
+// Value of an OCP E4M3 byte (the low-bit cache), without its row scale.
+__device__ __forceinline__ float ld_e4m3(const uint8_t* p) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(*p), 0);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

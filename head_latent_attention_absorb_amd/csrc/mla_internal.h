@@ -18,6 +18,8 @@ namespace mla {
 
 struct CacheView {
   const uint8_t* data;      // cache rows, (d_latent + d_rope) elements each
+  const float* scales;      // FP8 rows: one fp32 scale per row, else nullptr
+  int32_t fp8;              // 1: rows of OCP E4M3 bytes scaled by `scales`
   const int32_t* seq_lens;  // [batch]
   const int32_t* page_table;  // [batch, max_pages] or nullptr
   int32_t page_size;        // 0 => contiguous
@@ -80,6 +82,11 @@ hipError_t launch_cache_append(int dtype, int batch, int d_model, int d_c, int d
                                double yarn_alpha, double yarn_beta, double yarn_len,
                                const int32_t* positions, const CacheView& cache,
                                void* cache_data, void* workspace, hipStream_t stream);
+
+// Low-bit cache rows: E4M3 codes and one fp32 scale per row (src fp32 or
+// bf16 per src_dtype).
+hipError_t launch_quantize_rows(int src_dtype, int64_t n_rows, int width, const void* src,
+                                void* dst, float* scales, hipStream_t stream);
 
 // Constants of the MFMA decode kernel that the planner needs.
 constexpr int kMfmaHeadsPerGroup = 128;  // heads handled by one workgroup

@@ -61,6 +61,16 @@ typedef enum {
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
 
+/* How the cache stores its rows (mla_cache_t.row_format).  MLA_ROWS_NATIVE:
+ * elements of dims->dtype.  MLA_ROWS_FP8: the low-bit cache of deployment
+ * (ai-library "DeepSeek-V2" notes, "Training and Inference Efficiency" /
+ * "Inference cost": the KV cache quantised to about 6 bits per element; V3
+ * read-through section 4.4: scales computed online from the data): each row
+ * is d_latent + d_rope OCP E4M3 bytes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, largest finite value 448) with one fp32 scale per row, the
+ * element value being code * scale (see mla_quantize_rows). */
+typedef enum { MLA_ROWS_NATIVE = 0, MLA_ROWS_FP8 = 1 } mla_row_format_t;
+
 /* Model dimensions of one MLA layer (DeepSeek-V2: 128, 128, 64, 512; zeeklog
  * notes, the remark under the cache table: d_c = 4 d_h, d_h^R = d_h / 2). */
 typedef struct {
@@ -86,6 +96,10 @@ typedef struct {
                                 stride between requests of a contiguous cache;
                                 a multiple of page_size when paged            */
   int64_t num_pages;         /* paged: pages in the pool; ignored otherwise    */
+  const float* scales;       /* MLA_ROWS_FP8: device, one fp32 per row, indexed
+                                like the rows of data ([batch, max_len] or
+                                [num_pages, page_size]); NULL otherwise       */
+  int32_t row_format;        /* mla_row_format_t                               */
 } mla_cache_t;
 
 /* Split-KV plan: each request's tokens are cut into partitions of
@@ -106,7 +120,8 @@ typedef struct {
 const char* mla_status_str(mla_status_t status);
 
 /* Library ABI version (incremented on any signature change; 2 added
- * mla_decode_plan_t.q_len and mla_decode_plan_mq). */
+ * mla_decode_plan_t.q_len and mla_decode_plan_mq; 3 added mla_cache_t.scales,
+ * mla_cache_t.row_format and mla_quantize_rows). */
 int32_t mla_abi_version(void);
 
 /* Absorb W^UK into the query (V2 read-through section 2.3; V3 read-through
@@ -238,6 +253,19 @@ typedef struct {
   float yarn_beta;            /* ramp end, > yarn_alpha (when yarn_scale != 1)  */
   int32_t yarn_original_len;  /* L > 0 (when yarn_scale != 1)                  */
 } mla_rope_t;
+
+/* Quantise rows to the low-bit cache format (MLA_ROWS_FP8): for each of the
+ * n_rows rows of `width` elements,
+ *   scale[r] = max_j |x[r, j]| / 448   (1 for an all-zero row; fp32 division)
+ *   dst[r, j] = E4M3(x[r, j] / scale[r])   (fp32 division, round to nearest
+ *               with ties to even, |.| <= 448 by construction, sign kept)
+ * src [n_rows, width] device, src_dtype (MLA_F32 or MLA_BF16); dst
+ * [n_rows, width] device bytes; scales [n_rows] device fp32.  A contiguous or
+ * paged cache is quantised as its flat array of rows.  n_rows < 0 or width
+ * outside 1..4096 -> MLA_ERR_DIMS; NULL pointer -> MLA_ERR_NULL; src not
+ * 16-byte aligned -> MLA_ERR_ALIGN.  Asynchronous on `stream`. */
+mla_status_t mla_quantize_rows(int64_t n_rows, int32_t width, int32_t src_dtype, const void* src,
+                               void* dst, float* scales, void* stream);
 
 /* Device bytes of workspace mla_cache_append needs for these sizes. */
 size_t mla_cache_append_workspace_bytes(const mla_dims_t* dims, int32_t batch, int32_t d_model);

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_absorb_q", "mla_decode_attn", "mla_out_uv", "mla_decode_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
-    assert L.mla_abi_version() == 2
+    assert L.mla_abi_version() == 3
 
 
 def test_status_strings():
@@ -45,7 +45,7 @@ def test_status_strings():
 def test_struct_sizes_match_header():
     # mla_dims_t: 5 x int32; mla_cache_t: 3 pointers, 2 int32, int64; plan: 4 int32 + size_t.
     assert ctypes.sizeof(mla.Dims) == 20
-    assert ctypes.sizeof(mla.CacheDesc) == 40
+    assert ctypes.sizeof(mla.CacheDesc) == 56
     assert ctypes.sizeof(mla.Plan) == 32
     # mla_rope_t: 4 floats and an int32.
     assert ctypes.sizeof(mla.Rope) == 20
