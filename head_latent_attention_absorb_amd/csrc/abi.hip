@@ -53,10 +53,13 @@ mla_status_t check_dims(const mla_dims_t* d) {
 }
 
 bool use_mfma(const mla_dims_t* d, const mla_cache_t* c) {
-  return d->dtype == MLA_BF16 && c->row_format == MLA_ROWS_NATIVE && d->d_latent == 512 &&
-         d->d_rope == 64 &&
+  // Low-bit rows are loaded a whole 32-token tile at a time, which must lie
+  // within one page.
+  const int page_align = c->row_format == MLA_ROWS_FP8 ? 32 : 8;
+  return d->dtype == MLA_BF16 && d->d_latent == 512 && d->d_rope == 64 &&
          d->n_heads % mla::kMfmaHeadsPerGroup == 0 &&
-         (c->page_table == nullptr || (c->page_size % 8 == 0 && c->page_size >= 8));
+         (c->page_table == nullptr ||
+          (c->page_size % page_align == 0 && c->page_size >= page_align));
 }
 
 mla_status_t check_cache(const mla_cache_t* c) {

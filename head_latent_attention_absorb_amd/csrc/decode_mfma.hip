@@ -64,6 +64,24 @@ constexpr int kLdsBytes = kStages * kTileBytes;
 constexpr float kRescaleThreshold = 8.f;             // log2 units
 
 static_assert(kTileBytes == 4 * kGroups * 1024, "each wave issues kGroups loads per tile");
+
+// Low-bit cache rows (one OCP E4M3 byte per element and one fp32 scale per
+// row).  A 32-token tile of codes is copied, as the 32 rows back to back,
+// into the upper half of its ring stage, and its 32 scales into a small ring
+// of their own; at the start of the step that first reads the tile, the
+// workgroup converts the codes into the bf16 layout above (code * scale in
+// fp32, rounded to bf16), so the products and the softmax are those of a
+// bf16 cache.
+// Copying 18,432 bytes takes 18 sixteen-byte load instructions; with the
+// scale load twice, every wave issues five loads per tile.
+constexpr int kFp8RowBytes = kRow;
+constexpr int kFp8TileBytes = kTile * kFp8RowBytes;            // 18432
+constexpr int kFp8PieceLoads = kFp8TileBytes / 1024;          // 18
+constexpr int kFp8Loads = 5;                                   // per wave per tile
+constexpr int kFp8RawOffset = kTileBytes - kFp8TileBytes;      // codes: upper half
+constexpr int kFp8ScaleBytes = 64 * 4;                        // one scale load, per stage
+static_assert(kFp8PieceLoads + 2 == 4 * kFp8Loads, "two scale loads complete the count");
+static_assert(kFp8RowBytes % 16 == 0 && (kFp8RowBytes / 8) % 9 == 0, "");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert((kStages & (kStages - 1)) == 0, "stage index uses a mask");
 static_assert(kMfmaHeadsPerGroup == 4 * 32 && kMfmaTokenGranule == kTile, "");
@@ -102,6 +120,23 @@ __device__ __forceinline__ void load_to_lds16(const void* src, unsigned lds_base
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
                :
                : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base) - kOffset), "i"(kOffset)
+               : "memory", "m0");
+}
+
+// The same 16-byte and 4-byte loads from a wave-uniform base address (in
+// SGPRs) plus a 32-bit per-lane byte offset: one VGPR per address.
+__device__ __forceinline__ void load_to_lds16_sbase(unsigned voff, const void* sbase,
+                                                    unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void load_to_lds4_sbase(unsigned voff, const void* sbase,
+                                                   unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 
@@ -197,9 +232,14 @@ __device__ __forceinline__ int swz(int n, int chunk) {
   return (((chunk >> 3) * kTile + n) << 7) + (((chunk & 7) ^ swz_key(n)) << 4);
 }
 
-template <bool kPaged>
+template <bool kPaged, bool kFp8>
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  // Low-bit rows: the scales of the tile in each ring stage.
+  __shared__ __attribute__((aligned(16))) uint8_t sc_lds[kFp8 ? kStages * kFp8ScaleBytes : 16];
+  // Loads per wave per tile, and cache bytes per row.
+  constexpr int kLoads = kFp8 ? kFp8Loads : kGroups;
+  constexpr int kSrcRowBytes = kFp8 ? kFp8RowBytes : kRowBytes;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
@@ -241,7 +281,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   const int chunk_off = ((lane & 7) ^ swz_key(n_load)) * 16;
   const uint8_t* req_base =
       kPaged ? p.cache.data
-             : p.cache.data + static_cast<size_t>(b) * p.cache.max_len * kRowBytes;
+             : p.cache.data + static_cast<size_t>(b) * p.cache.max_len * kSrcRowBytes;
   // Paged cache: lane j holds the physical id of the partition's j-th page
   // (at most 64 pages, which the planner guarantees), fetched once here.  A
   // wave's 8 tokens of a tile are 8-aligned, so with page_size % 8 == 0 they
@@ -273,8 +313,124 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     return src + chunk_off;
   };
   auto tile_dst = [&](int stage) { return lds_address(lds + stage * kTileBytes) + wave * 1024; };
+
+  // Low-bit rows: load j of this wave for the tile at tile_t0 is instruction
+  // i = wave + 4j; instructions 0..17 copy 16-byte pieces (lane l of
+  // instruction i: piece i*64 + l, i.e. token piece / 36, byte (piece % 36) * 16
+  // of its row), 18 and 19 the scales (lane l: token min(l, 31)).  A tile
+  // lies within one page (page_size % 32 == 0).
+  // Low-bit rows, loads of the tile at tile_t0 into `stage`: instruction
+  // i < 18 copies 16-byte pieces (lane l: piece i*64 + l, i.e. token
+  // piece / 36, byte (piece % 36) * 16 of its row; the rows of a tile are
+  // contiguous), instructions 18 and 19 the 32 scales (lane l: token
+  // min(l, 31)).  Wave w issues pieces w, w+4, w+8, w+12 between its products
+  // (fp8_piece, branch-free) and, from fp8_extra, piece 16 + w (w < 2) or the
+  // scales (w >= 2): five loads per wave per tile.  Tiles past the partition
+  // re-read its last row, so addresses start at tile_a = min(tile_t0, t1 - 1)
+  // and tokens past lim (the last valid one, >= 0) re-read row lim.  A tile
+  // lies within one page (page_size % 32 == 0).
+  struct Fp8Tile {
+    const uint8_t* codes;   // row of token tile_a
+    const float* scales;    // its scale
+    int lim;
+    unsigned lds;           // the stage
+    unsigned lds_scales;    // its scales
+  };
+  auto fp8_tile = [&](int tile_t0, int stage) {
+    Fp8Tile f;
+    const int tile_a = min(tile_t0, t1 - 1);
+    f.lim = min(t1 - 1 - tile_a, kTile - 1);
+    size_t row0;
+    if constexpr (kPaged) {
+      const int page =
+          __builtin_amdgcn_readlane(page_of_lane, tile_a / p.cache.page_size - first_page);
+      row0 = static_cast<size_t>(page) * p.cache.page_size + tile_a % p.cache.page_size;
+    } else {
+      row0 = static_cast<size_t>(b) * p.cache.max_len + tile_a;
+    }
+    f.codes = p.cache.data + row0 * kFp8RowBytes;
+    f.scales = p.cache.scales + row0;
+    f.lds = lds_address(lds + stage * kTileBytes);
+    f.lds_scales = lds_address(sc_lds + stage * kFp8ScaleBytes);
+    return f;
+  };
+  auto fp8_piece_at = [&](const Fp8Tile& f, int i) {
+    const int piece = i * 64 + lane;
+    const int tok = piece / 36;
+    const unsigned off = min(tok, f.lim) * kFp8RowBytes + (piece - tok * 36) * 16;
+    load_to_lds16_sbase(off, f.codes, f.lds + kFp8RawOffset + i * 1024);
+  };
+  auto fp8_piece = [&](const Fp8Tile& f, int j) { fp8_piece_at(f, wave_u + 4 * j); };
+  auto fp8_extra = [&](const Fp8Tile& f) {
+    if (wave_u < 2)
+      fp8_piece_at(f, 16 + wave_u);
+    else
+      load_to_lds4_sbase(min(lane, f.lim) * 4, f.scales, f.lds_scales);
+  };
+  static_assert(4 * 4 + 2 == kFp8PieceLoads && kFp8Loads == 5, "four pieces and one extra");
+  // This wave's load J (< kGroups) of a bf16 tile: column group J of its
+  // token octet (src = tile_src(tile_t0), dst = tile_dst(stage)).
+  auto issue_load = [&](auto J, const uint8_t* src, unsigned dst) {
+    load_to_lds16<decltype(J)::value * 128>(src, dst + decltype(J)::value * 4096);
+  };
   auto issue_tile = [&](int stage, int tile_t0) {
-    load_row_groups(tile_src(tile_t0), tile_dst(stage), std::make_integer_sequence<int, kGroups>{});
+    if constexpr (kFp8) {
+      const Fp8Tile f = fp8_tile(tile_t0, stage);
+      fp8_extra(f);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fp8_piece(f, j);
+    } else {
+      load_row_groups(tile_src(tile_t0), tile_dst(stage),
+                      std::make_integer_sequence<int, kGroups>{});
+    }
+  };
+  // Low-bit rows: turn the codes of the tile in `stage` into the bf16 layout
+  // of that stage (code * scale rounded to bf16).  Lane (token
+  // n = w*8 + lane/8, part = lane%8) converts bf16 chunk part + 8k of its
+  // token for k = 0..8, i.e. the part-th chunk of every column group k (8
+  // code bytes each).  Groups 0-3 lie below the codes, so they are written at
+  // once; groups 4-8 overwrite codes and are written after a barrier that
+  // follows every lane's reads.  A second barrier publishes the tile.
+  auto fp8_convert = [&](int stage) {
+    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+    static_assert(4 * 4096 <= kFp8RawOffset, "groups 0-3 lie below the codes");
+    uint8_t* st = lds + stage * kTileBytes;
+    const int part = lane & 7;
+    const MLA_LDS uint8_t* raw =
+        (MLA_LDS const uint8_t*)(st + kFp8RawOffset + n_load * kFp8RowBytes + part * 8);
+    const float sc = *(MLA_LDS const float*)(uintptr_t)(lds_address(sc_lds) +
+                                                       stage * kFp8ScaleBytes + n_load * 4);
+    u32x2_t w[kGroups];
+#pragma unroll
+    for (int k = 0; k < kGroups; ++k) w[k] = *(MLA_LDS const u32x2_t*)(raw + k * 64);
+    // code * scale in fp32, rounded to bf16.
+    auto put = [&](int k) {
+      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      const f32x2_t x0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[k][0]), false);
+      const f32x2_t x1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[k][0]), true);
+      const f32x2_t x2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[k][1]), false);
+      const f32x2_t x3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[k][1]), true);
+      bf16x8_t v;
+      v[0] = static_cast<__bf16>(x0[0] * sc);
+      v[1] = static_cast<__bf16>(x0[1] * sc);
+      v[2] = static_cast<__bf16>(x1[0] * sc);
+      v[3] = static_cast<__bf16>(x1[1] * sc);
+      v[4] = static_cast<__bf16>(x2[0] * sc);
+      v[5] = static_cast<__bf16>(x2[1] * sc);
+      v[6] = static_cast<__bf16>(x3[0] * sc);
+      v[7] = static_cast<__bf16>(x3[1] * sc);
+      *(MLA_LDS bf16x8_t*)(st + swz(n_load, part + 8 * k)) = v;
+    };
+#pragma unroll
+    for (int k = 0; k < 4; ++k) put(k);
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 4; k < kGroups; ++k) put(k);
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   // Per-lane LDS offsets within a tile.  Score operand of K-step ks:
@@ -350,10 +506,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       // round's, so the second wait need not cover tile 1: when every
       // workgroup starts at once, the query and tile 0 arrive sooner with
       // tile 1 not yet competing for the memory system.  Loads complete in
-      // issue order, so vmcnt(kGroups) means: everything but the tile just
+      // issue order, so vmcnt(kLoads) means: everything but the tile just
       // issued has landed.
       issue_tile(round, t0 + round * kTile);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroups));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       if ((wave & 2) == hb0) {
@@ -398,22 +554,32 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // below.  Every step issues exactly one tile (past the last tile they
   // re-read the partition's last row into a stage that is never read
   // again), so at step t "this wave's loads of tile t+1 have landed" while
-  // those of tile t+2 may stay in flight is always vmcnt(kGroups).
+  // those of tile t+2 may stay in flight is always vmcnt(kLoads).
   //
-  // Scores of tile 0, with the loads of tile 2 one column group behind each
-  // of the first 9 score products.
+  // Scores of tile 0, with the loads of tile 2 one behind each of the first
+  // kLoads score products (low-bit rows: tile 0 is converted first).
+  if constexpr (kFp8) fp8_convert(0);
   {
     int qoff[4];
     k_offsets(0, qoff);
     bf16x8_t ta[kKSteps];
 #pragma unroll
     for (int ks = 0; ks < kKWindow; ++ks) ta[ks] = read_k(qoff, ks);
-    const uint8_t* src2 = tile_src(t0 + 2 * kTile);
+    const uint8_t* src2 = kFp8 ? nullptr : tile_src(t0 + 2 * kTile);
     const unsigned dst2 = tile_dst(2);
+    Fp8Tile f2{};
+    if constexpr (kFp8) {
+      f2 = fp8_tile(t0 + 2 * kTile, 2);
+      fp8_extra(f2);
+    }
     static_for<kKSteps>([&](auto K) {
       constexpr int ks = decltype(K)::value;
       qk(ta, qoff, ks);
-      if constexpr (ks < kGroups) load_to_lds16<ks * 128>(src2, dst2 + ks * 4096);
+      if constexpr (kFp8) {
+        if constexpr (ks < 4) fp8_piece(f2, ks);
+      } else if constexpr (ks < kGroups) {
+        issue_load(K, src2, dst2);
+      }
     });
     drain_v(sc);
   }
@@ -434,22 +600,33 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     float sv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = s_next[v];
+
     // Wait for this wave's loads of tile t+1 (tile t+2 may stay in flight),
     // then for everyone's.  A raw s_barrier, not __syncthreads(): the latter
     // also waits for every outstanding global load and would drain the
     // prefetch.  The compiler fence keeps LDS accesses on their side of the
     // barrier.  After it every wave is past step t-1, so the stage of tile
     // t-1, (t+3) % 4, is refilled with tile t+3.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroups));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // Low-bit rows: tile t+1, read by this step's score products, is
+    // converted now (tile t was converted one step earlier).
+    if constexpr (kFp8 && kNext) fp8_convert((t + 1) & (kStages - 1));
 
     const int nvalid = t1 - (t0 + t * kTile);
     int qoff[4], voff[4];
     k_offsets((t + 1) & (kStages - 1), qoff);
     v_offsets(t & (kStages - 1), voff);
-    const uint8_t* next_src = tile_src(t0 + (t + 3) * kTile);
-    const unsigned next_dst = tile_dst((t + 3) & (kStages - 1));
+    const int next_t0 = t0 + (t + 3) * kTile;
+    const int next_stage = (t + 3) & (kStages - 1);
+    const uint8_t* next_src = kFp8 ? nullptr : tile_src(next_t0);
+    const unsigned next_dst = tile_dst(next_stage);
+    Fp8Tile fn{};
+    if constexpr (kFp8) {
+      fn = fp8_tile(next_t0, next_stage);
+      fp8_extra(fn);
+    }
 
     bf16x8_t ta[kKSteps];
     if constexpr (kNext) {
@@ -571,8 +748,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       if constexpr (i + kVWindow < kPv) va[i + kVWindow] = read_v(voff, i + kVWindow);
       mfma_a(acc[i & 15], va[i], pb[i >> 4]);
       if constexpr (kNext && kSoftSlots + i < kKSteps) qk(ta, qoff, kSoftSlots + i);
-      if constexpr (i % 2 == 0 && i / 2 < kGroups)
-        load_to_lds16<(i / 2) * 128>(next_src, next_dst + (i / 2) * 4096);
+      if constexpr (kFp8) {
+        if constexpr (i % 2 == 0 && i / 2 < 4) fp8_piece(fn, i / 2);
+      } else if constexpr (i % 2 == 0 && i / 2 < kGroups) {
+        issue_load(std::integral_constant<int, i / 2>{}, next_src, next_dst);
+      }
     });
     static_assert(kKSteps - kSoftSlots <= kPv, "every score MFMA is paired");
     // The scores of tile t+1 leave the accumulator behind the last PV
@@ -649,10 +829,17 @@ hipError_t launch_partials_mfma(const DecodeArgs& a) {
   p.part_o = static_cast<uint16_t*>(a.part_o);
   p.part_ml = reinterpret_cast<float2*>(a.part_lse);
   const int grid = (p.work_items + 7) / 8 * 8;  // multiple of the 8 XCDs
-  if (a.cache.page_table != nullptr)
-    decode_mfma_kernel<true><<<grid, 256, 0, a.stream>>>(p);
-  else
-    decode_mfma_kernel<false><<<grid, 256, 0, a.stream>>>(p);
+  if (a.cache.page_table != nullptr) {
+    if (a.cache.fp8)
+      decode_mfma_kernel<true, true><<<grid, 256, 0, a.stream>>>(p);
+    else
+      decode_mfma_kernel<true, false><<<grid, 256, 0, a.stream>>>(p);
+  } else {
+    if (a.cache.fp8)
+      decode_mfma_kernel<false, true><<<grid, 256, 0, a.stream>>>(p);
+    else
+      decode_mfma_kernel<false, false><<<grid, 256, 0, a.stream>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -112,6 +112,7 @@ def test_bf16_query_over_fp8_cache(paged, split):
     q = draw_latent_query(cfg, 82)
     plan = mla.decode_plan(cfg.n_heads, cfg.d_latent, cfg.d_rope, torch.bfloat16, dc,
                            split_tokens=split)
+    assert plan.kernel == 1  # the MFMA kernel, converting the codes in LDS
     o_lat, lse = mla.decode_attn(_bf16(q), dc, cfg.scale, plan=plan)
     torch.cuda.synchronize()
     heads = np.arange(0, 128, 7)
