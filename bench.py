@@ -40,7 +40,7 @@ from workload import CONFIGS, f32_to_bf16_bits, make_append_case, make_case  # n
 METRIC = "MLA decode tokens/s and latent-cache HBM GB/s (% roofline), B=16 T=4096"
 WORKLOAD = "dsv2_b16_t4096"
 WORKLOADS = ("dsv2_b16_t4096", "ragged_b4_16k_32k", "paged_b128_t2048", "ctx128k_b2_60l",
-             "mtp2_b16_t4096")
+             "mtp2_b16_t4096", "fp8_b16_t4096")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partials_dsv2_b16_t4096_counters.json")
@@ -67,14 +67,21 @@ class Entry:
         self.w_uk = to_dev(case.w_uk)
         self.w_uv = to_dev(case.w_uv)
         self.cache_t = to_dev(case.cache)
+        self.scales = None
+        if cfg.cache_format == "fp8":
+            # The low-bit cache: the drawn rows quantised on the GPU (E4M3
+            # codes and one fp32 scale per row); the bf16 copy is dropped.
+            self.cache_t, self.scales = mla.quantize_rows(self.cache_t)
         self.lens = torch.from_numpy(case.seq_lens.astype(np.int32)).cuda()
         self.page_table = (torch.from_numpy(case.page_table).cuda()
                            if case.page_table is not None else None)
         self.cache = mla.latent_cache(self.cache_t, self.lens, cfg.d_rope, self.page_table,
-                                      cfg.page_size, cfg.max_len if cfg.paged else None)
+                                      cfg.page_size, cfg.max_len if cfg.paged else None,
+                                      scales=self.scales)
         self.tokens = int(case.seq_lens.sum())
         self.nbytes = sum(t.numel() * t.element_size()
-                          for t in (self.q_c, self.q_r, self.w_uk, self.w_uv, self.cache_t))
+                          for t in (self.q_c, self.q_r, self.w_uk, self.w_uv, self.cache_t,
+                                    self.scales) if t is not None)
         # Inputs of the cache append (the step before the decode path): the new
         # token's hidden state, W^DKV, W^KR and the RMSNorm weight.
         ac = make_append_case(cfg, seed)
@@ -348,7 +355,9 @@ def main():
     tokens = (sum(e.tokens for e in pool) if layered
               else sum(pool[i % n_pool].tokens for i in range(args.steps)) / args.steps)
     tokens_layer = tokens / layers_per_step
-    cache_bytes = tokens * row * 2
+    # Cached bytes per token: bf16 rows, or E4M3 rows plus one fp32 scale.
+    row_bytes = row + 4 if cfg.cache_format == "fp8" else row * 2
+    cache_bytes = tokens * row_bytes
     q_bytes = layers_per_step * B * ql * nh * row * 2
     olat_bytes = layers_per_step * B * ql * nh * (cfg.d_latent * 2 + 4)
     # Query token j of a request sees ql - 1 - j rows fewer than the request
@@ -396,7 +405,8 @@ def main():
             "workload": name, "batch": B, "seq_len": cfg.max_len,
             "seq_len_range": [cfg.len_lo, cfg.len_hi], "n_heads": nh,
             "d_head": cfg.d_head, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope,
-            "cache": f"paged, {cfg.page_size}-token pages" if cfg.paged else "contiguous",
+            "cache": (f"paged, {cfg.page_size}-token pages" if cfg.paged else "contiguous") +
+                     (", E4M3 rows + fp32 row scales" if cfg.cache_format == "fp8" else ""),
             "layers_per_step": layers_per_step,
             "rotating_pool_mb": round(pool_mb), "split_tokens": plan.split_tokens,
             "num_splits": plan.num_splits, "query_tokens_per_request": ql,

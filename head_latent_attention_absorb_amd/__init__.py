@@ -422,8 +422,10 @@ def cache_append(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr:
     _require(rms_weight, "rms_weight", (d_c,), h.dtype, dev)
     _require(positions, "positions", (B,), torch.int32, dev)
     _require(h, "h", (B, d_model), h.dtype, dev)
-    if cache.data.dtype != h.dtype or cache.data.shape[2] != d_c + d_r:
-        raise ValueError("cache row must be [d_latent + d_rope] of h's dtype")
+    if cache.data.shape[2] != d_c + d_r or (
+            cache.data.dtype != (torch.uint8 if cache.scales is not None else h.dtype)):
+        raise ValueError("cache row must be [d_latent + d_rope] of h's dtype "
+                         "(or of E4M3 codes for a low-bit cache)")
     dims = make_dims(1, 1, d_r, d_c, _dtype_code(h))
     need = int(lib().mla_cache_append_workspace_bytes(ctypes.byref(dims), B, d_model))
     if workspace is None:

@@ -449,11 +449,10 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t batch, int32_t d_m
   mla_status_t st = check_append(dims, batch, d_model, rms_eps, rope);
   if (st != MLA_OK) return st;
   if ((st = check_cache(cache)) != MLA_OK) return st;
-  // The append writes rows of dims->dtype only.
-  if (cache->row_format != MLA_ROWS_NATIVE) return MLA_ERR_DTYPE;
   if (batch == 0) return MLA_OK;
   if (h == nullptr || w_dkv == nullptr || (dims->d_rope > 0 && w_kr == nullptr) ||
-      rms_weight == nullptr || positions == nullptr || cache->data == nullptr)
+      rms_weight == nullptr || positions == nullptr || cache->data == nullptr ||
+      (cache->row_format == MLA_ROWS_FP8 && cache->scales == nullptr))
     return MLA_ERR_NULL;
   if (!aligned16(h) || !aligned16(w_dkv) || (dims->d_rope > 0 && !aligned16(w_kr)) ||
       !aligned16(cache->data))
@@ -466,8 +465,8 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t batch, int32_t d_m
   if ((st = current_device(&dev)) != MLA_OK) return st;
   mla::CacheView view;
   view.data = static_cast<const uint8_t*>(cache->data);
-  view.scales = nullptr;
-  view.fp8 = 0;
+  view.scales = cache->scales;
+  view.fp8 = cache->row_format == MLA_ROWS_FP8 ? 1 : 0;
   view.seq_lens = cache->seq_lens;
   view.page_table = cache->page_table;
   view.page_size = cache->page_table ? cache->page_size : 0;

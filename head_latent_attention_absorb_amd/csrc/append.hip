@@ -174,6 +174,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(AppendParams p) {
   extern __shared__ float y[];  // [d_c + d_r]
   __shared__ float red[kThreads / 64];
+  static_assert(kThreads == 256, "the block reductions below read four waves");
   const int b = blockIdx.x;
   const int n_total = p.d_c + p.d_r;
   // The slices' loads of kCols columns per thread are all issued before they
@@ -217,20 +218,45 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(AppendParams p) {
                                         pos / p.cache.page_size];
     phys = static_cast<size_t>(page) * p.cache.page_size + pos % p.cache.page_size;
   }
-  T* row = static_cast<T*>(p.cache_data) + phys * n_total;
+  // The finished row, in place in y: the normalised latent, then the rotated
+  // key pairs.
   const T* gamma = static_cast<const T*>(p.gamma);
-  for (int n = threadIdx.x; n < p.d_c; n += kThreads) st(row + n, y[n] * inv * ld(gamma + n));
+  for (int n = threadIdx.x; n < p.d_c; n += kThreads) y[n] = y[n] * inv * ld(gamma + n);
   for (int i = threadIdx.x; i < p.d_r / 2; i += kThreads) {
     // The angle is reduced modulo 2 pi in fp64; the reduced angle's sine and
     // cosine are fp32-accurate.
     const double ang = static_cast<double>(pos) * p.freq[i];
-    const float red = static_cast<float>(ang - 2.0 * M_PI * rint(ang / (2.0 * M_PI)));
+    const float ra = static_cast<float>(ang - 2.0 * M_PI * rint(ang / (2.0 * M_PI)));
     float sn, cs;
-    sincosf(red, &sn, &cs);
+    sincosf(ra, &sn, &cs);
     const float x0 = y[p.d_c + 2 * i], x1 = y[p.d_c + 2 * i + 1];
-    st(row + p.d_c + 2 * i, x0 * cs - x1 * sn);
-    st(row + p.d_c + 2 * i + 1, x0 * sn + x1 * cs);
+    y[p.d_c + 2 * i] = x0 * cs - x1 * sn;
+    y[p.d_c + 2 * i + 1] = x0 * sn + x1 * cs;
   }
+  __syncthreads();
+  if (!p.cache.fp8) {
+    T* row = static_cast<T*>(p.cache_data) + phys * n_total;
+    for (int n = threadIdx.x; n < n_total; n += kThreads) st(row + n, y[n]);
+    return;
+  }
+  // Low-bit cache: E4M3 codes with the row's scale max|y| / 448, as
+  // mla_quantize_rows computes them (fp32 divisions, round to nearest even).
+  float amax = 0.f;
+  for (int n = threadIdx.x; n < n_total; n += kThreads) amax = fmaxf(amax, fabsf(y[n]));
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = amax > 0.f ? amax / 448.f : 1.f;
+  uint8_t* codes = static_cast<uint8_t*>(p.cache_data) + phys * n_total;
+  for (int n = 2 * threadIdx.x; n < n_total; n += 2 * kThreads) {
+    const float a = fminf(fmaxf(y[n] / sc, -448.f), 448.f);
+    const float c = n + 1 < n_total ? fminf(fmaxf(y[n + 1] / sc, -448.f), 448.f) : 0.f;
+    const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(a, c, 0, false);
+    codes[n] = static_cast<uint8_t>(packed & 0xFF);
+    if (n + 1 < n_total) codes[n + 1] = static_cast<uint8_t>((packed >> 8) & 0xFF);
+  }
+  if (threadIdx.x == 0) const_cast<float*>(p.cache.scales)[phys] = sc;
 }
 
 // k slices of the MFMA projection: the most of 16, 8, 4, 2, 1 that divides

@@ -283,7 +283,9 @@ size_t mla_cache_append_workspace_bytes(const mla_dims_t* dims, int32_t batch, i
  * The row is written through cache->data (contiguous or paged exactly as
  * mla_decode_attn reads it); positions outside [0, max_len) write nothing.
  * Updating seq_lens is the caller's.  Accumulates in fp32 (angles in fp64),
- * rounds once to dims->dtype.  Uses dims->d_latent, d_rope and dtype;
+ * rounds once to dims->dtype; into a low-bit cache (MLA_ROWS_FP8) the fp32
+ * row is quantised as mla_quantize_rows does and its scale written to
+ * cache->scales.  Uses dims->d_latent, d_rope and dtype;
  * d_rope must be even.  Errors: NULL pointers (with batch > 0) ->
  * MLA_ERR_NULL; d_model < 1, odd d_rope, rms_eps < 0 or not finite, a bad
  * rope description -> MLA_ERR_DIMS; h, the weights or cache->data not

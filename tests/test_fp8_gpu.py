@@ -119,3 +119,43 @@ def test_bf16_query_over_fp8_cache(paged, split):
     o_ref, lse_ref = _reference(case, codes, scales, q, heads)
     assert_close(from_dev(o_lat)[:, heads], o_ref[:, heads], "bf16", "o_lat")
     assert_close(from_dev(lse)[:, heads], lse_ref[:, heads], "bf16", "lse")
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_append_into_fp8_cache(paged):
+    """mla_cache_append into a low-bit cache: the appended rows dequantise to
+    the oracle's rows (oracle.append_rows, fp64) within E4M3's rounding
+    (half a code step: 2^-4 relative, 2^-10 * scale below the normal range,
+    plus the fp32 arithmetic), the scale is the row's max|x| / 448 to fp32
+    rounding, and no other row or scale changes."""
+    from workload import make_append_case
+    if paged:
+        cfg = DSV2.replace(batch=4, max_len=256, len_lo=1, len_hi=256, page_size=64)
+    else:
+        cfg = DSV2.replace(batch=4, max_len=256, len_lo=1, len_hi=256)
+    ac = make_append_case(cfg, 91)
+    base = make_case(cfg, 91, pad_value=0.0)
+    codes0, scales0 = oracle.quantize_rows(base.cache)
+    dc = _device_cache(base, codes0, scales0)
+    mla.cache_append(dc, _bf16(ac.h), _bf16(ac.w_dkv), _bf16(ac.w_kr), _bf16(ac.rms_weight),
+                     torch.from_numpy(ac.positions).cuda(), rms_eps=1e-6, rope_base=10000.0)
+    torch.cuda.synchronize()
+    codes, scales = dc.data.cpu().numpy(), dc.scales.cpu().numpy()
+    rows = oracle.append_rows(ac.h, ac.w_dkv, ac.w_kr, ac.rms_weight, 1e-6, ac.positions,
+                              10000.0)
+    touched = np.zeros(codes.shape[:2], bool)
+    for b, pos in enumerate(ac.positions):
+        if base.page_table is None:
+            idx = (b, int(pos))
+        else:
+            idx = (int(base.page_table[b, pos // cfg.page_size]), int(pos % cfg.page_size))
+        touched[idx] = True
+        ref = rows[b]
+        s_ref = np.float32(np.max(np.abs(ref)) / 448.0)
+        assert abs(scales[idx] - s_ref) <= 1e-5 * s_ref, (b, scales[idx], s_ref)
+        deq = oracle.dequantize_rows(codes[idx][None], scales[idx][None])[0]
+        r = np.abs(ref / scales[idx])
+        bound = (np.where(r >= 2.0 ** -6, r * 2.0 ** -4, 2.0 ** -10) + 1e-3) * scales[idx]
+        assert np.all(np.abs(deq - ref) <= bound), b
+    assert np.array_equal(codes[~touched], codes0[~touched])
+    assert np.array_equal(scales[~touched], scales0[~touched])

@@ -76,6 +76,7 @@ class WorkloadConfig:
     softmax_scale: Optional[float] = None   # None => 1/sqrt(d_head + d_rope)
     d_model: int = 0         # hidden width d of the cache append; 0 => n_heads * d_head
     q_len: int = 1           # query tokens per request (several: speculative verification)
+    cache_format: str = "native"  # "fp8": E4M3 rows with one fp32 scale per row
 
     @property
     def row(self) -> int:
@@ -128,6 +129,11 @@ CONFIGS: Dict[str, WorkloadConfig] = {
     "mtp2_b16_t4096": WorkloadConfig("mtp2_b16_t4096", batch=16, dtype="bf16",
                                      len_lo=4096, len_hi=4096, max_len=4096, q_len=2,
                                      **_DSV2),
+    # The default shape over the low-bit cache: the same drawn rows, quantised
+    # to E4M3 with one scale per row.
+    "fp8_b16_t4096": WorkloadConfig("fp8_b16_t4096", batch=16, dtype="bf16",
+                                    len_lo=4096, len_hi=4096, max_len=4096,
+                                    cache_format="fp8", **_DSV2),
     # 128K-context decode: B=2, T=131072, 60 independently seeded layers.
     "ctx128k_b2_60l": WorkloadConfig("ctx128k_b2_60l", batch=2, dtype="bf16",
                                      len_lo=131072, len_hi=131072, max_len=131072,
