@@ -40,7 +40,7 @@ from workload import CONFIGS, f32_to_bf16_bits, make_append_case, make_case  # n
 METRIC = "MLA decode tokens/s and latent-cache HBM GB/s (% roofline), B=16 T=4096"
 WORKLOAD = "dsv2_b16_t4096"
 WORKLOADS = ("dsv2_b16_t4096", "ragged_b4_16k_32k", "paged_b128_t2048", "ctx128k_b2_60l",
-             "mtp2_b16_t4096", "fp8_b16_t4096")
+             "mtp2_b16_t4096", "fp8_b16_t4096", "prefill_c512_b4_t4096")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partials_dsv2_b16_t4096_counters.json")

@@ -77,8 +77,8 @@ mla_status_t check_cache(const mla_cache_t* c) {
 
 size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Most query tokens per request a plan accepts.
-constexpr int kMaxQueryLen = 16;
+// Most query tokens per request a plan accepts (a prefill chunk at most).
+constexpr int kMaxQueryLen = 1024;
 
 // Bytes of one partial output element: the MFMA kernel stores bf16 partials.
 size_t partial_elem_bytes(bool mfma) { return mfma ? 2 : sizeof(float); }

@@ -144,10 +144,11 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch, const void* q_c
 mla_status_t mla_decode_plan(const mla_dims_t* dims, int32_t batch, const mla_cache_t* cache,
                              int32_t split_tokens, mla_decode_plan_t* plan);
 
-/* As mla_decode_plan, for q_len query tokens per request (1 <= q_len <= 16):
+/* As mla_decode_plan, for q_len query tokens per request (1 <= q_len <= 1024):
  * the verification pass of speculative decoding, where tokens proposed by the
  * extra prediction depths are checked by the main model in one step (V3
- * read-through section 4.1).  The last q_len cached rows of request b are the
+ * read-through section 4.1), or a chunk of a prompt whose rows were just
+ * appended (chunked prefill, in the absorbed form).  The last q_len cached rows of request b are the
  * new tokens; query token j (0-based) is the one at position
  * seq_lens[b] - q_len + j and attends causally to rows
  * 0 .. seq_lens[b] - q_len + j (zeeklog MHA equation: attention over
@@ -155,7 +156,7 @@ mla_status_t mla_decode_plan(const mla_dims_t* dims, int32_t batch, const mla_ca
  * [batch, q_len, n_heads, d_latent + d_rope] and writes out_lat
  * [batch, q_len, n_heads, d_latent], lse [batch, q_len, n_heads] and, for
  * mla_decode_combine_out, out [batch, q_len, n_heads, d_head]; a token with
- * no visible row gets out_lat = 0 and lse = -inf.  q_len outside 1..16 ->
+ * no visible row gets out_lat = 0 and lse = -inf.  q_len outside 1..1024 ->
  * MLA_ERR_DIMS; other errors as mla_decode_plan. */
 mla_status_t mla_decode_plan_mq(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                                 const mla_cache_t* cache, int32_t split_tokens,

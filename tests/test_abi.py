@@ -184,7 +184,7 @@ def test_plan_shapes_and_workspace_errors():
                            plan.workspace_bytes, None)
     assert st == 2
     p2 = mla.Plan()
-    for q_len in (0, 17):
+    for q_len in (0, 1025):
         assert L.mla_decode_plan_mq(ctypes.byref(d), B, q_len, ctypes.byref(desc), 0,
                                     ctypes.byref(p2)) == 2
     torch.cuda.synchronize()

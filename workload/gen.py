@@ -129,6 +129,11 @@ CONFIGS: Dict[str, WorkloadConfig] = {
     "mtp2_b16_t4096": WorkloadConfig("mtp2_b16_t4096", batch=16, dtype="bf16",
                                      len_lo=4096, len_hi=4096, max_len=4096, q_len=2,
                                      **_DSV2),
+    # Chunked prefill in the absorbed form: 4 prompts of 4096 tokens whose last
+    # 512 rows are the chunk being processed (causal within it).
+    "prefill_c512_b4_t4096": WorkloadConfig("prefill_c512_b4_t4096", batch=4, dtype="bf16",
+                                            len_lo=4096, len_hi=4096, max_len=4096,
+                                            q_len=512, **_DSV2),
     # The default shape over the low-bit cache: the same drawn rows, quantised
     # to E4M3 with one scale per row.
     "fp8_b16_t4096": WorkloadConfig("fp8_b16_t4096", batch=16, dtype="bf16",
