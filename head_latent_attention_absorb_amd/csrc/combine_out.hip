@@ -17,7 +17,7 @@
 //
 // One workgroup = one head i and R = 8 / P requests (8 waves, P waves per
 // request).  The MFMA partials are row-major bf16,
-// part_o[((b * S + s) * n_rows + i) * 512 + c], so every (request, split)
+// part_o[((b * n_rows + i) * S + s) * 512 + c], so every (request, split)
 // contributes one contiguous 1 KiB row; (lse_s, m_s) are an fp32 pair per
 // (request, split, head).  Wave p of a request merges splits p, p + P,
 // p + 2P, ..., 8 latents per lane, with the loads of up to kBatch splits
@@ -108,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   const bool live = b < batch;
   // The rows this query token sees: up to its own position.
   const int len = live ? seq_lens[b] - (q_len - 1 - i / heads_per_token) : 0;
-  const size_t lbase = static_cast<size_t>(live ? b : 0) * num_splits * n_rows + i;
+  // Split-minor partials: the S rows and statistics of (b, i) are contiguous.
+  const size_t lbase = (static_cast<size_t>(live ? b : 0) * n_rows + i) * num_splits;
   // This wave's splits are p + k * P, k < nk.  Single pass with a running max
   // over batches of kB of them.  The loads of a batch (rows and statistics)
   // are issued together with the length load, without waiting for it and
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
   const uint16_t* row = part_o + lbase * kLat + seg * 8;
-  const size_t split_stride = static_cast<size_t>(n_rows) * kLat;
+  const size_t split_stride = kLat;
   int ns = 0;
   // One batch: returns false once the batch starts past the used splits.
   auto merge_batch = [&](int k0) {
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
     for (int j = 0; j < kB; ++j) {
       const size_t sidx = static_cast<size_t>(p + (min(k0 + j, nk - 1) << p_log2));
       v[j] = *reinterpret_cast<const bf16x8_t*>(row + sidx * split_stride);
-      const float2 ml = part_ml[lbase + sidx * n_rows];
+      const float2 ml = part_ml[lbase + sidx];
       x[j] = ml.x;
       y[j] = ml.y;
     }

@@ -775,7 +775,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // Softmax sum over both lane halves (each half saw half of the tokens).
   l = halves_sum(l);
   // bf16 partial, row-major per (request, split, head):
-  // part_o[((b * S + s) * n_rows + row) * 512 + c], written as accumulated
+  // part_o[((b * n_rows + row) * S + s) * 512 + c], written as accumulated
   // (relative to the running max m, not divided by l: the combine applies
   // both factors as one weight, which saves a multiply per element here).
   // Register v of latent
@@ -796,18 +796,21 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][g * 4 + e]);
       *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride + (cb * 32 + g * 8 + half * 4) * 2) = v4;
     }
+  // Split-minor layout: the S partial rows of one (request, row) are
+  // contiguous, so the combine reads each merge as one run.
   uint16_t* dst = p.part_o +
-                  ((static_cast<size_t>(b) * p.num_splits + s) * p.n_rows + hblock * 32) * 512 +
+                  ((static_cast<size_t>(b) * p.n_rows + hblock * 32) * p.num_splits + s) * 512 +
                   lane * 8;
+  const size_t row_stride = static_cast<size_t>(p.num_splits) * 512;
   // Plain stores: the combine that reads the partials right after this
   // kernel finds them in the last-level cache (non-temporal stores make this
   // kernel slightly faster but the whole step slower).
 #pragma unroll 8
   for (int r = 0; r < 32; ++r)
-    *reinterpret_cast<bf16x8_t*>(dst + r * 512) =
+    *reinterpret_cast<bf16x8_t*>(dst + r * row_stride) =
         *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
   if (half == 0)
-    p.part_ml[(static_cast<size_t>(b) * p.num_splits + s) * p.n_rows + head] =
+    p.part_ml[(static_cast<size_t>(b) * p.n_rows + head) * p.num_splits + s] =
         make_float2(m + __log2f(l), m);
 }
 

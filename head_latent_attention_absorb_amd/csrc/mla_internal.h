@@ -9,12 +9,13 @@
 namespace mla {
 
 // Split-KV partial results of the decode kernels live in the caller's
-// workspace: row-major partial outputs [request, split, head, d_latent] and
+// workspace: row-major partial outputs of d_latent elements and
 // per (request, split, head) statistics behind them.  The generic kernel
 // writes fp32 sums normalised by their own softmax sum and the fp32
-// natural-log sum-exp; the MFMA kernel writes bf16 sums relative to a
-// reference max m (not normalised) and the fp32 pair (log-sum-exp, m), both
-// in base-2 log units.
+// natural-log sum-exp, split-major ([request, split, row]); the MFMA kernel
+// writes bf16 sums relative to a reference max m (not normalised) and the
+// fp32 pair (log-sum-exp, m), both in base-2 log units, split-minor
+// ([request, row, split]: a merge reads one contiguous run).
 
 struct CacheView {
   const uint8_t* data;      // cache rows, (d_latent + d_rope) elements each
