@@ -248,6 +248,7 @@ def main():
     lse = torch.empty(lead + (nh,), dtype=torch.float32, device=dev)
     o = torch.empty(lead + (nh, cfg.d_head), dtype=torch.bfloat16, device=dev)
     q_rows = q_cat.view(B * ql, nh, row)
+    direct = plan.num_splits == 1
     stream = torch.cuda.current_stream()
 
     def layer(e: Entry, ev=None):
@@ -257,10 +258,19 @@ def main():
                      e.w_uk, out=q_rows)
         if ev is not None:
             ev[1].record(stream)
-        mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
-        if ev is not None:
-            ev[2].record(stream)
-        mla.decode_combine_out(e.cache, plan, ws, e.w_uv, o_lat, lse, out=o)
+        if direct:
+            # One split per request: mla_decode_attn's decode kernel writes
+            # o_lat and lse itself, then the per-head W^UV product.
+            mla.decode_attn(q_cat, e.cache, cfg.scale, plan, o_lat, lse, ws)
+            if ev is not None:
+                ev[2].record(stream)
+            mla.out_uv(o_lat.view(B * ql, nh, cfg.d_latent), e.w_uv,
+                       out=o.view(B * ql, nh, cfg.d_head))
+        else:
+            mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
+            if ev is not None:
+                ev[2].record(stream)
+            mla.decode_combine_out(e.cache, plan, ws, e.w_uv, o_lat, lse, out=o)
         if ev is not None:
             ev[3].record(stream)
 
@@ -326,28 +336,43 @@ def main():
         torch.cuda.synchronize()
         phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(4)] for ev in evs])
         append_us, absorb_us, partials_us, tail_us = (float(x) for x in phase.mean(axis=0) * 1e3)
-        kernels_us = {"absorb_q": absorb_us, "decode_partials": partials_us,
-                      "decode_combine_out": tail_us, "cache_append": append_us}
-        log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, partials "
-            f"{partials_us:.1f}, combine+out_uv {tail_us:.1f}")
+        if direct:
+            kernels_us = {"absorb_q": absorb_us, "decode_attn_direct": partials_us,
+                          "out_uv": tail_us, "cache_append": append_us}
+        else:
+            kernels_us = {"absorb_q": absorb_us, "decode_partials": partials_us,
+                          "decode_combine_out": tail_us, "cache_append": append_us}
+        log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, "
+            f"{'decode (direct)' if direct else 'partials'} {partials_us:.1f}, "
+            f"{'out_uv' if direct else 'combine+out_uv'} {tail_us:.1f}")
     else:
         log(f"[bench] step ({cfg.layers} layers) {ms_per_step*1e3:.1f} us")
 
     # The decode kernel alone, launched back to back on the same stream over
     # the same inputs: its average launch duration, free of the event records
     # that split the phases above.  This is the roofline's time.
+    # With one split the kernel runs in the form that writes o_lat directly
+    # (through mla_decode_attn, which then launches nothing else).
     n_dec = args.steps * (cfg.layers if layered else 1)
-    decode_us = timed(lambda i: mla.decode_partials(
-        q_cat, pool[i % n_pool].cache, cfg.scale, plan, ws), n_dec)
+    if direct:
+        decode_us = timed(lambda i: mla.decode_attn(
+            q_cat, pool[i % n_pool].cache, cfg.scale, plan, o_lat, lse, ws), n_dec)
+    else:
+        decode_us = timed(lambda i: mla.decode_partials(
+            q_cat, pool[i % n_pool].cache, cfg.scale, plan, ws), n_dec)
     log(f"[bench] decode kernel back to back: {decode_us:.1f} us per launch")
 
-    # mla_decode_attn (partials + split combine), back to back, per step.
+    # mla_decode_attn (partials + split combine, or the direct form), back to
+    # back, per step.
     def attn(i):
         for e in entries(i):
-            mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
-            mla.decode_combine(e.cache, nh, plan, ws, o_lat, lse)
+            if direct:
+                mla.decode_attn(q_cat, e.cache, cfg.scale, plan, o_lat, lse, ws)
+            else:
+                mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
+                mla.decode_combine(e.cache, nh, plan, ws, o_lat, lse)
     attn_us = timed(attn, args.steps)
-    log(f"[bench] mla_decode_attn (partials + combine) back to back: {attn_us:.1f} us per step")
+    log(f"[bench] mla_decode_attn back to back: {attn_us:.1f} us per step")
 
     # Algorithmic work per step (split partials excluded), averaged over the
     # entries the timed steps used.
@@ -416,7 +441,9 @@ def main():
         "step_roofline_us": t_roof_us,
         "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
         "attn": {
-            "what": "mla_decode_attn = decode partials + split combine, back to back",
+            "what": ("mla_decode_attn, one split: the decode kernel writes o_lat and lse "
+                     "directly" if direct else
+                     "mla_decode_attn = decode partials + split combine, back to back"),
             "us_per_step": attn_us,
             "roofline_us": t_roof_attn_us,
             "pct_roofline": 100.0 * t_roof_attn_us / attn_us,
@@ -427,7 +454,8 @@ def main():
         "tokens_per_layer": tokens_layer,
         "kernels_us": dict(kernels_us, decode_partials_back_to_back=decode_us),
         "roofline": {
-            "kernel": "decode_mfma_kernel (mla_decode_partials)",
+            "kernel": ("decode_mfma_kernel (mla_decode_attn, one split, direct output)" if direct
+                       else "decode_mfma_kernel (mla_decode_partials)"),
             "bound": "mfma" if k2_mfma_bound else "hbm",
             "achieved": k2_tflops if k2_mfma_bound else k2_gbps,
             "peak": MFMA_BF16_PEAK_TFLOPS if k2_mfma_bound else HBM_PEAK_GBPS,

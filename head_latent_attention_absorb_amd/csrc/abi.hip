@@ -346,7 +346,10 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* 
                                    &p, &a);
   if (st != MLA_OK || batch == 0) return st;
   (void)hipGetLastError();
-  if ((st = run_partials(a, p)) != MLA_OK) return st;
+  // One split per request: the MFMA kernel normalises its rows itself and
+  // writes o_lat and lse, so there is nothing to merge.
+  a.direct = p.kernel == 1 && p.num_splits == 1;
+  if ((st = run_partials(a, p)) != MLA_OK || a.direct) return st;
   return run_combine(a, p);
 }
 

@@ -52,15 +52,6 @@ __device__ __forceinline__ int used_splits(int len, int split_tokens) {
   return len > 0 ? (len + split_tokens - 1) / split_tokens : 0;
 }
 
-// 16-byte direct-to-LDS load (see the decode kernel): lands at lds_base +
-// 16 * lane.  Issued as inline asm; the kernel waits for it with an explicit
-// s_waitcnt vmcnt(0) before the barrier that publishes the LDS contents.
-__device__ __forceinline__ void load_to_lds16(const void* src, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
-}
 
 // kB: splits per batch of loads (at most kBatch), sized on the host to the
 // splits a wave merges.

@@ -102,6 +102,11 @@ struct MfmaParams {
   float scale_log2;       // softmax scale * log2(e)
   uint16_t* part_o;       // bf16 partials
   float2* part_ml;        // per (request, split, head): (base-2 log-sum-exp, m)
+  // One split only: when set, the kernel writes the normalised rows here
+  // ([B, n_rows, 512] bf16) and the natural-log lse to lse_out (if set)
+  // instead of partials.
+  uint16_t* out_lat;
+  float* lse_out;
 };
 
 // 16-byte direct-to-LDS load: every lane reads 16 bytes at `src` and writes
@@ -260,10 +265,22 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
                   (p.q_len - 1 - g * kMfmaHeadsPerGroup / p.heads_per_token);
   const int t0 = s * p.split_tokens;
   const int t1 = min(t0 + p.split_tokens, len);
-  if (t0 >= t1) return;  // the combine never reads partitions past the length
-
   const int hblock = g * 4 + wave;
   const int head = hblock * 32 + l32;
+  if (t0 >= t1) {
+    // The combine never reads partitions past the length.  Written directly,
+    // a row with nothing visible is o = 0, lse = -inf.
+    if (p.out_lat != nullptr) {
+      uint16_t* z = p.out_lat + (static_cast<size_t>(b) * p.n_rows + hblock * 32) * 512 + lane * 8;
+      bf16x8_t zero;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zero[e] = static_cast<__bf16>(0.f);
+      for (int r = 0; r < 32; ++r) *reinterpret_cast<bf16x8_t*>(z + r * 512) = zero;
+      if (p.lse_out != nullptr && half == 0)
+        p.lse_out[static_cast<size_t>(b) * p.n_rows + head] = -INFINITY;
+    }
+    return;
+  }
 
   f32x16_t acc[kCBlocks];
 #pragma unroll
@@ -787,18 +804,35 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   static_assert(4 * 32 * kOutStride <= kLdsBytes, "epilogue rows fit in the ring");
   __syncthreads();
   uint8_t* rows = lds + wave * 32 * kOutStride;
+  const bool direct = p.out_lat != nullptr;
+  if (direct) {
+    // Written directly (one split): each lane's row is its head's, divided
+    // by that head's softmax sum.
+    const float inv_l = 1.f / l;
 #pragma unroll
-  for (int cb = 0; cb < kCBlocks; ++cb)
+    for (int cb = 0; cb < kCBlocks; ++cb)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4_t v4;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t v4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][g * 4 + e]);
-      *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride + (cb * 32 + g * 8 + half * 4) * 2) = v4;
-    }
+        for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][g * 4 + e] * inv_l);
+        *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride + (cb * 32 + g * 8 + half * 4) * 2) = v4;
+      }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < kCBlocks; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][g * 4 + e]);
+        *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride + (cb * 32 + g * 8 + half * 4) * 2) = v4;
+      }
+  }
   // Split-minor layout: the S partial rows of one (request, row) are
-  // contiguous, so the combine reads each merge as one run.
-  uint16_t* dst = p.part_o +
+  // contiguous, so the combine reads each merge as one run.  With one split
+  // that is also the layout of out_lat.
+  uint16_t* dst = (direct ? p.out_lat : p.part_o) +
                   ((static_cast<size_t>(b) * p.n_rows + hblock * 32) * p.num_splits + s) * 512 +
                   lane * 8;
   const size_t row_stride = static_cast<size_t>(p.num_splits) * 512;
@@ -809,9 +843,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   for (int r = 0; r < 32; ++r)
     *reinterpret_cast<bf16x8_t*>(dst + r * row_stride) =
         *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
-  if (half == 0)
+  if (direct) {
+    if (p.lse_out != nullptr && half == 0)
+      p.lse_out[static_cast<size_t>(b) * p.n_rows + head] = (m + __log2f(l)) * kLn2;
+  } else if (half == 0) {
     p.part_ml[(static_cast<size_t>(b) * p.n_rows + head) * p.num_splits + s] =
         make_float2(m + __log2f(l), m);
+  }
 }
 
 }  // namespace
@@ -831,6 +869,9 @@ hipError_t launch_partials_mfma(const DecodeArgs& a) {
   p.scale_log2 = a.softmax_scale * kLog2e;
   p.part_o = static_cast<uint16_t*>(a.part_o);
   p.part_ml = reinterpret_cast<float2*>(a.part_lse);
+  if (a.direct && a.num_splits != 1) return hipErrorInvalidValue;
+  p.out_lat = a.direct ? static_cast<uint16_t*>(a.out_lat) : nullptr;
+  p.lse_out = a.direct ? a.lse : nullptr;
   const int grid = (p.work_items + 7) / 8 * 8;  // multiple of the 8 XCDs
   if (a.cache.page_table != nullptr) {
     if (a.cache.fp8)

@@ -44,6 +44,17 @@ __device__ __forceinline__ float ld_e4m3(const uint8_t* p) {
   return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(*p), 0);
 }
 
+// 16-byte direct-to-LDS load: lane l's 16 bytes land at lds_base +
+// 16 * l (M0 holds the wave's base).  Issued as inline asm; the caller waits
+// for it with an explicit s_waitcnt vmcnt(0) before the barrier that
+// publishes the LDS contents.
+__device__ __forceinline__ void load_to_lds16(const void* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

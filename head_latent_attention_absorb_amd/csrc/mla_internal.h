@@ -45,6 +45,9 @@ struct DecodeArgs {
   void* part_o;         // workspace: fp32 (generic kernel) or bf16 (MFMA kernel)
   float* part_lse;      // workspace: lse (generic kernel) or (lse, m) pairs (MFMA kernel)
   hipStream_t stream;
+  // MFMA kernel with one split: write out_lat and lse directly (no partials,
+  // no combine).
+  bool direct = false;
 };
 
 // Launchers return the hipError_t of the launch (hipSuccess when nothing

@@ -176,7 +176,10 @@ mla_status_t mla_decode_plan_mq(const mla_dims_t* dims, int32_t batch, int32_t q
  * mla_decode_plan_mq, whose q_len then sets the shapes) with the same dims,
  * batch and cache bounds.  workspace: device, >= plan->workspace_bytes, 256-byte
  * aligned, contents need no initialisation; calls that share a workspace
- * must be ordered on one stream. */
+ * must be ordered on one stream.  With a one-split plan on the MFMA kernel
+ * (plan->num_splits == 1, plan->kernel == 1) the decode kernel normalises its
+ * rows and writes out_lat and lse itself: nothing is merged and the workspace
+ * is not touched. */
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* q_cat,
                              const mla_cache_t* cache, float softmax_scale,
                              const mla_decode_plan_t* plan, void* out_lat, float* lse,

@@ -209,3 +209,33 @@ def test_prefill_chunk(paged):
         got_o = o_lat[b][np.ix_(toks, heads)]
         assert_close(got_o, o_ref[toks], "bf16", f"o_lat request {b}")
         assert_close(lse[b][np.ix_(toks, heads)], lse_ref[toks], "bf16", f"lse request {b}")
+
+
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_one_split_writes_output_directly(q_len):
+    """One split per request: mla_decode_attn has the MFMA kernel normalise its
+    rows and write o_lat and lse itself (no partials, no combine).  Lengths
+    include 0 and requests shorter than q_len, whose tokens see nothing."""
+    cfg = DSV2.replace(batch=5, len_lo=0, len_hi=700, max_len=704)
+    lens = np.array([0, 700, 2, 129, 33], np.int32)
+    case = make_case(cfg, 61 + q_len, seq_lens=lens)
+    _log(f"[direct] q_len={q_len}")
+    dc = DevCase(case)
+    q, q_dev = _query(cfg, 61 + q_len, q_len)
+    plan = mla.decode_plan(cfg.n_heads, cfg.d_latent, cfg.d_rope, torch.bfloat16, dc.cache,
+                           split_tokens=1024, q_len=q_len)
+    assert plan.kernel == 1 and plan.num_splits == 1
+    q_in = q_dev if q_len > 1 else q_dev[:, 0]
+    ws = mla.workspace_for(plan, "cuda")
+    o_lat, lse = mla.decode_attn(q_in, dc.cache, cfg.scale, plan=plan, workspace=ws)
+    # The same plan through the separate partials and combine calls.
+    mla.decode_partials(q_in, dc.cache, cfg.scale, plan, ws)
+    o_lat2 = torch.empty_like(o_lat)
+    lse2 = torch.empty_like(lse)
+    mla.decode_combine(dc.cache, cfg.n_heads, plan, ws, o_lat2, lse2)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _reference(case, q, q_len)
+    shape = (cfg.batch, q_len, cfg.n_heads)
+    for o_dev, l_dev in ((o_lat, lse), (o_lat2, lse2)):
+        _check(from_dev(o_dev).reshape(shape + (cfg.d_latent,)), from_dev(l_dev).reshape(shape),
+               o_ref, lse_ref, "bf16")

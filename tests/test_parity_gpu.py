@@ -239,6 +239,40 @@ def test_absorb_q_bf16_b16():
                  "q_cat")
 
 
+# Heads checked at prefill row counts (every row of them): both ends, and
+# heads on either side of the groups of 8 that share an XCD.
+_SAMPLED_HEADS = [0, 1, 7, 8, 9, 63, 64, 120, 126, 127]
+
+
+@pytest.mark.parametrize("batch", [256, 300, 2085])
+def test_absorb_q_bf16_many_rows(batch):
+    """Prefill-sized row counts: the form that keeps a head's whole W^UK in
+    LDS, with row runs split over workgroups and a ragged last run."""
+    cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1)
+    case = make_case(cfg, 5)
+    dc = DevCase(case)
+    _log(f"[absorb many rows] batch={batch}")
+    q_cat = mla.absorb_q(dc.q_c, dc.q_r, dc.w_uk)
+    torch.cuda.synchronize()
+    hs = _SAMPLED_HEADS
+    assert_close(from_dev(q_cat)[:, hs],
+                 oracle.absorb_query(case.q_c[:, hs], case.q_r[:, hs], case.w_uk[hs]), "bf16",
+                 "q_cat")
+
+
+@pytest.mark.parametrize("batch", [256, 300, 2085])
+def test_out_uv_bf16_many_rows(batch):
+    cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1)
+    case = make_case(cfg, 6)
+    o_lat_np = draw_latent_output(cfg, 6)
+    _log(f"[out_uv many rows] batch={batch}")
+    o = mla.out_uv(_bf16_dev(o_lat_np), DevCase(case).w_uv)
+    torch.cuda.synchronize()
+    hs = _SAMPLED_HEADS
+    assert_close(from_dev(o)[:, hs], oracle.project_out(o_lat_np[:, hs], case.w_uv[hs]), "bf16",
+                 "o")
+
+
 @pytest.mark.parametrize("batch", [1, 16, 128])
 def test_out_uv_bf16(batch):
     cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1)
