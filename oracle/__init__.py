@@ -31,7 +31,8 @@ pages is partly garbled; each reading taken is stated where it is used):
 
 Parity status: every function below is pinned by a test in
 ``tests/test_oracle_pins.py`` (decode), ``tests/test_oracle_append.py``
-(cache append), ``tests/test_oracle_causal.py`` (several query tokens) or
+(cache append), ``tests/test_oracle_causal.py`` (several query tokens),
+``tests/test_oracle_prefill.py`` (the unabsorbed chunk form) or
 ``tests/test_oracle_quant.py`` (low-bit cache) except where its docstring says
 "parity unpinned".
 """
@@ -47,6 +48,7 @@ from .mla_ref import (  # noqa: F401
     latent_attention_causal,
     mla_decode_absorbed,
     mla_decode_reference,
+    mla_prefill_reference,
     project_out,
     softmax_attention,
     up_project,

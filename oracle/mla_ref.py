@@ -226,6 +226,42 @@ def latent_attention_causal(q_cat: np.ndarray, rows: np.ndarray, d_latent: int,
     return o_lat, lse
 
 
+def mla_prefill_reference(q_c: np.ndarray, q_r: np.ndarray, latent: np.ndarray,
+                          k_rope: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray,
+                          scale: float, heads=None) -> Tuple[np.ndarray, np.ndarray]:
+    """A chunk of new tokens of one request in the primary (unabsorbed) form:
+    the cached latents are up-projected to per-head keys and values (zeeklog
+    equations 10-11), each key gets the shared k^R (ai-library "Multi-Head
+    Latent Attention"; V3 read-through section 2.3, k = [k_c; k_r]), and each
+    new token attends causally with the textbook softmax (zeeklog MHA
+    equation, positions 1..t).  The V2 read-through (section 2.3) notes that
+    the absorbed form is the one that pays off at decode; for a long chunk of
+    queries the explicit keys and values are computed once and shared.
+
+    latent [T, d_c], k_rope [T, d_h^R]: the request's cached rows, the chunk's
+    own rows included.  q_c [q_len, n_h, d_h], q_r [q_len, n_h, d_h^R]: token
+    j sits at position T - q_len + j and sees rows 0 .. T - q_len + j.
+    ``heads`` restricts the work to a subset (others stay 0 / -inf).
+    Returns (o [q_len, n_h, d_h], lse [q_len, n_h]) in float64.
+    """
+    q_c = np.asarray(q_c, np.float64)
+    q_r = np.asarray(q_r, np.float64)
+    q_len, n_h = q_c.shape[:2]
+    hs = np.arange(n_h) if heads is None else np.asarray(heads)
+    T = np.asarray(latent).shape[0]
+    k_c, v = up_project(latent, np.asarray(w_uk)[hs], np.asarray(w_uv)[hs])
+    k = np.concatenate([k_c, np.broadcast_to(np.asarray(k_rope, np.float64),
+                                             (len(hs), T, np.asarray(k_rope).shape[1]))],
+                       axis=2)
+    o = np.zeros((q_len, n_h, v.shape[2]))
+    lse = np.full((q_len, n_h), -np.inf)
+    for j in range(q_len):
+        visible = max(T - q_len + j + 1, 0)
+        q = np.concatenate([q_c[j, hs], q_r[j, hs]], axis=1)
+        o[j, hs], lse[j, hs] = softmax_attention(q, k[:, :visible], v[:, :visible], scale)
+    return o, lse
+
+
 def project_out(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
     """Apply W^UV after the latent-space sum: o_i[h] = sum_c W^UV[i,c,h] o_lat_i[c]
     (V2 read-through section 2.3; zeeklog equation 11 moved past the sum).
