@@ -112,6 +112,12 @@ def lib() -> ctypes.CDLL:
     L.mla_cache_append.argtypes = [ctypes.POINTER(Dims), i32, i32, vp, vp, vp, vp,
                                    ctypes.c_float, ctypes.POINTER(Rope), vp,
                                    ctypes.POINTER(CacheDesc), vp, sz, vp]
+    L.mla_prefill_expand.restype = ctypes.c_int
+    L.mla_prefill_expand.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(CacheDesc), vp,
+                                     vp, vp, vp, vp]
+    L.mla_prefill_attn.restype = ctypes.c_int
+    L.mla_prefill_attn.argtypes = [ctypes.POINTER(Dims), i32, i32, vp, vp,
+                                   ctypes.POINTER(CacheDesc), vp, vp, ctypes.c_float, vp, vp, vp]
     _lib = L
     return L
 
@@ -437,3 +443,60 @@ def cache_append(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr:
         ctypes.byref(dims), B, d_model, _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(rms_weight),
         float(rms_eps), ctypes.byref(rope), _ptr(positions), ctypes.byref(desc),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# A chunk of new tokens in the unabsorbed form
+# ----------------------------------------------------------------------------
+
+def prefill_expand(cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                   k_c: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                   stream=None):
+    """Explicit keys and values of every cached row (rows past each request's
+    length are left as they are): k_c[b,i,t] = W^UK_i c_t, v[b,i,t] = c_t W^UV_i,
+    both [B, n_h, max_len, d_h] bf16.  Contiguous native bf16 cache only."""
+    nh, dh, dc = w_uk.shape
+    B, max_len = cache.batch(), cache.data.shape[1]
+    dims = make_dims(nh, dh, cache.d_rope, dc, w_uk.dtype)
+    dev = w_uk.device
+    _require(w_uv, "w_uv", (nh, dc, dh), w_uk.dtype, dev)
+    shape = (B, nh, max_len, dh)
+    if k_c is None:
+        k_c = torch.empty(shape, dtype=w_uk.dtype, device=dev)
+    if v is None:
+        v = torch.empty(shape, dtype=w_uk.dtype, device=dev)
+    _require(k_c, "k_c", shape, w_uk.dtype, dev)
+    _require(v, "v", shape, w_uk.dtype, dev)
+    desc = cache.desc()
+    _check("mla_prefill_expand", lib().mla_prefill_expand(
+        ctypes.byref(dims), B, ctypes.byref(desc), _ptr(w_uk), _ptr(w_uv), _ptr(k_c), _ptr(v),
+        _stream(stream)))
+    return k_c, v
+
+
+def prefill_attn(q_c: torch.Tensor, q_r: torch.Tensor, cache: LatentCache, k_c: torch.Tensor,
+                 v: torch.Tensor, softmax_scale: float, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, stream=None):
+    """Causal attention of the last q_len positions of each request over the
+    explicit keys [k_c ; k^R] and values: q_c [B, q_len, n_h, d_h], q_r [B, q_len,
+    n_h, d_h^R] -> (out [B, q_len, n_h, d_h], lse [B, q_len, n_h])."""
+    B, q_len, nh, dh = q_c.shape
+    dr = q_r.shape[3]
+    dc = cache.data.shape[2] - dr
+    dims = make_dims(nh, dh, dr, dc, q_c.dtype)
+    dev = q_c.device
+    _require(q_r, "q_r", (B, q_len, nh, dr), q_c.dtype, dev)
+    max_len = cache.data.shape[1]
+    _require(k_c, "k_c", (B, nh, max_len, dh), q_c.dtype, dev)
+    _require(v, "v", (B, nh, max_len, dh), q_c.dtype, dev)
+    if out is None:
+        out = torch.empty((B, q_len, nh, dh), dtype=q_c.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, q_len, nh), dtype=torch.float32, device=dev)
+    _require(out, "out", (B, q_len, nh, dh), q_c.dtype, dev)
+    _require(lse, "lse", (B, q_len, nh), torch.float32, dev)
+    desc = cache.desc()
+    _check("mla_prefill_attn", lib().mla_prefill_attn(
+        ctypes.byref(dims), B, q_len, _ptr(q_c), _ptr(q_r), ctypes.byref(desc), _ptr(k_c),
+        _ptr(v), ctypes.c_float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse

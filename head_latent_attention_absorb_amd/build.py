@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(REPO_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libmla_absorb.so")
 
-SOURCES = ["abi.hip", "absorb_out.hip", "append.hip", "quant.hip", "combine_out.hip", "decode_generic.hip", "decode_mfma.hip"]
+SOURCES = ["abi.hip", "absorb_out.hip", "append.hip", "quant.hip", "combine_out.hip", "decode_generic.hip", "decode_mfma.hip", "prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

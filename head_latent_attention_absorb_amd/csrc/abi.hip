@@ -151,7 +151,7 @@ const char* mla_status_str(mla_status_t s) {
   return "MLA_ERR_UNKNOWN";
 }
 
-int32_t mla_abi_version(void) { return 3; }
+int32_t mla_abi_version(void) { return 4; }
 
 mla_status_t mla_quantize_rows(int64_t n_rows, int32_t width, int32_t src_dtype, const void* src,
                                void* dst, float* scales, void* stream) {
@@ -483,3 +483,80 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t batch, int32_t d_m
       const_cast<void*>(cache->data), workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
+
+// ----------------------------------------------------------------------------
+// Unabsorbed chunk form (explicit keys and values)
+// ----------------------------------------------------------------------------
+
+namespace {
+
+// Shared checks of the two chunk-form calls: bf16 at the DeepSeek-V2 widths,
+// a contiguous cache of native rows.
+mla_status_t check_prefill(const mla_dims_t* dims, int32_t batch, const mla_cache_t* cache) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_cache(cache)) != MLA_OK) return st;
+  if (batch < 0) return MLA_ERR_DIMS;
+  if (dims->dtype != MLA_BF16 || cache->row_format != MLA_ROWS_NATIVE) return MLA_ERR_DTYPE;
+  if (!mla::prefill_supported(1, dims->n_heads, dims->d_head, dims->d_latent, dims->d_rope) ||
+      cache->page_table != nullptr)
+    return MLA_ERR_DIMS;
+  return MLA_OK;
+}
+
+mla::CacheView contiguous_view(const mla_cache_t* cache) {
+  mla::CacheView view{};
+  view.data = static_cast<const uint8_t*>(cache->data);
+  view.seq_lens = cache->seq_lens;
+  view.max_len = cache->max_len;
+  return view;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_prefill_expand(const mla_dims_t* dims, int32_t batch, const mla_cache_t* cache,
+                                const void* w_uk, const void* w_uv, void* k_c, void* v,
+                                void* stream) {
+  mla_status_t st = check_prefill(dims, batch, cache);
+  if (st != MLA_OK || batch == 0) return st;
+  if (cache->data == nullptr || cache->seq_lens == nullptr || w_uk == nullptr ||
+      w_uv == nullptr || k_c == nullptr || v == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(cache->data) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(k_c) ||
+      !aligned16(v))
+    return MLA_ERR_ALIGN;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != MLA_OK) return st;
+  (void)hipGetLastError();
+  const hipError_t e = mla::launch_expand_kv(batch, dims->n_heads, contiguous_view(cache), w_uk,
+                                             w_uv, k_c, v, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status_t mla_prefill_attn(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                              const void* q_c, const void* q_r, const mla_cache_t* cache,
+                              const void* k_c, const void* v, float softmax_scale, void* out,
+                              float* lse, void* stream) {
+  mla_status_t st = check_prefill(dims, batch, cache);
+  if (st != MLA_OK) return st;
+  if (q_len < 1 || q_len > cache->max_len) return MLA_ERR_DIMS;
+  if (batch == 0) return MLA_OK;
+  if (q_c == nullptr || q_r == nullptr || cache->data == nullptr ||
+      cache->seq_lens == nullptr || k_c == nullptr || v == nullptr || out == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned16(q_c) || !aligned16(q_r) || !aligned16(cache->data) || !aligned16(k_c) ||
+      !aligned16(v) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return MLA_ERR_ALIGN;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != MLA_OK) return st;
+  (void)hipGetLastError();
+  const hipError_t e = mla::launch_prefill_attn(batch, q_len, dims->n_heads,
+                                                contiguous_view(cache), q_c, q_r, k_c, v,
+                                                softmax_scale, out, lse,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+}  // extern "C"

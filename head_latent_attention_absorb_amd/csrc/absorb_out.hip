@@ -254,22 +254,40 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
 }
 
 
-// The same products for many rows (a prefill chunk: batch = requests x query
-// tokens): a workgroup owns head i and a run of rows_per_wg rows, stages the
-// whole [K x N] weight of the head in LDS once (128 KiB at both DeepSeek-V2
-// shapes) and streams its rows through it.  Each wave takes 64 rows (two M
-// tiles that share every B operand read) per pass of 256 rows; K is walked in
-// chunks of 128 whose A operands are loaded a chunk ahead.  The weight lands
-// in LDS with direct loads, its rows XOR-swizzled in 8-byte units so that the
-// transposing reads of four consecutive k rows hit distinct banks: logical
-// unit u of row k sits at u ^ ((k & 3) << 3).  Workgroups of one head are 8
-// apart in launch order, so they share one XCD and the weight's trip through
-// its L2.
-template <int K, int N>
-__global__ __launch_bounds__(256) void head_proj_wide_kernel(
-    const __bf16* __restrict__ X, const __bf16* __restrict__ W, __bf16* __restrict__ Y,
-    int batch, int n_heads, int y_row, int rows_per_wg, int chunks,
-    const __bf16* __restrict__ tail_src, int tail_w) {
+// The same products for many rows: a workgroup owns head i and a run of
+// rows_per_wg rows of one request, stages the whole weight of the head in LDS
+// once (128 KiB at the DeepSeek-V2 shapes) and streams its rows through it.
+// Rows are (request b, row t < len_b) with element offsets
+//   X: b * x_req + t * x_row + i * x_head,  Y: b * y_req + t * y_row + i * y_head,
+// which covers the absorbed query and W^UV product of a prefill chunk (one
+// "request" of batch rows) and the explicit key / value expansion of cached
+// latents (rows of each request's cache, shared by all heads).
+// Each wave takes 64 rows (two M tiles that share every weight read) per pass
+// of 256 rows; K is walked in chunks of 128 whose row operands are loaded a
+// chunk ahead.  The weight is the MFMA A operand (the product is computed
+// transposed, so that each lane ends up owning one output row), read from LDS
+// either with the transposing read (kWT false: W[i] stored [K][N], as W^UK in
+// the absorption and W^UV) or plainly (kWT true: stored [N][K], as W^UK in the
+// key expansion).  The weight lands in LDS with direct loads, XOR-swizzled
+// against bank conflicts: [K][N] rows in 8-byte units, unit u of row k at
+// u ^ ((k & 3) << 3); [N][K] rows in 16-byte units, unit c of row n at
+// c ^ (n & 15).  Output blocks go through LDS so that stores write whole
+// 256-byte row runs.
+struct WideArgs {
+  const __bf16* X;
+  const __bf16* W;
+  __bf16* Y;
+  const int32_t* seq_lens;  // rows of request b: seq_lens[b] (NULL: rows_per_req)
+  int n_req, rows_per_req, n_heads;
+  long long x_req, x_row, x_head, y_req, y_row, y_head;
+  int rows_per_wg, chunks;  // row runs per request
+  const __bf16* tail_src;   // RoPE tail copied after the N product columns:
+  int tail_w;               // row t of head i (one request) at
+  long long tail_row;       // tail_src + t * tail_row + i * tail_w
+};
+
+template <int K, int N, bool kWT>
+__global__ __launch_bounds__(256) void head_proj_wide_kernel(WideArgs p) {
   constexpr int KC = 128, NKC = K / KC, NG = N / 128;
   static_assert(K % KC == 0 && N % 128 == 0 && (NKC == 1 || NG == 1), "");
   static_assert(K * N * 2 + 4 * 32 * 256 <= 160 * 1024, "the weight must fit in LDS");
@@ -278,24 +296,34 @@ __global__ __launch_bounds__(256) void head_proj_wide_kernel(
   // memory (256-byte rows, 16-byte chunks XOR-swizzled by row & 15).
   __shared__ __attribute__((aligned(16))) uint8_t y_s[4][32 * 256];
 
-  // Head and row run of this workgroup (see above for the XCD grouping).
+  // (head, work) of this workgroup; work = request * chunks + run.  When the
+  // works split evenly over the 8 XCDs, every XCD takes whole works and runs
+  // all heads of each (its rows, shared by the heads, stay in its L2);
+  // otherwise workgroups of one head are n_heads apart (same XCD when
+  // n_heads % 8 == 0) and share the head's weight through L2.
   const int id = blockIdx.x;
-  int i, chunk;
-  if (n_heads % 8 == 0) {
-    i = (id / (8 * chunks)) * 8 + id % 8;
-    chunk = (id / 8) % chunks;
+  const int n_works = p.n_req * p.chunks;
+  int i, work;
+  if (n_works % 8 == 0) {
+    i = (id >> 3) % p.n_heads;
+    work = ((id >> 3) / p.n_heads) * 8 + (id & 7);
   } else {
-    i = id / chunks;
-    chunk = id % chunks;
+    i = id % p.n_heads;
+    work = id / p.n_heads;
   }
-  const int r0 = chunk * rows_per_wg;
-  const int r1 = min(batch, r0 + rows_per_wg);
+  const int b = work / p.chunks, chunk = work - b * p.chunks;
+  const int len = p.seq_lens != nullptr ? min(p.seq_lens[b], p.rows_per_req) : p.rows_per_req;
+  const int r0 = chunk * p.rows_per_wg;
+  const int r1 = min(len, r0 + p.rows_per_wg);
   if (r0 >= r1) return;
+  const __bf16* X = p.X + b * p.x_req + i * p.x_head;
+  __bf16* Y = p.Y + b * p.y_req + i * p.y_head;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
 
-  // A operand fragments of the wave's two M tiles for one K chunk: row
-  // m + t*32 + l32, K elements kc*128 + ks*16 + half*8 .. +7 (zero past r1).
+  // Row operand fragments of the wave's two M tiles for one K chunk: row
+  // m + t*32 + l32, K elements kc*128 + ks*16 + half*8 .. +7 (rows past r1
+  // repeat the last row and are not stored).
   bf16x8_t a[2][8], an[2][8];
   const int passes = (r1 - r0 + 255) / 256;
   const int n_chunks = passes * NKC;
@@ -304,8 +332,7 @@ __global__ __launch_bounds__(256) void head_proj_wide_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int row = r0 + pass * 256 + wave * 64 + t * 32 + l32;
-      const __bf16* xr = X + (static_cast<size_t>(min(row, r1 - 1)) * n_heads + i) * K +
-                         kc * KC + half * 8;
+      const __bf16* xr = X + min(row, r1 - 1) * p.x_row + kc * KC + half * 8;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) dst[t][ks] = *reinterpret_cast<const bf16x8_t*>(xr + ks * 16);
     }
@@ -313,39 +340,45 @@ __global__ __launch_bounds__(256) void head_proj_wide_kernel(
   load_a(0, a);
 
   // The whole weight of head i into LDS: wave instruction j fills 1 KiB, lane
-  // l its 16-byte unit (k, v) with v the physical 16-byte column; the source is
-  // the logical unit v ^ ((k & 3) << 2).
+  // l its physical 16-byte unit; the source is the logical unit it holds.
   {
-    constexpr int kUnitsPerRow = N / 8;
-    const __bf16* src = W + static_cast<size_t>(i) * K * N;
+    const __bf16* src = p.W + static_cast<size_t>(i) * K * N;
     const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS __bf16*)w_s));
     for (int j = wave; j < K * N * 2 / 1024; j += 4) {
       const int unit = j * 64 + lane;
-      const int k = unit / kUnitsPerRow, v = unit - k * kUnitsPerRow;
-      load_to_lds16(src + static_cast<size_t>(k) * N + ((v ^ ((k & 3) << 2)) * 8), base + j * 1024);
+      if constexpr (kWT) {
+        constexpr int kUnitsPerRow = K / 8;
+        const int n = unit / kUnitsPerRow, c = unit - n * kUnitsPerRow;
+        load_to_lds16(src + static_cast<size_t>(n) * K + ((c ^ (n & 15)) * 8), base + j * 1024);
+      } else {
+        constexpr int kUnitsPerRow = N / 8;
+        const int k = unit / kUnitsPerRow, v = unit - k * kUnitsPerRow;
+        load_to_lds16(src + static_cast<size_t>(k) * N + ((v ^ ((k & 3) << 2)) * 8),
+                      base + j * 1024);
+      }
     }
   }
   // The RoPE tail of the absorbed query rows is copied unchanged, 8 vectors
   // per thread per round: all their loads, then all their stores (one memory
   // round trip per round).
-  if (tail_src != nullptr) {
-    const int tq = tail_w / 4, n_tail = (r1 - r0) * tq;
+  if (p.tail_src != nullptr) {
+    const __bf16* tsrc = p.tail_src + i * p.tail_w;
+    const long long t_row = p.tail_row;
+    const int tq = p.tail_w / 4, n_tail = (r1 - r0) * tq;
     for (int e0 = tid; e0 < n_tail; e0 += 8 * 256) {
       bf16x4_t v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int e = min(e0 + j * 256, n_tail - 1);
         const int row = r0 + e / tq, c4 = e - (e / tq) * tq;
-        v[j] = *reinterpret_cast<const bf16x4_t*>(
-            tail_src + (static_cast<size_t>(row) * n_heads + i) * tail_w + c4 * 4);
+        v[j] = *reinterpret_cast<const bf16x4_t*>(tsrc + row * t_row + c4 * 4);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int e = e0 + j * 256;
         if (e < n_tail) {
           const int row = r0 + e / tq, c4 = e - (e / tq) * tq;
-          *reinterpret_cast<bf16x4_t*>(Y + (static_cast<size_t>(row) * n_heads + i) * y_row + N +
-                                       c4 * 4) = v[j];
+          *reinterpret_cast<bf16x4_t*>(Y + row * p.y_row + N + c4 * 4) = v[j];
         }
       }
     }
@@ -353,20 +386,42 @@ __global__ __launch_bounds__(256) void head_proj_wide_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Transposing-read coordinates (see head_proj_mfma_kernel): lane (G, q)
-  // reads k row k0 + (G/2)*8 + q/4 (+4 for the high half), 8-byte unit
-  // 4*(G%2) + q%4 of the 32-column block; k & 3 = q / 4 for both halves.
+  // Weight fragment for k rows k0 .. k0+15 (this lane: k0 + half*8 .. +7) and
+  // output column n0 + l32.  [K][N]: transposing reads, lane (G, q) reading k
+  // row k0 + (G/2)*8 + q/4 (+4 for the high half) at 8-byte unit 4*(G%2) +
+  // q%4 of the 32-column block (k & 3 = q / 4 for both halves).
   const int G = lane >> 4, q16 = lane & 15;
   const int tr_k = ((G >> 1) << 3) + (q16 >> 2);
   const int tr_u = ((G & 1) << 2) + (q16 & 3);
   const int swz = (q16 >> 2) << 3;
-  const i16x4_t* wl = reinterpret_cast<const i16x4_t*>(w_s);  // 8-byte units
-  constexpr int kU = N / 4;                                     // units per k row
+  auto wfrag = [&](int k0, int n0) -> bf16x8_t {
+    if constexpr (kWT) {
+      const int n = n0 + l32;
+      const int c = ((k0 >> 3) + half) ^ (n & 15);
+      return *reinterpret_cast<const bf16x8_t*>(w_s + n * K + c * 8);
+    } else {
+      const i16x4_t* wl = reinterpret_cast<const i16x4_t*>(w_s);  // 8-byte units
+      constexpr int kU = N / 4;
+      const int un = ((n0 >> 2) + tr_u) ^ swz;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (MLA_LDS i16x4_t*)(wl + (k0 + tr_k) * kU + un));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (MLA_LDS i16x4_t*)(wl + (k0 + tr_k + 4) * kU + un));
+      return __builtin_bit_cast(bf16x8_t,
+                                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
 
   f32x16_t acc[2][4];
   for (int u = 0; u < n_chunks; ++u) {
     const int pass = u / NKC, kc = u - pass * NKC;
-    if (u + 1 < n_chunks) load_a(u + 1, an);
+    // Several K chunks: the next chunk's rows are loaded while this one is
+    // multiplied.  One chunk (the NG column groups share it): the next pass's
+    // rows are loaded after this pass, which saves the registers of a second
+    // buffer.
+    if constexpr (NKC > 1) {
+      if (u + 1 < n_chunks) load_a(u + 1, an);
+    }
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
       if (kc == 0) {
@@ -379,20 +434,13 @@ __global__ __launch_bounds__(256) void head_proj_wide_kernel(
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int k0 = kc * KC + ks * 16 + tr_k;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const int un = ((ng * 4 + nb) * 8 + tr_u) ^ swz;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (MLA_LDS i16x4_t*)(wl + k0 * kU + un));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (MLA_LDS i16x4_t*)(wl + (k0 + 4) * kU + un));
-          const bf16x8_t bop = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          // Transposed product (weight as the A operand): the accumulator holds
-          // Y^T, so each lane owns one row and runs of 4 columns.
-          acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, a[0][ks], acc[0][nb], 0, 0, 0);
-          acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, a[1][ks], acc[1][nb], 0, 0, 0);
+          const bf16x8_t wop = wfrag(kc * KC + ks * 16, (ng * 4 + nb) * 32);
+          // Transposed product (weight as the A operand): the accumulator
+          // holds Y^T, so each lane owns one row and runs of 4 columns.
+          acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop, a[0][ks], acc[0][nb], 0, 0, 0);
+          acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop, a[1][ks], acc[1][nb], 0, 0, 0);
         }
       }
       if (kc == NKC - 1) {
@@ -422,30 +470,41 @@ __global__ __launch_bounds__(256) void head_proj_wide_kernel(
                 *reinterpret_cast<const bf16x8_t*>(ys + rr * 256 + ((c16 ^ (rr & 15)) << 4));
             const int row = r0 + pass * 256 + wave * 64 + t * 32 + rr;
             if (row < r1)
-              *reinterpret_cast<bf16x8_t*>(Y + (static_cast<size_t>(row) * n_heads + i) * y_row +
-                                           ng * 128 + c16 * 8) = v;
+              *reinterpret_cast<bf16x8_t*>(Y + row * p.y_row + ng * 128 + c16 * 8) = v;
           }
         }
       }
     }
     if (u + 1 < n_chunks) {
+      if constexpr (NKC > 1) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) a[t][ks] = an[t][ks];
+          for (int ks = 0; ks < 8; ++ks) a[t][ks] = an[t][ks];
+      } else {
+        load_a(u + 1, a);
+      }
     }
   }
 }
 
-// Workgroups per head of head_proj_wide_kernel and rows per workgroup (a
-// multiple of 256): about 512 workgroups in all, fewer when the rows run out.
-void wide_split(int batch, int n_heads, int* rows_per_wg, int* chunks) {
-  const int tiles = (batch + 255) / 256;
-  int c = 512 / n_heads;
+// Runs per request of head_proj_wide_kernel and rows per run (a multiple of
+// 256): about 512 workgroups in all, fewer when the rows run out.
+void wide_split(int n_req, int rows, int n_heads, int* rows_per_wg, int* chunks) {
+  const int tiles = (rows + 255) / 256;
+  int c = 512 / (n_heads * n_req);
   c = c < 1 ? 1 : (c > tiles ? tiles : c);
   const int per = (tiles + c - 1) / c;
   *rows_per_wg = per * 256;
-  *chunks = (batch + *rows_per_wg - 1) / *rows_per_wg;
+  *chunks = (rows + *rows_per_wg - 1) / *rows_per_wg;
+}
+
+// Launch over n_req requests of up to rows_per_req rows.
+template <int K, int N, bool kWT>
+hipError_t launch_wide(WideArgs p, hipStream_t stream) {
+  wide_split(p.n_req, p.rows_per_req, p.n_heads, &p.rows_per_wg, &p.chunks);
+  head_proj_wide_kernel<K, N, kWT><<<p.n_heads * p.n_req * p.chunks, 256, 0, stream>>>(p);
+  return hipGetLastError();
 }
 
 // Row count from which the wide form replaces head_proj_mfma_kernel.
@@ -458,13 +517,21 @@ hipError_t launch_absorb_q(int dtype, int batch, int n_heads, int d_head, int d_
   if (batch == 0) return hipSuccess;
   if (dtype == 1 && d_head == 128 && d_latent == 512 && d_rope % 4 == 0 &&
       batch >= kWideRows) {
-    int rows, chunks;
-    wide_split(batch, n_heads, &rows, &chunks);
-    head_proj_wide_kernel<128, 512><<<n_heads * chunks, 256, 0, stream>>>(
-        static_cast<const __bf16*>(q_c), static_cast<const __bf16*>(w_uk),
-        static_cast<__bf16*>(q_cat), batch, n_heads, d_latent + d_rope, rows, chunks,
-        d_rope > 0 ? static_cast<const __bf16*>(q_r) : nullptr, d_rope);
-    return hipGetLastError();
+    WideArgs p{};
+    p.X = static_cast<const __bf16*>(q_c);
+    p.W = static_cast<const __bf16*>(w_uk);
+    p.Y = static_cast<__bf16*>(q_cat);
+    p.n_req = 1;
+    p.rows_per_req = batch;
+    p.n_heads = n_heads;
+    p.x_row = static_cast<long long>(n_heads) * d_head;
+    p.x_head = d_head;
+    p.y_row = static_cast<long long>(n_heads) * (d_latent + d_rope);
+    p.y_head = d_latent + d_rope;
+    p.tail_src = d_rope > 0 ? static_cast<const __bf16*>(q_r) : nullptr;
+    p.tail_w = d_rope;
+    p.tail_row = static_cast<long long>(n_heads) * d_rope;
+    return launch_wide<128, 512, false>(p, stream);
   }
   if (dtype == 1 && d_head == 128 && d_latent % 128 == 0 && d_rope % 4 == 0) {
     head_proj_mfma_kernel<128, 128, 4><<<dim3(d_latent / 128, n_heads), 256, 0, stream>>>(
@@ -490,17 +557,51 @@ hipError_t launch_absorb_q(int dtype, int batch, int n_heads, int d_head, int d_
   return hipGetLastError();
 }
 
+// Explicit keys and values of every cached latent row of each request (rows
+// 0 .. seq_lens[b]-1 of a contiguous bf16 cache): k_c[b, i, t] = W^UK[i] c_t
+// and v[b, i, t, h] = sum_c W^UV[i, c, h] c_t[c], both [B, n_h, max_len, d_h].
+hipError_t launch_expand_kv(int batch, int n_heads, const CacheView& cache, const void* w_uk,
+                            const void* w_uv, void* k_c, void* v, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  constexpr int kDc = 512, kDh = 128, kRowElems = 576;
+  WideArgs p{};
+  p.X = reinterpret_cast<const __bf16*>(cache.data);
+  p.seq_lens = cache.seq_lens;
+  p.n_req = batch;
+  p.rows_per_req = cache.max_len;
+  p.n_heads = n_heads;
+  p.x_req = static_cast<long long>(cache.max_len) * kRowElems;
+  p.x_row = kRowElems;
+  p.x_head = 0;
+  p.y_req = static_cast<long long>(n_heads) * cache.max_len * kDh;
+  p.y_row = kDh;
+  p.y_head = static_cast<long long>(cache.max_len) * kDh;
+  p.W = static_cast<const __bf16*>(w_uk);  // [n_h][d_h][d_c]: N rows of K
+  p.Y = static_cast<__bf16*>(k_c);
+  hipError_t e = launch_wide<kDc, kDh, true>(p, stream);
+  if (e != hipSuccess) return e;
+  p.W = static_cast<const __bf16*>(w_uv);  // [n_h][d_c][d_h]: K rows of N
+  p.Y = static_cast<__bf16*>(v);
+  return launch_wide<kDc, kDh, false>(p, stream);
+}
+
 hipError_t launch_out_uv(int dtype, int batch, int n_heads, int d_head, int d_latent,
                          const void* out_lat, const void* w_uv, void* out,
                          hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   if (dtype == 1 && d_latent == 512 && d_head == 128 && batch >= kWideRows) {
-    int rows, chunks;
-    wide_split(batch, n_heads, &rows, &chunks);
-    head_proj_wide_kernel<512, 128><<<n_heads * chunks, 256, 0, stream>>>(
-        static_cast<const __bf16*>(out_lat), static_cast<const __bf16*>(w_uv),
-        static_cast<__bf16*>(out), batch, n_heads, d_head, rows, chunks, nullptr, 0);
-    return hipGetLastError();
+    WideArgs p{};
+    p.X = static_cast<const __bf16*>(out_lat);
+    p.W = static_cast<const __bf16*>(w_uv);
+    p.Y = static_cast<__bf16*>(out);
+    p.n_req = 1;
+    p.rows_per_req = batch;
+    p.n_heads = n_heads;
+    p.x_row = static_cast<long long>(n_heads) * d_latent;
+    p.x_head = d_latent;
+    p.y_row = static_cast<long long>(n_heads) * d_head;
+    p.y_head = d_head;
+    return launch_wide<512, 128, false>(p, stream);
   }
   if (dtype == 1 && d_latent == 512 && d_head % 64 == 0) {
     head_proj_mfma_kernel<512, 64, 2><<<dim3(d_head / 64, n_heads), 256, 0, stream>>>(

@@ -59,6 +59,17 @@ hipError_t launch_out_uv(int dtype, int batch, int n_heads, int d_head, int d_la
                          const void* out_lat, const void* w_uv, void* out,
                          hipStream_t stream);
 
+// Unabsorbed chunk form (bf16, d_h = 128, d_h^R = 64, d_c = 512, contiguous
+// native cache): explicit keys and values of the cached rows, then causal
+// attention of q_len new tokens per request over them.
+bool prefill_supported(int dtype, int n_heads, int d_head, int d_latent, int d_rope);
+hipError_t launch_expand_kv(int batch, int n_heads, const CacheView& cache, const void* w_uk,
+                            const void* w_uv, void* k_c, void* v, hipStream_t stream);
+hipError_t launch_prefill_attn(int batch, int q_len, int n_heads, const CacheView& cache,
+                               const void* q_c, const void* q_r, const void* k_c,
+                               const void* v, float softmax_scale, void* out, float* lse,
+                               hipStream_t stream);
+
 // Generic split-KV partials (fp32 VALU arithmetic, any dims, fp32 or bf16
 // storage), row-major partial layout.
 hipError_t launch_partials_generic(const DecodeArgs& a);

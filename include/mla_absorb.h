@@ -121,7 +121,8 @@ const char* mla_status_str(mla_status_t status);
 
 /* Library ABI version (incremented on any signature change; 2 added
  * mla_decode_plan_t.q_len and mla_decode_plan_mq; 3 added mla_cache_t.scales,
- * mla_cache_t.row_format and mla_quantize_rows). */
+ * mla_cache_t.row_format and mla_quantize_rows; 4 added mla_prefill_expand and
+ * mla_prefill_attn). */
 int32_t mla_abi_version(void);
 
 /* Absorb W^UK into the query (V2 read-through section 2.3; V3 read-through
@@ -300,6 +301,49 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t batch, int32_t d_m
                               const void* rms_weight, float rms_eps, const mla_rope_t* rope,
                               const int32_t* positions, const mla_cache_t* cache,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- A chunk of new tokens in the primary (unabsorbed) form ----
+ * For a long chunk of new tokens (prefill) the explicit per-head keys and
+ * values can cost less than absorption: the up-projection (zeeklog equations
+ * 10-11) is paid once per cached row and shared by every query of the chunk,
+ * after which each query-key pair costs (d_h + d_h^R) + d_h multiply-adds per
+ * head instead of (d_c + d_h^R) + d_c (V2 read-through section 2.3 places the
+ * absorption's gain at decode).  Two calls:
+ *   mla_prefill_expand  k_c[b,i,t] = W^UK_i c_t,  v[b,i,t,h] = sum_c W^UV[i,c,h] c_t[c]
+ *   mla_prefill_attn    causal attention of the chunk over [k_c ; k^R] and v
+ * Supported: dims->dtype MLA_BF16, d_head 128, d_rope 64, d_latent 512, any
+ * n_heads >= 1; a contiguous cache (page_table NULL) of native rows.  Other
+ * dims -> MLA_ERR_DIMS, other storage -> MLA_ERR_DTYPE. */
+
+/* Explicit keys and values of every cached row of each request (rows
+ * 0 .. seq_lens[b]-1; the rows past the length are not written):
+ *   k_c[b, i, t, :] = W^UK[i] c_t        (w_uk [n_heads, d_head, d_latent])
+ *   v  [b, i, t, h] = sum_c w_uv[i, c, h] c_t[c]   (w_uv [n_heads, d_latent, d_head])
+ * with c_t = row t of request b [0:d_latent].  k_c and v: device,
+ * [batch, n_heads, cache->max_len, d_head] bf16, caller-owned (2 * batch *
+ * n_heads * max_len * d_head * 2 bytes together).  fp32 accumulation, one
+ * rounding to bf16.  batch 0 is a no-op. */
+mla_status_t mla_prefill_expand(const mla_dims_t* dims, int32_t batch, const mla_cache_t* cache,
+                                const void* w_uk, const void* w_uv, void* k_c, void* v,
+                                void* stream);
+
+/* Causal attention of q_len new tokens per request, unabsorbed (zeeklog MHA
+ * equation; keys [k^C ; k^R] with k^R shared by the heads, ai-library
+ * "Multi-Head Latent Attention"): token j of request b sits at position
+ * seq_lens[b] - q_len + j (its row already in the cache and expanded) and
+ *   s[t]         = softmax_scale * (q_c[b,j,i] . k_c[b,i,t] + q_r[b,j,i] . k^R_t)
+ *   out[b,j,i,:] = sum_{t <= pos} softmax_t(s) v[b,i,t,:]
+ *   lse[b,j,i]   = ln sum_{t <= pos} exp(s[t])
+ * q_c [batch, q_len, n_heads, d_head], q_r [batch, q_len, n_heads, d_rope],
+ * k_c and v as written by mla_prefill_expand, k^R_t = cache row t [d_latent:];
+ * out [batch, q_len, n_heads, d_head] bf16, lse fp32 (may be NULL).  A token
+ * with no visible row gets out = 0 and lse = -inf.  q_len outside
+ * 1..cache->max_len -> MLA_ERR_DIMS.  fp32 scores, softmax and accumulation;
+ * the probabilities enter the value product as bf16. */
+mla_status_t mla_prefill_attn(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                              const void* q_c, const void* q_r, const mla_cache_t* cache,
+                              const void* k_c, const void* v, float softmax_scale, void* out,
+                              float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_absorb_q", "mla_decode_attn", "mla_out_uv", "mla_decode_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
-    assert L.mla_abi_version() == 3
+    assert L.mla_abi_version() == 4
 
 
 def test_status_strings():
