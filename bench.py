@@ -40,7 +40,8 @@ from workload import CONFIGS, f32_to_bf16_bits, make_append_case, make_case  # n
 METRIC = "MLA decode tokens/s and latent-cache HBM GB/s (% roofline), B=16 T=4096"
 WORKLOAD = "dsv2_b16_t4096"
 WORKLOADS = ("dsv2_b16_t4096", "ragged_b4_16k_32k", "paged_b128_t2048", "ctx128k_b2_60l",
-             "mtp2_b16_t4096", "fp8_b16_t4096", "prefill_c512_b4_t4096")
+             "mtp2_b16_t4096", "fp8_b16_t4096", "prefill_c512_b4_t4096",
+             "prefill_unabsorbed_c512_b4_t4096")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partials_dsv2_b16_t4096_counters.json")
@@ -188,6 +189,155 @@ def percentiles(x):
             "p90": float(np.percentile(x, 90))}
 
 
+def run_unabsorbed(args, cfg, name):
+    """The chunk in the unabsorbed form: one step = mla_prefill_expand (explicit
+    keys and values of every cached row) + mla_prefill_attn (causal attention
+    of the q_len new tokens over them), per request batch.  Same inputs, pool
+    rotation, timing and JSON line as the absorbed workloads; the roofline is
+    prefill_attn_kernel's MFMA one."""
+    B, nh, ql = cfg.batch, cfg.n_heads, cfg.q_len
+    dh, dr, dc = cfg.d_head, cfg.d_rope, cfg.d_latent
+    log(f"[bench] generating inputs for {name}")
+    pool = [Entry(cfg, 0)]
+    n_pool = max(1, math.ceil(args.pool_mb * 1e6 / pool[0].nbytes))
+    for i in range(1, n_pool):
+        pool.append(Entry(cfg, i))
+    pool_mb = sum(e.nbytes for e in pool) / 1e6
+    log(f"[bench] pool: {n_pool} entries, {pool_mb:.0f} MB")
+    dev = "cuda"
+    kv_shape = (B, nh, cfg.max_len, dh)
+    k_c = torch.empty(kv_shape, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(kv_shape, dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, ql, nh, dh), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, ql, nh), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def views(e):
+        return e.q_c.view(B, ql, nh, dh), e.q_r.view(B, ql, nh, dr)
+
+    def step(i, ev=None):
+        e = pool[i % n_pool]
+        q_c, q_r = views(e)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.prefill_expand(e.cache, e.w_uk, e.w_uv, k_c=k_c, v=v)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.prefill_attn(q_c, q_r, e.cache, k_c, v, cfg.scale, out=out, lse=lse)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e_start.elapsed_time(e_end) / args.steps
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    bounds[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        bounds[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_us = [bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(2)] for ev in evs])
+    expand_us, attn_phase_us = (float(x) for x in phase.mean(axis=0) * 1e3)
+    log(f"[bench] step {ms_per_step*1e3:.1f} us: expand {expand_us:.1f}, attn {attn_phase_us:.1f}")
+    # The attention kernel alone, back to back over the expanded keys/values
+    # of the last step (the roofline's time).
+    def attn_only(i):
+        q_c, q_r = views(pool[i % n_pool])
+        mla.prefill_attn(q_c, q_r, pool[i % n_pool].cache, k_c, v, cfg.scale, out=out, lse=lse)
+    attn_us = timed(attn_only, args.steps)
+    expand_b2b_us = timed(lambda i: mla.prefill_expand(
+        pool[i % n_pool].cache, pool[i % n_pool].w_uk, pool[i % n_pool].w_uv, k_c=k_c, v=v),
+        args.steps)
+    log(f"[bench] prefill_attn back to back: {attn_us:.1f} us; expand back to back: "
+        f"{expand_b2b_us:.1f} us")
+
+    tokens = sum(pool[i % n_pool].tokens for i in range(args.steps)) / args.steps
+    # Query-key pairs: token j of a request sees len - q_len + j + 1 rows.
+    visible = ql * tokens - B * ql * (ql - 1) / 2
+    attn_flops = 2.0 * nh * (dh + dr + dh) * visible
+    expand_flops = 2.0 * nh * tokens * dc * 2 * dh
+    kv_bytes = 2 * nh * tokens * dh * 2
+    cache_bytes = tokens * (dc + dr) * 2
+    w_bytes = 2 * nh * dh * dc * 2
+    io_bytes = B * ql * nh * (dh + dr + dh) * 2 + B * ql * nh * 4
+    # Step: the cache, weights, queries and outputs once, and the explicit keys
+    # and values written once and read once (the form's own round trip).
+    step_bytes = cache_bytes + w_bytes + io_bytes + 2 * kv_bytes
+    step_flops = attn_flops + expand_flops
+    t_roof_us = max(step_bytes / (HBM_PEAK_GBPS * 1e9),
+                    step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    attn_bytes = kv_bytes + B * cfg.max_len * dr * 2 + io_bytes
+    attn_tflops = attn_flops / (attn_us * 1e-6) / 1e12
+    result = {
+        "metric": f"MLA decode tokens/s and latent-cache HBM GB/s (% roofline), {name}",
+        "value": B * ql / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": name, "batch": B, "seq_len": cfg.max_len,
+            "seq_len_range": [cfg.len_lo, cfg.len_hi], "n_heads": nh, "d_head": dh,
+            "d_latent": dc, "d_rope": dr, "cache": "contiguous", "layers_per_step": 1,
+            "rotating_pool_mb": round(pool_mb), "query_tokens_per_request": ql,
+            "form": "unabsorbed (explicit keys and values)", "parallelism": "single-gpu",
+        },
+        "step_us": percentiles(step_us),
+        "step_roofline_us": t_roof_us,
+        "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
+        "kernels_us": {"prefill_expand": expand_us, "prefill_attn": attn_phase_us,
+                       "prefill_attn_back_to_back": attn_us,
+                       "prefill_expand_back_to_back": expand_b2b_us},
+        "expand_tflops": expand_flops / (expand_b2b_us * 1e-6) / 1e12,
+        "roofline": {
+            "kernel": "prefill_attn_kernel (mla_prefill_attn)",
+            "bound": "mfma",
+            "achieved": attn_tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+            "alg_flops_per_launch": attn_flops,
+            "alg_bytes_per_launch": attn_bytes,
+            "launch_us": attn_us,
+        },
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +365,9 @@ def main():
 
     name = args.workload
     cfg = CONFIGS[name]
+    if cfg.form == "unabsorbed":
+        run_unabsorbed(args, cfg, name)
+        return
     B, nh, row = cfg.batch, cfg.n_heads, cfg.row
     # Query tokens per request: the verification workload decodes the last
     # q_len positions of every request at once; the absorb and the output

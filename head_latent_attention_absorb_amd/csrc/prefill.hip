@@ -14,10 +14,12 @@
 // (d_c + d_h^R) + d_c in the absorbed form (V2 read-through, section 2.3:
 // absorption pays at decode).
 //
-// Kernel: one workgroup per (request, head, block of 128 queries), 4 waves
-// of 32 queries.  Keys and values stream through a two-stage LDS ring in
-// tiles of 64 tokens (k^C 16 KiB, k^R 8 KiB, v 16 KiB), loaded with direct
-// loads.  Both products are computed transposed so that a lane owns one query
+// Kernel: one workgroup per (request, head, block of 256 queries), 8 waves
+// of 32 queries (two per SIMD: one's softmax overlaps the other's products).
+// Keys and values stream through a three-stage LDS ring in tiles of 64 tokens
+// (k^C 16 KiB, k^R 8 KiB, v 16 KiB), loaded with direct loads two tiles
+// ahead: the tiles in flight, not the products, bound the kernel at two
+// stages, and 256 queries per tile halve the bytes per product of 128.  Both products are computed transposed so that a lane owns one query
 // throughout:
 //   S^T = K Q^T   (A: key rows from LDS, B: the wave's queries in registers)
 //   O^T += V^T P^T (A: value columns through the transposing LDS read, B: the
@@ -39,14 +41,18 @@ constexpr int kDh = 128;        // d_h (content and value width)
 constexpr int kDr = 64;         // d_h^R
 constexpr int kDc = 512;        // d_c
 constexpr int kRow = kDc + kDr; // cache row (elements)
-constexpr int kQBlock = 128;    // queries per workgroup
+constexpr int kQT = 1;          // 32-query tiles per wave
+constexpr float kLazy = 8.f;    // log2 headroom before the running max moves
+constexpr int kWaves = 8;
+constexpr int kQBlock = kWaves * 32 * kQT;  // queries per workgroup
+constexpr int kStages = 3;
 constexpr int kTile = 64;       // keys per tile
 constexpr int kKcBytes = kTile * kDh * 2;   // 16 KiB
 constexpr int kKrBytes = kTile * kDr * 2;   // 8 KiB
 constexpr int kVBytes = kTile * kDh * 2;    // 16 KiB
 constexpr int kStageBytes = kKcBytes + kKrBytes + kVBytes;
-constexpr int kLoadsPerWave = kStageBytes / 1024 / 4;  // 1 KiB per wave instruction
-static_assert(kStageBytes % 4096 == 0, "");
+constexpr int kLoadsPerWave = kStageBytes / 1024 / kWaves;  // 1 KiB per wave instruction
+static_assert(kStageBytes % (1024 * kWaves) == 0, "");
 
 struct PrefillParams {
   const __bf16* q_c;     // [B, C, n_h, d_h]
@@ -67,19 +73,27 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Two workgroups per CU (80 KiB of LDS and at most 256 registers per lane
-// each): one's softmax and loads overlap the other's products.
-__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[2 * kStageBytes];
+__global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
-  // Workgroup -> (request, head, query block); the heads of one request and
-  // block are consecutive, so their shared k^R tiles meet in L2 now and then.
-  const int qb = blockIdx.x % p.q_blocks;
-  const int rest = blockIdx.x / p.q_blocks;
-  const int i = rest % p.n_heads;
-  const int b = rest / p.n_heads;
+  // Workgroup -> (request, head, query block).  Workgroup x runs on XCD
+  // x % 8: with (requests x heads) % 8 == 0 the query blocks of one (request,
+  // head) go to one XCD, adjacent in its order, so they share the head's key
+  // and value tiles through that XCD's L2 (and its neighbours there, heads of
+  // the same request, share the k^R tiles).
+  const int n_bh = gridDim.x / p.q_blocks;
+  int qb, bh;
+  if (n_bh % 8 == 0) {
+    bh = (blockIdx.x / (8 * p.q_blocks)) * 8 + (blockIdx.x & 7);
+    qb = (blockIdx.x >> 3) % p.q_blocks;
+  } else {
+    qb = blockIdx.x % p.q_blocks;
+    bh = blockIdx.x / p.q_blocks;
+  }
+  const int i = bh % p.n_heads;
+  const int b = bh / p.n_heads;
   const int len = p.seq_lens[b];
   const int C = p.q_len;
   // Position of query j: len - C + j.  Queries of this workgroup and wave.
@@ -87,27 +101,42 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
   const int q_last = min(C, q_first + kQBlock) - 1;
   const int pos_max = len - C + q_last;                 // workgroup's last position
   const int nt = pos_max < 0 ? 0 : pos_max / kTile + 1;
-  const int qw0 = q_first + wave * 32;
+  const int qw0 = q_first + wave * 32 * kQT;
   // This wave's last position (-1: no query of the chunk in this wave).
-  const int pos_w = qw0 > q_last ? -1 : len - C + min(q_last, qw0 + 31);
-  const int q_idx = qw0 + l32;
-  const bool q_ok = q_idx <= q_last;
-  const int my_pos = q_ok ? len - C + q_idx : -1;
+  const int pos_w = qw0 > q_last ? -1 : len - C + min(q_last, qw0 + 32 * kQT - 1);
 
-  // Queries as B operands: lane (query l32, half) holds d = ks*16 + half*8
-  // .. +7 of [q^C | q^R] for ks < 12.
-  bf16x8_t qf[12];
-  {
+  // Queries as B operands: lane (query qw0 + qt*32 + l32, half) holds d =
+  // ks*16 + half*8 .. +7 of [q^C | q^R] for ks < 12.
+  bf16x8_t qf[kQT][12];
+  int my_pos[kQT];
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    const int q_idx = qw0 + qt * 32 + l32;
+    my_pos[qt] = q_idx <= q_last ? len - C + q_idx : -1;
     const size_t qrow = (static_cast<size_t>(b) * C + min(q_idx, q_last)) * p.n_heads + i;
     const __bf16* qc = p.q_c + qrow * kDh + half * 8;
     const __bf16* qr = p.q_r + qrow * kDr + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qc + ks * 16);
+    for (int ks = 0; ks < 8; ++ks) qf[qt][ks] = *reinterpret_cast<const bf16x8_t*>(qc + ks * 16);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[8 + ks] = *reinterpret_cast<const bf16x8_t*>(qr + ks * 16);
+    for (int ks = 0; ks < 4; ++ks)
+      qf[qt][8 + ks] = *reinterpret_cast<const bf16x8_t*>(qr + ks * 16);
+  }
+  // Wait for the queries here, before any tile load is in flight: the
+  // compiler cannot see the direct loads, and a query load it still counts
+  // as pending inside the loop would make it wait for every outstanding load
+  // (the ring's prefetches included) at each tile.
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));  // vmcnt(0)
+  // A tile needs no mask when all its keys precede the first position of a
+  // query tile whose queries all lie in the chunk.
+  int pos_unmasked[kQT];
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    const int q0 = qw0 + qt * 32;
+    pos_unmasked[qt] = q0 + 31 <= q_last ? len - C + q0 : -1;
   }
 
-  // Tile loads: instruction j of the stage (wave j % 4 issues it) fills
+  // Tile loads: instruction j of the stage (wave j % kWaves issues it) fills
   // 1 KiB: j < 16 the k^C rows (16 units of 16 bytes per 256-byte row, unit
   // c at c ^ (row & 15)), j < 24 the k^R rows (8 units per 128-byte row, unit
   // c at c ^ (row & 7)), else the value rows (16 units per row, unit v at
@@ -122,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
     const unsigned sbase = ring_base + stage * kStageBytes;
 #pragma unroll
     for (int n = 0; n < kLoadsPerWave; ++n) {
-      const int j = wave + n * 4;
+      const int j = wave + n * kWaves;
       const void* src;
       if (j < 16) {
         const int unit = j * 64 + lane, r = unit >> 4, c = unit & 15;
@@ -141,12 +170,19 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
     }
   };
 
-  f32x16_t o[4];
+  f32x16_t o[kQT][4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float m = -INFINITY, l = 0.f;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[qt][db][e] = 0.f;
+  float m[kQT], l[kQT];
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    m[qt] = -INFINITY;
+    l[qt] = 0.f;
+  }
 
   // Value read coordinates (transposing read): lane (G, q) addresses token
   // row k0 + (G/2)*4 + q/4 (+8 for the second half of the fragment) at 8-byte
@@ -156,25 +192,34 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
   const int tr_u = ((G & 1) << 2) + (q16 & 3);
   const int swz = (q16 >> 2) << 3;
 
+  // Ring: tile t in stage t % 3.  Iteration t waits for tile t, and after
+  // the barrier (every wave is past tile t - 1) refills tile t - 1's stage
+  // with tile t + 2.
   if (nt > 0) issue_tile(0, 0);
+  if (nt > 1) issue_tile(1, 1);
   for (int t = 0; t < nt; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < nt) {
-      issue_tile(t + 1, stage ^ 1);
+    const int stage = t % kStages;
+    if (t + 1 < nt)
       wait_vm<kLoadsPerWave>();
-    } else {
+    else
       wait_vm<0>();
-    }
     __syncthreads();
+    if (t + 2 < nt) issue_tile(t + 2, (t + 2) % kStages);
     const uint8_t* st = ring + stage * kStageBytes;
     if (t * kTile <= pos_w) {
-      // S^T for the tile's two 32-token blocks: lane (query l32, half) gets
-      // token tb*32 + (e/4)*8 + half*4 + e%4 in register e.
-      f32x16_t s[2];
+      const i16x4_t* vl = reinterpret_cast<const i16x4_t*>(st + kKcBytes + kKrBytes);
+      // The tile's two 32-token blocks, one online-softmax update each.
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
+        if (t * kTile + tb * 32 > pos_w) break;
+        // S^T for the block and each query tile: lane (query l32, half) gets
+        // token tb*32 + (e/4)*8 + half*4 + e%4 in register e.  Each key
+        // fragment feeds every query tile.
+        f32x16_t s[kQT];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[tb][e] = 0.f;
+        for (int qt = 0; qt < kQT; ++qt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[qt][e] = 0.f;
         const int r = tb * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < 12; ++ks) {
@@ -184,80 +229,97 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
           else
             kf = *reinterpret_cast<const bf16x8_t*>(st + kKcBytes + r * 128 +
                                                     ((((ks - 8) * 2 + half) ^ (r & 7)) << 4));
-          s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[tb], 0, 0, 0);
+#pragma unroll
+          for (int qt = 0; qt < kQT; ++qt)
+            s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qt][ks], s[qt], 0, 0, 0);
         }
-      }
-      // Causal mask, running max and probabilities (base 2).
-      float mx = -INFINITY;
+        // Causal mask (blocks that reach the diagonal), running max and the
+        // probabilities (base 2).
+        bf16x8_t pf[kQT][2];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+        for (int qt = 0; qt < kQT; ++qt) {
+          const int tok0 = t * kTile + tb * 32;
+          const bool masked = tok0 + 31 > pos_unmasked[qt];
+          float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int tok = t * kTile + tb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-          const float x = tok <= my_pos ? s[tb][e] * p.scale_log2 : -INFINITY;
-          s[tb][e] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);  // 0 while m = -inf
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-      bf16x8_t pf[4];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(s[tb][kk * 8 + e] - m_use);
-            l += pe;
-            pf[tb * 2 + kk][e] = static_cast<__bf16>(pe);
+          for (int e = 0; e < 16; ++e) {
+            const int tok = tok0 + (e >> 2) * 8 + half * 4 + (e & 3);
+            float x = s[qt][e] * p.scale_log2;
+            if (masked) x = tok <= my_pos[qt] ? x : -INFINITY;
+            s[qt][e] = x;
+            mx = fmaxf(mx, x);
           }
-      // O^T += V^T P^T over the tile's four 16-token steps.
-      const i16x4_t* vl = reinterpret_cast<const i16x4_t*>(st + kKcBytes + kKrBytes);
+          mx = halves_max(mx);
+          // Lazy rescale: the reference max m (exponent base of l and o)
+          // moves only when a score exceeds it by more than kLazy (so every
+          // probability stays below 2^kLazy), and the accumulators are
+          // rescaled only when some lane's reference moved.
+          const bool move = mx > m[qt] + kLazy;
+          if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            const float m_new = move ? mx : m[qt];
+            const float alpha = move ? __builtin_amdgcn_exp2f(m[qt] - m_new) : 1.f;  // 0 from -inf
+            m[qt] = m_new;
+            l[qt] *= alpha;
 #pragma unroll
-      for (int kstep = 0; kstep < 4; ++kstep) {
-        const int k0 = kstep * 16;
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int un = ((db * 8) + tr_u) ^ swz;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (MLA_LDS i16x4_t*)(vl + (k0 + tr_k) * 32 + un));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (MLA_LDS i16x4_t*)(vl + (k0 + 8 + tr_k) * 32 + un));
-          const bf16x8_t vf = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kstep], o[db], 0, 0, 0);
+              for (int e = 0; e < 16; ++e) o[qt][db][e] *= alpha;
+          }
+          const float m_use = m[qt] == -INFINITY ? 0.f : m[qt];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float pe = __builtin_amdgcn_exp2f(s[qt][kk * 8 + e] - m_use);
+              l[qt] += pe;
+              pf[qt][kk][e] = static_cast<__bf16>(pe);
+            }
+        }
+        // O^T += V^T P^T over the block's two 16-token steps; each value
+        // fragment feeds every query tile.
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int k0 = tb * 32 + kk * 16;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int un = ((db * 8) + tr_u) ^ swz;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (MLA_LDS i16x4_t*)(vl + (k0 + tr_k) * 32 + un));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (MLA_LDS i16x4_t*)(vl + (k0 + 8 + tr_k) * 32 + un));
+            const bf16x8_t vf = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int qt = 0; qt < kQT; ++qt)
+              o[qt][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qt][kk], o[qt][db], 0, 0, 0);
+          }
         }
       }
     }
-    __syncthreads();
   }
 
   // Both halves saw half of every tile's tokens.
-  l = halves_sum(l);
-  if (!q_ok) return;
-  const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  const size_t orow = (static_cast<size_t>(b) * C + q_idx) * p.n_heads + i;
-  // Register e of block db: d = db*32 + (e/4)*8 + half*4 + e%4.
-  __bf16* dst = p.out + orow * kDh + half * 4;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int qt = 0; qt < kQT; ++qt) {
+    const float lt = halves_sum(l[qt]);
+    const int q_idx = qw0 + qt * 32 + l32;
+    if (q_idx > q_last) continue;
+    const float inv_l = lt > 0.f ? 1.f / lt : 0.f;
+    const size_t orow = (static_cast<size_t>(b) * C + q_idx) * p.n_heads + i;
+    // Register e of block db: d = db*32 + (e/4)*8 + half*4 + e%4.
+    __bf16* dst = p.out + orow * kDh + half * 4;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4_t v4;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(o[db][g * 4 + e] * inv_l);
-      *reinterpret_cast<bf16x4_t*>(dst + db * 32 + g * 8) = v4;
-    }
-  if (p.lse != nullptr && half == 0)
-    p.lse[orow] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(o[qt][db][g * 4 + e] * inv_l);
+        *reinterpret_cast<bf16x4_t*>(dst + db * 32 + g * 8) = v4;
+      }
+    if (p.lse != nullptr && half == 0)
+      p.lse[orow] = lt > 0.f ? (m[qt] + __log2f(lt)) * kLn2 : -INFINITY;
+  }
 }
 
 }  // namespace
@@ -287,7 +349,7 @@ hipError_t launch_prefill_attn(int batch, int q_len, int n_heads, const CacheVie
   p.scale_log2 = softmax_scale * kLog2e;
   const long long grid = static_cast<long long>(batch) * n_heads * p.q_blocks;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  prefill_attn_kernel<<<static_cast<unsigned>(grid), 256, 0, stream>>>(p);
+  prefill_attn_kernel<<<static_cast<unsigned>(grid), kWaves * 64, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -66,11 +66,14 @@ def test_expand_keys_and_values():
         assert (k_np[b, :, n:] == 7.0).all() and (v_np[b, :, n:] == 7.0).all()
 
 
-@pytest.mark.parametrize("q_len,lens", [(150, (300, 100)), (64, (64, 1000)), (1, (5, 129))],
-                         ids=["ragged_block_short_history", "one_block", "one_token"])
+@pytest.mark.parametrize("q_len,lens", [(150, (300, 100)), (300, (700, 290)), (64, (64, 1000)),
+                                        (1, (5, 129))],
+                         ids=["ragged_block_short_history", "two_blocks", "one_block",
+                              "one_token"])
 def test_prefill_attention(q_len, lens):
-    """Ragged query blocks (150 = 128 + 22), a request shorter than the chunk
-    (its first 50 tokens see nothing), tiles cut by the length."""
+    """Ragged query blocks (150 queries: waves with part of a tile, a wave
+    with none; 300 = 256 + 44), requests shorter than the chunk (their first
+    tokens see nothing), tiles cut by the length."""
     cfg = DSV2.replace(batch=2, len_lo=1, len_hi=1024, max_len=1024, q_len=q_len)
     case = make_case(cfg, 72 + q_len, seq_lens=np.array(lens, np.int32))
     _log(f"[prefill attn] q_len={q_len} lens={lens}")

@@ -77,6 +77,9 @@ class WorkloadConfig:
     d_model: int = 0         # hidden width d of the cache append; 0 => n_heads * d_head
     q_len: int = 1           # query tokens per request (several: speculative verification)
     cache_format: str = "native"  # "fp8": E4M3 rows with one fp32 scale per row
+    # "unabsorbed": the chunk runs with explicit keys and values (benchmark only;
+    # the drawn inputs are the same)
+    form: str = "absorbed"
 
     @property
     def row(self) -> int:
@@ -134,6 +137,10 @@ CONFIGS: Dict[str, WorkloadConfig] = {
     "prefill_c512_b4_t4096": WorkloadConfig("prefill_c512_b4_t4096", batch=4, dtype="bf16",
                                             len_lo=4096, len_hi=4096, max_len=4096,
                                             q_len=512, **_DSV2),
+    # The same chunk in the unabsorbed form (explicit keys and values).
+    "prefill_unabsorbed_c512_b4_t4096": WorkloadConfig(
+        "prefill_unabsorbed_c512_b4_t4096", batch=4, dtype="bf16", len_lo=4096, len_hi=4096,
+        max_len=4096, q_len=512, form="unabsorbed", **_DSV2),
     # The default shape over the low-bit cache: the same drawn rows, quantised
     # to E4M3 with one scale per row.
     "fp8_b16_t4096": WorkloadConfig("fp8_b16_t4096", batch=16, dtype="bf16",
