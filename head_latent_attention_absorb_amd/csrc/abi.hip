@@ -348,7 +348,7 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* 
   (void)hipGetLastError();
   // One split per request: the MFMA kernel normalises its rows itself and
   // writes o_lat and lse, so there is nothing to merge.
-  a.direct = p.kernel == 1 && p.num_splits == 1;
+  a.direct = p.kernel == 1 && p.num_splits == 1 && cache->row_format == MLA_ROWS_NATIVE;
   if ((st = run_partials(a, p)) != MLA_OK || a.direct) return st;
   return run_combine(a, p);
 }

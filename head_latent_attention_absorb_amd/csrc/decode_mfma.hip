@@ -237,7 +237,10 @@ __device__ __forceinline__ int swz(int n, int chunk) {
   return (((chunk >> 3) * kTile + n) << 7) + (((chunk & 7) ^ swz_key(n)) << 4);
 }
 
-template <bool kPaged, bool kFp8>
+// kDirect: one split, the rows are normalised and written to out_lat (with
+// lse) instead of partials; a separate instantiation keeps that epilogue out
+// of the split kernels.
+template <bool kPaged, bool kFp8, bool kDirect>
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   // Low-bit rows: the scales of the tile in each ring stage.
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   if (t0 >= t1) {
     // The combine never reads partitions past the length.  Written directly,
     // a row with nothing visible is o = 0, lse = -inf.
-    if (p.out_lat != nullptr) {
+    if constexpr (kDirect) {
       uint16_t* z = p.out_lat + (static_cast<size_t>(b) * p.n_rows + hblock * 32) * 512 + lane * 8;
       bf16x8_t zero;
 #pragma unroll
@@ -804,8 +807,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   static_assert(4 * 32 * kOutStride <= kLdsBytes, "epilogue rows fit in the ring");
   __syncthreads();
   uint8_t* rows = lds + wave * 32 * kOutStride;
-  const bool direct = p.out_lat != nullptr;
-  if (direct) {
+  if constexpr (kDirect) {
     // Written directly (one split): each lane's row is its head's, divided
     // by that head's softmax sum.
     const float inv_l = 1.f / l;
@@ -832,7 +834,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // Split-minor layout: the S partial rows of one (request, row) are
   // contiguous, so the combine reads each merge as one run.  With one split
   // that is also the layout of out_lat.
-  uint16_t* dst = (direct ? p.out_lat : p.part_o) +
+  uint16_t* dst = (kDirect ? p.out_lat : p.part_o) +
                   ((static_cast<size_t>(b) * p.n_rows + hblock * 32) * p.num_splits + s) * 512 +
                   lane * 8;
   const size_t row_stride = static_cast<size_t>(p.num_splits) * 512;
@@ -843,7 +845,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   for (int r = 0; r < 32; ++r)
     *reinterpret_cast<bf16x8_t*>(dst + r * row_stride) =
         *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
-  if (direct) {
+  if constexpr (kDirect) {
     if (p.lse_out != nullptr && half == 0)
       p.lse_out[static_cast<size_t>(b) * p.n_rows + head] = (m + __log2f(l)) * kLn2;
   } else if (half == 0) {
@@ -873,17 +875,14 @@ hipError_t launch_partials_mfma(const DecodeArgs& a) {
   p.out_lat = a.direct ? static_cast<uint16_t*>(a.out_lat) : nullptr;
   p.lse_out = a.direct ? a.lse : nullptr;
   const int grid = (p.work_items + 7) / 8 * 8;  // multiple of the 8 XCDs
-  if (a.cache.page_table != nullptr) {
-    if (a.cache.fp8)
-      decode_mfma_kernel<true, true><<<grid, 256, 0, a.stream>>>(p);
-    else
-      decode_mfma_kernel<true, false><<<grid, 256, 0, a.stream>>>(p);
-  } else {
-    if (a.cache.fp8)
-      decode_mfma_kernel<false, true><<<grid, 256, 0, a.stream>>>(p);
-    else
-      decode_mfma_kernel<false, false><<<grid, 256, 0, a.stream>>>(p);
-  }
+  const bool paged = a.cache.page_table != nullptr, fp8 = a.cache.fp8 != 0;
+  // The direct form exists for bf16 rows only (the low-bit one would spill).
+  if (a.direct && fp8) return hipErrorInvalidValue;
+  const auto kernel =
+      a.direct ? (paged ? decode_mfma_kernel<true, false, true> : decode_mfma_kernel<false, false, true>)
+               : (paged ? (fp8 ? decode_mfma_kernel<true, true, false> : decode_mfma_kernel<true, false, false>)
+                        : (fp8 ? decode_mfma_kernel<false, true, false> : decode_mfma_kernel<false, false, false>));
+  kernel<<<grid, 256, 0, a.stream>>>(p);
   return hipGetLastError();
 }
 

@@ -178,7 +178,8 @@ mla_status_t mla_decode_plan_mq(const mla_dims_t* dims, int32_t batch, int32_t q
  * batch and cache bounds.  workspace: device, >= plan->workspace_bytes, 256-byte
  * aligned, contents need no initialisation; calls that share a workspace
  * must be ordered on one stream.  With a one-split plan on the MFMA kernel
- * (plan->num_splits == 1, plan->kernel == 1) the decode kernel normalises its
+ * (plan->num_splits == 1, plan->kernel == 1) over native rows the decode kernel
+ * normalises its
  * rows and writes out_lat and lse itself: nothing is merged and the workspace
  * is not touched. */
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* q_cat,

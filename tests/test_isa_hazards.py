@@ -189,7 +189,7 @@ def kernels():
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     ks = parse_kernels(r.stdout)
-    assert len(ks) == 4, sorted(ks)  # contiguous / paged x bf16 / low-bit rows
+    assert len(ks) == 6, sorted(ks)  # contiguous / paged x (bf16 / low-bit rows, split) + bf16 direct
     return ks
 
 
