@@ -359,8 +359,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(one GPU holds the whole batch; see the project notes on sharding). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     name = args.workload

@@ -794,7 +794,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
 
   // Softmax sum over both lane halves (each half saw half of the tokens).
   l = halves_sum(l);
-  // bf16 partial, row-major per (request, split, head):
+  // bf16 partial, split-minor per (request, row, split):
   // part_o[((b * n_rows + row) * S + s) * 512 + c], written as accumulated
   // (relative to the running max m, not divided by l: the combine applies
   // both factors as one weight, which saves a multiply per element here).

@@ -17,7 +17,7 @@ request, in the pages' order:
   4. The row [c^KV | k^R] is what is cached (V3 read-through section 2.2,
      cache.append((c_kv, k_r)); section 2.4).
 
-Readings where the pages are silent (also listed in the design doc):
+Readings where the pages are silent:
   * RMSNorm is x / sqrt(mean(x^2) + eps) * gamma with a caller-given gamma and
     eps; the pages give neither.
   * RoPE rotates consecutive pairs (x[2i], x[2i+1]) by the angle pos * f_i
