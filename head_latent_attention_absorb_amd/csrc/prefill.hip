@@ -73,6 +73,10 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// kPosScale (softmax scale > 0): the max is taken over the raw scores and the
+// scale is folded into the exponent's fused multiply-add, saving a multiply
+// per score.
+template <bool kPosScale>
 __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
 
@@ -244,12 +248,13 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int tok = tok0 + (e >> 2) * 8 + half * 4 + (e & 3);
-            float x = s[qt][e] * p.scale_log2;
+            float x = kPosScale ? s[qt][e] : s[qt][e] * p.scale_log2;
             if (masked) x = tok <= my_pos[qt] ? x : -INFINITY;
             s[qt][e] = x;
             mx = fmaxf(mx, x);
           }
           mx = halves_max(mx);
+          if constexpr (kPosScale) mx *= p.scale_log2;  // -inf stays -inf
           // Lazy rescale: the reference max m (exponent base of l and o)
           // moves only when a score exceeds it by more than kLazy (so every
           // probability stays below 2^kLazy), and the accumulators are
@@ -270,7 +275,9 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
           for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float pe = __builtin_amdgcn_exp2f(s[qt][kk * 8 + e] - m_use);
+              const float pe = __builtin_amdgcn_exp2f(
+                  kPosScale ? fmaf(s[qt][kk * 8 + e], p.scale_log2, -m_use)
+                            : s[qt][kk * 8 + e] - m_use);
               l[qt] += pe;
               pf[qt][kk][e] = static_cast<__bf16>(pe);
             }
@@ -349,7 +356,10 @@ hipError_t launch_prefill_attn(int batch, int q_len, int n_heads, const CacheVie
   p.scale_log2 = softmax_scale * kLog2e;
   const long long grid = static_cast<long long>(batch) * n_heads * p.q_blocks;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  prefill_attn_kernel<<<static_cast<unsigned>(grid), kWaves * 64, 0, stream>>>(p);
+  if (p.scale_log2 > 0.f)
+    prefill_attn_kernel<true><<<static_cast<unsigned>(grid), kWaves * 64, 0, stream>>>(p);
+  else
+    prefill_attn_kernel<false><<<static_cast<unsigned>(grid), kWaves * 64, 0, stream>>>(p);
   return hipGetLastError();
 }
 

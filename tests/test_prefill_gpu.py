@@ -131,3 +131,25 @@ def test_prefill_c512_b4_t4096_sampled():
     o_ref, lse_ref = _reference(case, heads)
     assert_close(from_dev(out)[:, :, heads], o_ref[:, :, heads], "bf16", "o")
     assert_close(from_dev(lse)[:, :, heads], lse_ref[:, :, heads], "bf16", "lse")
+
+
+@pytest.mark.parametrize("scale", [-0.0722, 0.0], ids=["negative", "zero"])
+def test_prefill_scale_sign_and_zero(scale):
+    """The kernel folds a positive scale into the exponent; a negative or zero
+    scale takes the plain path."""
+    q_len = 80
+    cfg = DSV2.replace(batch=1, len_lo=1, len_hi=400, max_len=400, q_len=q_len)
+    case = make_case(cfg, 91, seq_lens=np.array([400], np.int32))
+    dc = DevCase(case)
+    q_c = dc.q_c.view(1, q_len, cfg.n_heads, cfg.d_head)
+    q_r = dc.q_r.view(1, q_len, cfg.n_heads, cfg.d_rope)
+    k_c, v = mla.prefill_expand(dc.cache, dc.w_uk, dc.w_uv)
+    out, lse = mla.prefill_attn(q_c, q_r, dc.cache, k_c, v, scale)
+    torch.cuda.synchronize()
+    heads = [0, 64, 127]
+    rows = oracle.gather_rows(case.cache, 0, 400)
+    o_ref, lse_ref = oracle.mla_prefill_reference(
+        case.q_c[0], case.q_r[0], rows[:, :cfg.d_latent], rows[:, cfg.d_latent:], case.w_uk,
+        case.w_uv, scale, heads=heads)
+    assert_close(from_dev(out)[0][:, heads], o_ref[:, heads], "bf16", "o")
+    assert_close(from_dev(lse)[0][:, heads], lse_ref[:, heads], "bf16", "lse")
