@@ -316,6 +316,8 @@ def run_unabsorbed(args, cfg, name):
             "form": "unabsorbed (explicit keys and values)", "parallelism": "single-gpu",
         },
         "step_us": percentiles(step_us),
+        "launch": "hip graph per step (three kernels)" if graphs is not None else "eager calls",
+        "eager_ms_per_step": eager_ms,
         "step_roofline_us": t_roof_us,
         "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
         "kernels_us": {"prefill_expand": expand_us, "prefill_attn": attn_phase_us,
@@ -349,6 +351,8 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests in the CPU oracle sample (0 skips it; default workload only)")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a HIP graph instead of plain calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device copies (a known-size kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -430,7 +434,16 @@ def main():
     def entries(i):
         return pool if layered else [pool[i % n_pool]]
 
+    # --graph: single-layer workloads replay each pool entry's step from a HIP
+    # graph (captured once, after the warmup).  Measured slower than plain
+    # calls on MI355X (54.5 vs 53.1 us at B=16): the gaps between the three
+    # dependent kernels are on the GPU side, so plain calls are the default.
+    graphs = None
+
     def step(i):
+        if graphs is not None:
+            graphs[i % n_pool].replay()
+            return
         for e in entries(i):
             layer(e)
 
@@ -448,6 +461,20 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    eager_ms = None
+    if not layered and args.graph:
+        eager_ms = timed(step, args.steps) / 1e3
+        graphs = []
+        for e in pool:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layer(e)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        log(f"[bench] eager step {eager_ms*1e3:.1f} us; timing graph replays")
 
     # Timed region: exactly --steps whole steps, between device synchronisations.
     e_start = torch.cuda.Event(enable_timing=True)
