@@ -316,8 +316,6 @@ def run_unabsorbed(args, cfg, name):
             "form": "unabsorbed (explicit keys and values)", "parallelism": "single-gpu",
         },
         "step_us": percentiles(step_us),
-        "launch": "hip graph per step (three kernels)" if graphs is not None else "eager calls",
-        "eager_ms_per_step": eager_ms,
         "step_roofline_us": t_roof_us,
         "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
         "kernels_us": {"prefill_expand": expand_us, "prefill_attn": attn_phase_us,
@@ -618,6 +616,8 @@ def main():
             "parallelism": "single-gpu",
         },
         "step_us": percentiles(step_us),
+        "launch": "hip graph per step (three kernels)" if graphs is not None else "eager calls",
+        "eager_ms_per_step": eager_ms,
         "step_roofline_us": t_roof_us,
         "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
         "attn": {
