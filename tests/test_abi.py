@@ -201,3 +201,37 @@ def test_generic_and_mfma_plans_selected_by_dims():
     assert mla.decode_plan(128, 512, 64, torch.bfloat16, cache).kernel == 1
     assert mla.decode_plan(96, 512, 64, torch.bfloat16, cache).kernel == 0
     assert mla.decode_plan(128, 512, 64, torch.bfloat16, cache, split_tokens=33).split_tokens == 64
+
+
+def test_prefill_host_checks():
+    """mla_prefill_expand / mla_prefill_attn reject bad arguments on the host
+    (before any device query), and report the missing device last."""
+    L = mla.lib()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    d = ctypes.byref(_dims())
+    cache = mla.CacheDesc(0x1000, 0x2000, None, 0, 64, 0)
+    c = ctypes.byref(cache)
+    E = L.mla_prefill_expand
+    assert E(None, 1, c, fake, fake, fake, fake, None) == 1
+    assert E(ctypes.byref(_dims(d_head=64)), 1, c, fake, fake, fake, fake, None) == 2
+    assert E(ctypes.byref(_dims(dtype=mla.MLA_F32)), 1, c, fake, fake, fake, fake, None) == 3
+    paged = mla.CacheDesc(0x1000, 0x2000, 0x3000, 16, 64, 4)
+    assert E(d, 1, ctypes.byref(paged), fake, fake, fake, fake, None) == 2
+    fp8 = mla.CacheDesc(0x1000, 0x2000, None, 0, 64, 0)
+    fp8.scales = 0x4000
+    fp8.row_format = mla.MLA_ROWS_FP8
+    assert E(d, 1, ctypes.byref(fp8), fake, fake, fake, fake, None) == 3
+    assert E(d, -1, c, fake, fake, fake, fake, None) == 2
+    assert E(d, 0, c, None, None, None, None, None) == 0
+    assert E(d, 1, c, None, fake, fake, fake, None) == 1
+    assert E(d, 1, c, fake, fake, odd, fake, None) == 5
+    assert E(d, 1, c, fake, fake, fake, fake, None) == 7
+    A = L.mla_prefill_attn
+    args = (fake, fake, c, fake, fake, ctypes.c_float(0.07), fake)
+    assert A(d, 1, 0, *args, None, None) == 2        # q_len 0
+    assert A(d, 1, 65, *args, None, None) == 2       # q_len past max_len
+    assert A(d, 0, 8, *args, None, None) == 0
+    assert A(d, 1, 8, None, fake, c, fake, fake, ctypes.c_float(0.07), fake, None, None) == 1
+    assert A(d, 1, 8, *args, ctypes.c_void_p(0x1002), None) == 5   # lse not 4-byte aligned
+    assert A(d, 1, 8, *args, None, None) == 7

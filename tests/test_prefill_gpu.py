@@ -153,3 +153,22 @@ def test_prefill_scale_sign_and_zero(scale):
         case.w_uv, scale, heads=heads)
     assert_close(from_dev(out)[0][:, heads], o_ref[:, heads], "bf16", "o")
     assert_close(from_dev(lse)[0][:, heads], lse_ref[:, heads], "bf16", "lse")
+
+
+def test_prefill_long_chunk_1024():
+    """A 1024-token chunk (four query blocks) over 2048 rows, the longest
+    chunk the absorbed plan takes, every token of sampled heads."""
+    q_len = 1024
+    cfg = DSV2.replace(batch=1, len_lo=1, len_hi=2048, max_len=2048, q_len=q_len)
+    case = make_case(cfg, 93, seq_lens=np.array([2048], np.int32))
+    _log("[prefill attn] 1024-token chunk")
+    dc = DevCase(case)
+    k_c, v = mla.prefill_expand(dc.cache, dc.w_uk, dc.w_uv)
+    out, lse = mla.prefill_attn(dc.q_c.view(1, q_len, cfg.n_heads, cfg.d_head),
+                                dc.q_r.view(1, q_len, cfg.n_heads, cfg.d_rope), dc.cache, k_c, v,
+                                cfg.scale)
+    torch.cuda.synchronize()
+    heads = [5, 100]
+    o_ref, lse_ref = _reference(case, heads)
+    assert_close(from_dev(out)[:, :, heads], o_ref[:, :, heads], "bf16", "o")
+    assert_close(from_dev(lse)[:, :, heads], lse_ref[:, :, heads], "bf16", "lse")
