@@ -2,18 +2,18 @@
 """Benchmark: MLA absorbed decode on one MI355X (default: DeepSeek-V2 shape B=16, T=4096).
 
 A step is one whole decode step of one layer on one batch of synthetic input:
-    mla_absorb_q -> mla_decode_partials -> mla_decode_combine_out
-(the last merges the split partials and applies W^UV in one kernel; it does
-exactly what mla_decode_combine followed by mla_out_uv does).  For the
+    mla_absorb_q -> mla_decode_attn -> mla_out_uv
+(mla_decode_attn is one launch whenever its workgroups all fit on the device:
+the split partitions merge each other's partials inside the decode kernel).  For the
 60-layer workload a step is the 60 layers back to back, each with its own
 weights and cache.  Inputs are resident in HBM before the timed region.  A
 single-layer step uses the next entry of a rotating pool of independently
 seeded (cache, W^UK, W^UV, q) sets totalling > 512 MB, twice the 256 MB
 Infinity Cache, so the cache bytes really come from HBM.
 
-Beside the step, the attention alone (mla_decode_partials followed by
-mla_decode_combine, i.e. mla_decode_attn) is timed back to back over the same
-inputs and set against its roofline.
+Beside the step, the attention alone (mla_decode_attn) is timed back to back
+over the same inputs and set against its roofline, and so is its two-phase
+form (mla_decode_partials followed by mla_decode_combine) for comparison.
 
 Prints ONE JSON line on stdout (everything else goes to stderr).
 """
@@ -139,34 +139,52 @@ def traffic_from_counters(sha: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(entry: Entry, cfg, n_requests: int, min_seconds: float = 10.0):
-    """The oracle (unabsorbed, fp64) on a bounded sample of the same workload."""
+def cpu_baseline(entry: Entry, cfg, n_requests: int, min_seconds: float = 8.0):
+    """The oracle on a bounded sample of the same workload, on the host cores:
+    its absorbed form in fp32 (the method itself on the CPU: absorb, latent
+    attention, W^UV, numpy BLAS) as the reported value, and beside it the same
+    absorbed form in fp64 and the unabsorbed fp64 form that parity is graded
+    against.  Each leg repeats whole passes over the sample until min_seconds
+    have elapsed."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        blas_threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        blas_threads = None
     case = entry.case
     reqs = list(range(n_requests))
-    # Whole passes over the sample until at least min_seconds have elapsed.
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.mla_decode_reference(case.q_c, case.q_r, case.cache, case.seq_lens, case.w_uk,
-                                    case.w_uv, cfg.scale, requests=reqs)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
+    args = (case.q_c, case.q_r, case.cache, case.seq_lens, case.w_uk, case.w_uv, cfg.scale)
+
+    def leg(fn):
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            fn()
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                return passes * n_requests / dt, passes, dt
+
+    kw = dict(page_table=case.page_table, page_size=cfg.page_size, requests=reqs)
+    v32, p32, t32 = leg(lambda: oracle.mla_decode_absorbed(*args, dtype=np.float32, **kw))
+    v64a, p64a, t64a = leg(lambda: oracle.mla_decode_absorbed(*args, **kw))
+    v64u, p64u, t64u = leg(lambda: oracle.mla_decode_reference(
+        *args, case.page_table, cfg.page_size, requests=reqs))
     return {
-        "value": passes * n_requests / dt,
+        "value": v32,
         "unit": "tokens/s",
-        "cores": int(threads),
+        "cores": int(blas_threads or os.cpu_count()),
         "kind": "oracle",
-        "sample": (f"unabsorbed fp64 oracle, {n_requests} of {cfg.batch} requests x all "
-                   f"{cfg.n_heads} heads x T={cfg.max_len}, one layer, {passes} passes; "
-                   f"{dt:.2f} s"),
+        "sample": (f"absorbed oracle in fp32 (numpy BLAS), {n_requests} of {cfg.batch} "
+                   f"requests x all {cfg.n_heads} heads x T={cfg.max_len}, one layer, "
+                   f"{p32} passes in {t32:.2f} s"),
+        "cpu_count": os.cpu_count(),
+        "blas_threads": blas_threads,
+        "absorbed_fp64_tokens_per_s": v64a,
+        "unabsorbed_fp64_tokens_per_s": v64u,
+        "legs": (f"absorbed fp64: {p64a} passes in {t64a:.2f} s; unabsorbed fp64 (the parity "
+                 f"reference): {p64u} passes in {t64u:.2f} s"),
     }
 
 
@@ -404,6 +422,15 @@ def main():
     o = torch.empty(lead + (nh, cfg.d_head), dtype=torch.bfloat16, device=dev)
     q_rows = q_cat.view(B * ql, nh, row)
     direct = plan.num_splits == 1
+    # mla_decode_attn runs as one launch when its workgroups all fit on the
+    # device (one split: the decode kernel writes o_lat itself; several: the
+    # splits merge each other's partials in the same launch), else as the
+    # partials kernel followed by the combine kernel.
+    grid = -(-B * plan.num_splits * plan.head_groups // 8) * 8
+    one_launch = direct or grid <= torch.cuda.get_device_properties(0).multi_processor_count
+    attn_form = ("one launch, one split: the decode kernel writes o_lat and lse" if direct else
+                 "one launch: split partials merged inside the decode kernel" if one_launch else
+                 "decode partials kernel + split combine kernel")
     stream = torch.cuda.current_stream()
 
     def layer(e: Entry, ev=None):
@@ -413,19 +440,11 @@ def main():
                      e.w_uk, out=q_rows)
         if ev is not None:
             ev[1].record(stream)
-        if direct:
-            # One split per request: mla_decode_attn's decode kernel writes
-            # o_lat and lse itself, then the per-head W^UV product.
-            mla.decode_attn(q_cat, e.cache, cfg.scale, plan, o_lat, lse, ws)
-            if ev is not None:
-                ev[2].record(stream)
-            mla.out_uv(o_lat.view(B * ql, nh, cfg.d_latent), e.w_uv,
-                       out=o.view(B * ql, nh, cfg.d_head))
-        else:
-            mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
-            if ev is not None:
-                ev[2].record(stream)
-            mla.decode_combine_out(e.cache, plan, ws, e.w_uv, o_lat, lse, out=o)
+        mla.decode_attn(q_cat, e.cache, cfg.scale, plan, o_lat, lse, ws)
+        if ev is not None:
+            ev[2].record(stream)
+        mla.out_uv(o_lat.view(B * ql, nh, cfg.d_latent), e.w_uv,
+                   out=o.view(B * ql, nh, cfg.d_head))
         if ev is not None:
             ev[3].record(stream)
 
@@ -513,44 +532,40 @@ def main():
             layer(e, evs[i][1:])
         torch.cuda.synchronize()
         phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(4)] for ev in evs])
-        append_us, absorb_us, partials_us, tail_us = (float(x) for x in phase.mean(axis=0) * 1e3)
-        if direct:
-            kernels_us = {"absorb_q": absorb_us, "decode_attn_direct": partials_us,
-                          "out_uv": tail_us, "cache_append": append_us}
-        else:
-            kernels_us = {"absorb_q": absorb_us, "decode_partials": partials_us,
-                          "decode_combine_out": tail_us, "cache_append": append_us}
+        append_us, absorb_us, attn_ph_us, tail_us = (float(x) for x in phase.mean(axis=0) * 1e3)
+        kernels_us = {"absorb_q": absorb_us, "decode_attn": attn_ph_us, "out_uv": tail_us,
+                      "cache_append": append_us}
         log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, "
-            f"{'decode (direct)' if direct else 'partials'} {partials_us:.1f}, "
-            f"{'out_uv' if direct else 'combine+out_uv'} {tail_us:.1f}")
+            f"decode_attn {attn_ph_us:.1f}, out_uv {tail_us:.1f}")
     else:
         log(f"[bench] step ({cfg.layers} layers) {ms_per_step*1e3:.1f} us")
 
-    # The decode kernel alone, launched back to back on the same stream over
-    # the same inputs: its average launch duration, free of the event records
-    # that split the phases above.  This is the roofline's time.
-    # With one split the kernel runs in the form that writes o_lat directly
-    # (through mla_decode_attn, which then launches nothing else).
+    # mla_decode_attn alone, back to back on the same stream over the same
+    # inputs: its average duration per layer, free of the event records that
+    # split the phases above.  In its one-launch form this is the decode
+    # kernel's own launch duration, the roofline's time.
     n_dec = args.steps * (cfg.layers if layered else 1)
-    if direct:
-        decode_us = timed(lambda i: mla.decode_attn(
-            q_cat, pool[i % n_pool].cache, cfg.scale, plan, o_lat, lse, ws), n_dec)
-    else:
-        decode_us = timed(lambda i: mla.decode_partials(
-            q_cat, pool[i % n_pool].cache, cfg.scale, plan, ws), n_dec)
-    log(f"[bench] decode kernel back to back: {decode_us:.1f} us per launch")
+    decode_us = timed(lambda i: mla.decode_attn(
+        q_cat, pool[i % n_pool].cache, cfg.scale, plan, o_lat, lse, ws), n_dec)
+    log(f"[bench] mla_decode_attn back to back: {decode_us:.1f} us per launch ({attn_form})")
+    attn_us = decode_us * (cfg.layers if layered else 1)
+    # For comparison, the two-phase form of the same call (the partials
+    # kernel, then the separate combine kernel), and the partials kernel alone.
+    two_phase = {}
+    if not direct:
+        ws2 = mla.workspace_for(plan, dev)
 
-    # mla_decode_attn (partials + split combine, or the direct form), back to
-    # back, per step.
-    def attn(i):
-        for e in entries(i):
-            if direct:
-                mla.decode_attn(q_cat, e.cache, cfg.scale, plan, o_lat, lse, ws)
-            else:
-                mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
-                mla.decode_combine(e.cache, nh, plan, ws, o_lat, lse)
-    attn_us = timed(attn, args.steps)
-    log(f"[bench] mla_decode_attn back to back: {attn_us:.1f} us per step")
+        def two(i):
+            e = pool[i % n_pool]
+            mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws2)
+            mla.decode_combine(e.cache, nh, plan, ws2, o_lat, lse)
+        two_phase = {
+            "partials_us": timed(lambda i: mla.decode_partials(
+                q_cat, pool[i % n_pool].cache, cfg.scale, plan, ws2), n_dec),
+            "partials_plus_combine_us": timed(two, n_dec),
+        }
+        log(f"[bench] two-phase form: partials {two_phase['partials_us']:.1f} us, "
+            f"+ combine {two_phase['partials_plus_combine_us']:.1f} us")
 
     # Algorithmic work per step (split partials excluded), averaged over the
     # entries the timed steps used.
@@ -570,7 +585,10 @@ def main():
     attn_bytes = cache_bytes + q_bytes + olat_bytes
     t_roof_attn_us = max(attn_bytes / (HBM_PEAK_GBPS * 1e9),
                          flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
-    k2_bytes = (cache_bytes + q_bytes) / layers_per_step
+    # The dominant kernel's algorithmic bytes: in the one-launch form it reads
+    # the cache and the query and writes o_lat and lse; the partials kernel
+    # of the two-phase form writes only (non-algorithmic) partials.
+    k2_bytes = (attn_bytes if one_launch else cache_bytes + q_bytes) / layers_per_step
     k2_gbps = k2_bytes / (decode_us * 1e-6) / 1e9
     k2_tflops = flops / layers_per_step / (decode_us * 1e-6) / 1e12
     # The decode kernel's bound: HBM, unless its products take longer at the
@@ -621,9 +639,7 @@ def main():
         "step_roofline_us": t_roof_us,
         "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
         "attn": {
-            "what": ("mla_decode_attn, one split: the decode kernel writes o_lat and lse "
-                     "directly" if direct else
-                     "mla_decode_attn = decode partials + split combine, back to back"),
+            "what": f"mla_decode_attn back to back ({attn_form})",
             "us_per_step": attn_us,
             "roofline_us": t_roof_attn_us,
             "pct_roofline": 100.0 * t_roof_attn_us / attn_us,
@@ -632,9 +648,10 @@ def main():
         },
         "latent_cache_GBps": cache_bytes / layers_per_step / (decode_us * 1e-6) / 1e9,
         "tokens_per_layer": tokens_layer,
-        "kernels_us": dict(kernels_us, decode_partials_back_to_back=decode_us),
+        "kernels_us": dict(kernels_us, decode_attn_back_to_back=decode_us,
+                           **{f"two_phase_{k}": v for k, v in two_phase.items()}),
         "roofline": {
-            "kernel": ("decode_mfma_kernel (mla_decode_attn, one split, direct output)" if direct
+            "kernel": (f"decode_mfma_kernel (mla_decode_attn, {attn_form})" if one_launch
                        else "decode_mfma_kernel (mla_decode_partials)"),
             "bound": "mfma" if k2_mfma_bound else "hbm",
             "achieved": k2_tflops if k2_mfma_bound else k2_gbps,

@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_plan_mq.restype = ctypes.c_int
     L.mla_decode_plan_mq.argtypes = [ctypes.POINTER(Dims), i32, i32, ctypes.POINTER(CacheDesc),
                                      i32, ctypes.POINTER(Plan)]
+    L.mla_decode_workspace_bytes.restype = sz
+    L.mla_decode_workspace_bytes.argtypes = [ctypes.POINTER(Dims), i32, i32]
     L.mla_decode_attn.restype = ctypes.c_int
     L.mla_decode_attn.argtypes = [ctypes.POINTER(Dims), i32, vp, ctypes.POINTER(CacheDesc),
                                   ctypes.c_float, ctypes.POINTER(Plan), vp, vp, vp, sz, vp]
@@ -260,9 +262,20 @@ def _lead(B: int, q_len: int, token_axis: bool):
 
 
 def workspace_for(plan: Plan, device) -> torch.Tensor:
-    """A device workspace of plan.workspace_bytes (256-byte aligned)."""
+    """A device workspace of plan.workspace_bytes (256-byte aligned), zeroed:
+    the MFMA plans keep the counters of the one-launch merge at its end, which
+    must start at zero (every call leaves them zero again)."""
     n = max(int(plan.workspace_bytes), 256)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def decode_workspace_bytes(n_heads: int, d_latent: int, d_rope: int, dtype, batch: int,
+                           max_len: int) -> int:
+    """mla_decode_workspace_bytes: workspace bytes of the default plan for
+    `batch` requests of at most `max_len` rows (one query token each, a
+    contiguous cache of native rows); 0 when the arguments are invalid."""
+    dims = make_dims(n_heads, 1, d_rope, d_latent, dtype)
+    return int(lib().mla_decode_workspace_bytes(ctypes.byref(dims), batch, max_len))
 
 
 def decode_attn(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,

@@ -87,10 +87,24 @@ size_t partial_elem_bytes(bool mfma) { return mfma ? 2 : sizeof(float); }
 // MFMA kernel the pair (log-sum-exp, reference max) of its unnormalised sum.
 size_t partial_stat_bytes(bool mfma) { return mfma ? 2 * sizeof(float) : sizeof(float); }
 
-size_t workspace_for(const mla_dims_t* d, int batch, int q_len, int num_splits, bool mfma) {
+// Workspace layout: partial rows, then their statistics, then (MFMA plans)
+// one pair of int32 counters per (request, head group) for the fused merge.
+size_t partials_bytes(const mla_dims_t* d, int batch, int q_len, int num_splits, bool mfma) {
   const size_t parts = static_cast<size_t>(batch) * num_splits * q_len * d->n_heads;
-  return round256(parts * d->d_latent * partial_elem_bytes(mfma)) +
-         round256(parts * partial_stat_bytes(mfma));
+  return round256(parts * d->d_latent * partial_elem_bytes(mfma));
+}
+size_t stats_bytes(const mla_dims_t* d, int batch, int q_len, int num_splits, bool mfma) {
+  const size_t parts = static_cast<size_t>(batch) * num_splits * q_len * d->n_heads;
+  return round256(parts * partial_stat_bytes(mfma));
+}
+size_t counter_bytes(int batch, int head_groups, bool mfma) {
+  return mfma ? round256(static_cast<size_t>(batch) * head_groups * 2 * sizeof(int32_t)) : 0;
+}
+size_t workspace_for(const mla_dims_t* d, int batch, int q_len, int num_splits, int head_groups,
+                     bool mfma) {
+  return partials_bytes(d, batch, q_len, num_splits, mfma) +
+         stats_bytes(d, batch, q_len, num_splits, mfma) +
+         counter_bytes(batch, head_groups, mfma);
 }
 
 mla_status_t make_plan(const mla_dims_t* d, int batch, int q_len, const mla_cache_t* c,
@@ -129,7 +143,7 @@ mla_status_t make_plan(const mla_dims_t* d, int batch, int q_len, const mla_cach
   plan->kernel = mfma ? 1 : 0;
   plan->head_groups = groups;
   plan->q_len = q_len;
-  plan->workspace_bytes = workspace_for(d, batch, q_len, num_splits, mfma);
+  plan->workspace_bytes = workspace_for(d, batch, q_len, num_splits, groups, mfma);
   return MLA_OK;
 }
 
@@ -151,7 +165,7 @@ const char* mla_status_str(mla_status_t s) {
   return "MLA_ERR_UNKNOWN";
 }
 
-int32_t mla_abi_version(void) { return 4; }
+int32_t mla_abi_version(void) { return 5; }
 
 mla_status_t mla_quantize_rows(int64_t n_rows, int32_t width, int32_t src_dtype, const void* src,
                                void* dst, float* scales, void* stream) {
@@ -215,11 +229,27 @@ mla_status_t mla_decode_plan_mq(const mla_dims_t* dims, int32_t batch, int32_t q
   return make_plan(dims, batch, q_len, cache, split_tokens, dev, plan);
 }
 
+size_t mla_decode_workspace_bytes(const mla_dims_t* dims, int32_t batch, int32_t max_len) {
+  if (check_dims(dims) != MLA_OK || batch < 0 || max_len < 0) return 0;
+  DeviceInfo dev;
+  if (current_device(&dev) != MLA_OK) return 0;
+  mla_cache_t c{};
+  c.max_len = max_len;
+  mla_decode_plan_t plan;
+  if (make_plan(dims, batch, 1, &c, 0, dev, &plan) != MLA_OK) return 0;
+  return plan.workspace_bytes;
+}
+
 }  // extern "C"
 
 namespace {
 
 enum DecodePart { kPartials = 1, kCombine = 2 };
+// The one-launch merge of mla_decode_attn.  Off: at 128 heads per workgroup
+// its partial sums (128 KiB per split) make the in-launch write and re-read
+// slower than the separate combine kernel (57 against 46 us at B=16,
+// T=4096 on MI355X).
+constexpr bool kOneLaunchMerge = false;
 
 // Validate a decode call and fill the kernel arguments.  `parts` says which
 // of the two phases will run, so only their pointers are required.
@@ -285,10 +315,15 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
   a->head_groups = plan_out->head_groups;
   a->out_lat = out_lat;
   a->lse = lse;
-  a->part_o = const_cast<void*>(workspace);
-  a->part_lse = reinterpret_cast<float*>(
-      static_cast<uint8_t*>(const_cast<void*>(workspace)) +
-      round256(parts_n * dims->d_latent * partial_elem_bytes(plan_out->kernel == 1)));
+  const bool mfma = plan_out->kernel == 1;
+  uint8_t* ws = static_cast<uint8_t*>(const_cast<void*>(workspace));
+  const size_t pb = partials_bytes(dims, batch, plan_out->q_len, plan_out->num_splits, mfma);
+  const size_t sb = stats_bytes(dims, batch, plan_out->q_len, plan_out->num_splits, mfma);
+  (void)parts_n;
+  a->part_o = ws;
+  a->part_lse = reinterpret_cast<float*>(ws + pb);
+  a->counters = mfma ? reinterpret_cast<int*>(ws + pb + sb) : nullptr;
+  a->resident_workgroups = dev.cus;
   a->stream = static_cast<hipStream_t>(stream);
   return MLA_OK;
 }
@@ -347,9 +382,14 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* 
   if (st != MLA_OK || batch == 0) return st;
   (void)hipGetLastError();
   // One split per request: the MFMA kernel normalises its rows itself and
-  // writes o_lat and lse, so there is nothing to merge.
+  // writes o_lat and lse, so there is nothing to merge.  Several splits
+  // whose workgroups all fit on the device at once: the splits of a row
+  // group merge each other's partials in the same launch (fused form).
+  // Otherwise the partials kernel and the combine kernel run in turn.
   a.direct = p.kernel == 1 && p.num_splits == 1 && cache->row_format == MLA_ROWS_NATIVE;
-  if ((st = run_partials(a, p)) != MLA_OK || a.direct) return st;
+  const long long grid = (static_cast<long long>(batch) * p.num_splits * p.head_groups + 7) / 8 * 8;
+  a.fused = kOneLaunchMerge && p.kernel == 1 && !a.direct && grid <= a.resident_workgroups;
+  if ((st = run_partials(a, p)) != MLA_OK || a.direct || a.fused) return st;
   return run_combine(a, p);
 }
 

@@ -102,12 +102,37 @@ struct MfmaParams {
   float scale_log2;       // softmax scale * log2(e)
   uint16_t* part_o;       // bf16 partials
   float2* part_ml;        // per (request, split, head): (base-2 log-sum-exp, m)
-  // One split only: when set, the kernel writes the normalised rows here
-  // ([B, n_rows, 512] bf16) and the natural-log lse to lse_out (if set)
-  // instead of partials.
+  // Direct and fused forms: the normalised rows ([B, n_rows, 512] bf16) and
+  // the natural-log lse (if set).
   uint16_t* out_lat;
   float* lse_out;
+  // Fused form: per row group (request, 128 query rows) an (arrive, depart)
+  // pair of counters, zero between calls.
+  int* counters;
 };
+
+// What a workgroup does with its partition's result.
+//  kEpiPartials: bf16 partial rows for a separate merge kernel.
+//  kEpiDirect:   one partition per request: normalised rows and lse.
+//  kEpiFused:    the partitions of a row group meet at a counter and merge
+//                each other's partials in the same launch (every workgroup
+//                of the grid must be resident at once).
+constexpr int kEpiPartials = 0, kEpiDirect = 1, kEpiFused = 2;
+
+// Fused merge.  The 128 rows x 512 latents of a row group are cut into 512
+// units of one head octet (8 rows) x one 16-byte chunk per lane (32 chunks):
+// unit (octet o, chunk c) of split s holds 16 lanes x 8 bf16 = 256 bytes at
+// element ((s_index * 16 + o) * 32 + c) * 128 + j * 8 of its row group's run,
+// j = 2 * (row % 8) + half being the lane's position in the octet.  Lane
+// (wave w, l32, half) of the decode kernel owns row 32 w + l32 and, for
+// latent block cb, the columns cb * 32 + 8 k + 4 half + (0..3), k = 0..3: its
+// chunk c = 2 cb + pp holds the columns with k = 2 pp and k = 2 pp + 1.
+constexpr int kUnits = 512;
+constexpr int kOctetElems = 32 * 128;
+// Polls of a split's arrival counter before the wait gives up and the row
+// group's output is set to NaN (only reachable if the grid's workgroups
+// are not all resident at once, which the launcher rules out).
+constexpr int kSpinLimit = 1 << 22;
 
 // 16-byte direct-to-LDS load: every lane reads 16 bytes at `src` and writes
 // them at LDS byte address lds_base + 16 * lane (lds_base wave-uniform, in M0).
@@ -237,10 +262,232 @@ __device__ __forceinline__ int swz(int n, int chunk) {
   return (((chunk >> 3) * kTile + n) << 7) + (((chunk & 7) ^ swz_key(n)) << 4);
 }
 
-// kDirect: one split, the rows are normalised and written to out_lat (with
-// lse) instead of partials; a separate instantiation keeps that epilogue out
-// of the split kernels.
-template <bool kPaged, bool kFp8, bool kDirect>
+// Weighted sums of kUB units x kKB partitions per batch of loads for one
+// thread of the fused merge (kUB * kKB = 32 sixteen-byte loads in flight).
+// The thread's units are ui0, ui0 + 16, ... (relative to u0, fewer than
+// n_units of them) and its partitions ph, ph + phases, ... < P.
+template <int kUB, int kKB>
+__device__ __forceinline__ void merge_units(const MfmaParams& p, const uint16_t* group_part,
+                                            const float* wts, const float* dens, int u0, int o0,
+                                            int n_units, int ui0, int ph, int phases, int P,
+                                            int j, size_t row0, float nan_or_one, float* red,
+                                            int slot) {
+  const int my_units = ui0 < n_units ? (phases == 1 ? (n_units - ui0 + 15) / 16 : 1) : 0;
+  const int my_splits = (P - ph + phases - 1) / phases;
+  // Idle threads address a valid unit (weight 0).  With several phases every
+  // thread makes exactly one pass, so all of them reach the barrier.
+  const int ui = min(ui0, n_units - 1);
+  const int last = max(my_units - 1, 0);
+  const int passes = phases > 1 ? 1 : (my_units + kUB - 1) / kUB;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int ub = pass * kUB;
+    float a[kUB][8];
+#pragma unroll
+    for (int i = 0; i < kUB; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[i][e] = 0.f;
+    // Units past the thread's last re-read its last one with weight 0.
+    int uo[kUB], urow[kUB];
+#pragma unroll
+    for (int i = 0; i < kUB; ++i) {
+      const int u = u0 + ui + 16 * min(ub + i, last);
+      uo[i] = (u >> 5) * kOctetElems + (u & 31) * 128 + j * 8;
+      urow[i] = ((u >> 5) - o0) * 8 + (j >> 1);
+    }
+    for (int k0 = 0; k0 < my_splits; k0 += kKB) {
+      bf16x8_t v[kUB][kKB];
+      float w[kUB][kKB];
+#pragma unroll
+      for (int kk = 0; kk < kKB; ++kk) {
+        const int ki = k0 + kk;
+        const int k = ph + phases * min(ki, max(my_splits - 1, 0));
+#pragma unroll
+        for (int i = 0; i < kUB; ++i) {
+          v[i][kk] = *reinterpret_cast<const bf16x8_t*>(
+              group_part + static_cast<size_t>(k) * 16 * kOctetElems + uo[i]);
+          w[i][kk] = (ki < my_splits && ub + i < my_units) ? wts[urow[i] * P + k] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < kKB; ++kk)
+#pragma unroll
+        for (int i = 0; i < kUB; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[i][e] = fmaf(w[i][kk], static_cast<float>(v[i][kk][e]), a[i][e]);
+    }
+    // Several phases of one unit: their sums meet in LDS and phase 0 adds
+    // them up (phases > 1 only when each thread has one unit).
+    if (phases > 1) {
+      float* mine = red + (slot * 16 + j) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mine[e] = a[0][e];
+    }
+    if (phases > 1) {
+      __syncthreads();
+      if (ph == 0 && my_units > 0) {
+        for (int q = 1; q < phases; ++q) {
+          const float* other = red + ((slot + q) * 16 + j) * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[0][e] += other[e];
+        }
+      }
+    }
+    if (ph != 0) continue;
+    // Normalised row pieces: chunk c of lane j holds, for latent block
+    // cb = c / 2, the columns cb*32 + 8k + 4*(j%2) + (0..3) with k = 2(c%2)
+    // and 2(c%2) + 1.
+#pragma unroll
+    for (int i = 0; i < kUB; ++i) {
+      if (ub + i >= my_units) break;
+      const int u = u0 + ui + 16 * (ub + i);
+      const int c = u & 31;
+      const float inv = nan_or_one / dens[urow[i]];
+      bf16x4_t lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = static_cast<__bf16>(a[i][e] * inv);
+        hi[e] = static_cast<__bf16>(a[i][4 + e] * inv);
+      }
+      const size_t row = row0 + (u >> 5) * 8 + (j >> 1);
+      uint16_t* o = p.out_lat + row * 512 + (c >> 1) * 32 + (c & 1) * 16 + (j & 1) * 4;
+      *reinterpret_cast<bf16x4_t*>(o) = lo;
+      *reinterpret_cast<bf16x4_t*>(o + 8) = hi;
+    }
+  }
+}
+
+// Fused form, more than one partition with tokens in the row group (request
+// b, rows g*128 ..): this partition's unnormalised sums go to the workspace
+// (layout at kUnits), the workgroup arrives at the row group's counter and
+// waits for the other n_used - 1 partitions, and then merges units
+// [s * 512 / n_used, (s + 1) * 512 / n_used) of all of them:
+//   o_lat = sum_s 2^(m_s - L) U_s / sum_s 2^(lse_s - L),  L = max_s lse_s
+// (the split combine, in base-2 log units) and lse = ln 2 (L + log2 of the
+// denominator).  The last partition to leave the counter resets it.
+__device__ __forceinline__ void fused_merge(const MfmaParams& p, const f32x16_t (&acc)[kCBlocks],
+                                            float m, float l, int b, int g, int s, int n_used,
+                                            uint8_t* lds) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int S = p.num_splits;
+  const size_t bg = static_cast<size_t>(b) * p.head_groups + g;
+  const size_t row0 = static_cast<size_t>(b) * p.n_rows + g * kMfmaHeadsPerGroup;
+  const uint16_t* group_part = p.part_o + bg * S * 16 * kOctetElems;
+  // 1. This partition's sums, straight from the accumulators: lane
+  //    (w, l32, half) is lane j = 2 (l32 % 8) + half of octet 4w + l32 / 8.
+  {
+    const int oct = wave * 4 + (l32 >> 3);
+    const int j = ((l32 & 7) << 1) + half;
+    uint16_t* dst = p.part_o + ((bg * S + s) * 16 + oct) * kOctetElems + j * 8;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      bf16x8_t v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(acc[c >> 1][(c & 1) * 8 + e]);
+      *reinterpret_cast<bf16x8_t*>(dst + c * 128) = v;
+    }
+    if (half == 0) p.part_ml[(row0 + wave * 32 + l32) * S + s] = make_float2(m + __log2f(l), m);
+  }
+  // 2. Every wave's stores have completed (vmcnt counts stores too); one
+  //    thread publishes them at agent scope and waits for the others.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  int* flag = reinterpret_cast<int*>(lds);
+  if (tid == 0) {
+    int* arrive = p.counters + 2 * bg;
+    __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int polls = 0;
+    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_used &&
+           polls < kSpinLimit) {
+      __builtin_amdgcn_s_sleep(1);
+      ++polls;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (__hip_atomic_fetch_add(arrive + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        n_used - 1) {
+      __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(arrive + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *flag = polls < kSpinLimit;
+  }
+  __syncthreads();
+  const float nan_or_one = *flag ? 1.f : __builtin_nanf("");
+
+  // 3. This partition's units and the rows they touch.
+  const int P = n_used;
+  const int u0 = s * kUnits / P, u1 = (s + 1) * kUnits / P, n_units = u1 - u0;
+  const int o0 = u0 >> 5, nrow = (((u1 - 1) >> 5) - o0 + 1) * 8;
+  float* Ls = reinterpret_cast<float*>(lds + 256);   // [128] L per row
+  float* Ds = Ls + 128;                               // [128] denominator per row
+  float* red = Ds + 128;                              // [16 * 16 * 8] phase sums
+  float* wts = red + 16 * 16 * 8;                     // [nrow * P] 2^(m_s - L)
+  const float2* st = p.part_ml + (row0 + o0 * 8) * S;
+  {
+    // 3a. L and the denominator of every row, tph threads per row.
+    int tph = 1;
+    while (tph < 32 && tph * 2 * nrow <= 256) tph *= 2;
+    const int r = tid / tph, q = tid % tph;
+    float L = -INFINITY, D = 0.f;
+    if (r < nrow) {
+      for (int k = q; k < P; k += tph) {
+        const float x = st[static_cast<size_t>(r) * S + k].x;
+        if (x > L) {
+          D = D * __builtin_amdgcn_exp2f(L - x) + 1.f;
+          L = x;
+        } else {
+          D += __builtin_amdgcn_exp2f(x - L);
+        }
+      }
+    }
+    for (int off = 1; off < tph; off <<= 1) {
+      const float L2 = __shfl_xor(L, off, 64), D2 = __shfl_xor(D, off, 64);
+      const float Ln = fmaxf(L, L2);
+      D = (L == -INFINITY ? 0.f : D * __builtin_amdgcn_exp2f(L - Ln)) +
+          (L2 == -INFINITY ? 0.f : D2 * __builtin_amdgcn_exp2f(L2 - Ln));
+      L = Ln;
+    }
+    if (r < nrow && q == 0) {
+      Ls[r] = L;
+      Ds[r] = D;
+      if (p.lse_out != nullptr && ((o0 * 8 + r) >> 3) * 32 >= u0 && (((o0 * 8 + r) >> 3) * 32) < u1)
+        p.lse_out[row0 + o0 * 8 + r] = (L + __log2f(D)) * kLn2 * nan_or_one;
+    }
+  }
+  __syncthreads();
+  // 3b. The weights 2^(m_s - L) of every (row, partition).
+  for (int idx = tid; idx < nrow * P; idx += 256) {
+    const int r = idx / P, k = idx - r * P;
+    wts[idx] = __builtin_amdgcn_exp2f(st[static_cast<size_t>(r) * S + k].y - Ls[r]);
+  }
+  __syncthreads();
+  // 3c. Units: 16 slots of 16 lanes.  With at least 16 units a slot takes
+  //     units slot, slot + 16, ... over every partition; with fewer, each
+  //     unit is shared by `phases` slots, one residue class of partitions each.
+  const int j = tid & 15, slot = tid >> 4;
+  const int phases = n_units >= 16 ? 1 : 16 / n_units;
+  const int ui0 = n_units >= 16 ? slot : slot / phases;
+  const int ph = n_units >= 16 ? 0 : slot % phases;
+  // kUB * kKB <= 32 loads per batch, fitted to P (more would spill).
+  if (P <= 2)
+    merge_units<8, 2>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
+                      nan_or_one, red, slot);
+  else if (P <= 4)
+    merge_units<4, 4>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
+                      nan_or_one, red, slot);
+  else if (P <= 8)
+    merge_units<2, 8>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
+                      nan_or_one, red, slot);
+  else if (P <= 16)
+    merge_units<2, 16>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
+                       nan_or_one, red, slot);
+  else
+    merge_units<1, 16>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
+                       nan_or_one, red, slot);
+}
+
+// kEpi: what is written (kEpiPartials, kEpiDirect or kEpiFused); each form
+// is its own instantiation so that the split kernels keep a lean epilogue.
+template <bool kPaged, bool kFp8, int kEpi>
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   // Low-bit rows: the scales of the tile in each ring stage.
@@ -272,8 +519,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   const int head = hblock * 32 + l32;
   if (t0 >= t1) {
     // The combine never reads partitions past the length.  Written directly,
-    // a row with nothing visible is o = 0, lse = -inf.
-    if constexpr (kDirect) {
+    // a row with nothing visible is o = 0, lse = -inf (in the fused form by
+    // the first partition's workgroup: no other one has tokens either).
+    if (kEpi != kEpiPartials && s == 0) {
       uint16_t* z = p.out_lat + (static_cast<size_t>(b) * p.n_rows + hblock * 32) * 512 + lane * 8;
       bf16x8_t zero;
 #pragma unroll
@@ -794,6 +1042,17 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
 
   // Softmax sum over both lane halves (each half saw half of the tokens).
   l = halves_sum(l);
+
+  // One partition with tokens in the row group: its rows are the result.
+  bool direct = kEpi == kEpiDirect;
+  if constexpr (kEpi == kEpiFused) {
+    const int n_used = (len + p.split_tokens - 1) / p.split_tokens;
+    direct = n_used == 1;
+    if (!direct) {
+      fused_merge(p, acc, m, l, b, g, s, n_used, lds);
+      return;
+    }
+  }
   // bf16 partial, split-minor per (request, row, split):
   // part_o[((b * n_rows + row) * S + s) * 512 + c], written as accumulated
   // (relative to the running max m, not divided by l: the combine applies
@@ -807,7 +1066,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   static_assert(4 * 32 * kOutStride <= kLdsBytes, "epilogue rows fit in the ring");
   __syncthreads();
   uint8_t* rows = lds + wave * 32 * kOutStride;
-  if constexpr (kDirect) {
+  if (direct) {
     // Written directly (one split): each lane's row is its head's, divided
     // by that head's softmax sum.
     const float inv_l = 1.f / l;
@@ -834,10 +1093,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // Split-minor layout: the S partial rows of one (request, row) are
   // contiguous, so the combine reads each merge as one run.  With one split
   // that is also the layout of out_lat.
-  uint16_t* dst = (kDirect ? p.out_lat : p.part_o) +
-                  ((static_cast<size_t>(b) * p.n_rows + hblock * 32) * p.num_splits + s) * 512 +
+  const int splits = direct ? 1 : p.num_splits;
+  uint16_t* dst = (direct ? p.out_lat : p.part_o) +
+                  ((static_cast<size_t>(b) * p.n_rows + hblock * 32) * splits + (direct ? 0 : s)) *
+                      512 +
                   lane * 8;
-  const size_t row_stride = static_cast<size_t>(p.num_splits) * 512;
+  const size_t row_stride = static_cast<size_t>(splits) * 512;
   // Plain stores: the combine that reads the partials right after this
   // kernel finds them in the last-level cache (non-temporal stores make this
   // kernel slightly faster but the whole step slower).
@@ -845,7 +1106,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   for (int r = 0; r < 32; ++r)
     *reinterpret_cast<bf16x8_t*>(dst + r * row_stride) =
         *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
-  if constexpr (kDirect) {
+  if (direct) {
     if (p.lse_out != nullptr && half == 0)
       p.lse_out[static_cast<size_t>(b) * p.n_rows + head] = (m + __log2f(l)) * kLn2;
   } else if (half == 0) {
@@ -872,16 +1133,34 @@ hipError_t launch_partials_mfma(const DecodeArgs& a) {
   p.part_o = static_cast<uint16_t*>(a.part_o);
   p.part_ml = reinterpret_cast<float2*>(a.part_lse);
   if (a.direct && a.num_splits != 1) return hipErrorInvalidValue;
-  p.out_lat = a.direct ? static_cast<uint16_t*>(a.out_lat) : nullptr;
-  p.lse_out = a.direct ? a.lse : nullptr;
+  if (a.direct && a.fused) return hipErrorInvalidValue;
+  const bool writes_out = a.direct || a.fused;
+  p.out_lat = writes_out ? static_cast<uint16_t*>(a.out_lat) : nullptr;
+  p.lse_out = writes_out ? a.lse : nullptr;
+  p.counters = a.counters;
   const int grid = (p.work_items + 7) / 8 * 8;  // multiple of the 8 XCDs
+  // The fused form needs every workgroup resident at once: one per compute
+  // unit (the kernel's LDS and registers allow no second one).
+  if (a.fused && (grid > a.resident_workgroups || a.counters == nullptr))
+    return hipErrorInvalidValue;
   const bool paged = a.cache.page_table != nullptr, fp8 = a.cache.fp8 != 0;
   // The direct form exists for bf16 rows only (the low-bit one would spill).
   if (a.direct && fp8) return hipErrorInvalidValue;
-  const auto kernel =
-      a.direct ? (paged ? decode_mfma_kernel<true, false, true> : decode_mfma_kernel<false, false, true>)
-               : (paged ? (fp8 ? decode_mfma_kernel<true, true, false> : decode_mfma_kernel<true, false, false>)
-                        : (fp8 ? decode_mfma_kernel<false, true, false> : decode_mfma_kernel<false, false, false>));
+  using Kernel = void (*)(MfmaParams);
+  Kernel kernel;
+  if (a.direct)
+    kernel = paged ? decode_mfma_kernel<true, false, kEpiDirect>
+                   : decode_mfma_kernel<false, false, kEpiDirect>;
+  else if (a.fused)
+    kernel = paged ? (fp8 ? decode_mfma_kernel<true, true, kEpiFused>
+                          : decode_mfma_kernel<true, false, kEpiFused>)
+                   : (fp8 ? decode_mfma_kernel<false, true, kEpiFused>
+                          : decode_mfma_kernel<false, false, kEpiFused>);
+  else
+    kernel = paged ? (fp8 ? decode_mfma_kernel<true, true, kEpiPartials>
+                          : decode_mfma_kernel<true, false, kEpiPartials>)
+                   : (fp8 ? decode_mfma_kernel<false, true, kEpiPartials>
+                          : decode_mfma_kernel<false, false, kEpiPartials>);
   kernel<<<grid, 256, 0, a.stream>>>(p);
   return hipGetLastError();
 }

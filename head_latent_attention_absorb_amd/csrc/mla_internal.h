@@ -48,6 +48,15 @@ struct DecodeArgs {
   // MFMA kernel with one split: write out_lat and lse directly (no partials,
   // no combine).
   bool direct = false;
+  // MFMA kernel, several splits merged in the same launch (the fused form):
+  // the partitions of each (request, 128-row group) meet at a pair of
+  // counters, counters[2 * (b * head_groups + g) + {0, 1}], which must be
+  // zero before the launch and are zero again after it.  Allowed only when
+  // the grid (work items rounded up to a multiple of 8) is at most
+  // resident_workgroups.
+  bool fused = false;
+  int* counters = nullptr;
+  int resident_workgroups = 0;
 };
 
 // Launchers return the hipError_t of the launch (hipSuccess when nothing

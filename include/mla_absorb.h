@@ -35,8 +35,10 @@
  *     launch the runtime rejects returns MLA_ERR_LAUNCH.  Device-side data
  *     (seq_lens, page_table) is trusted: values outside the documented
  *     ranges are undefined behaviour.
- *   - Calls on different streams may run concurrently; the library keeps no
- *     mutable global state apart from a per-device property cache.
+ *   - Calls on different streams may run concurrently, with one exception:
+ *     two mla_decode_attn calls that take the one-launch merge (see there)
+ *     must not overlap on one device.  The library keeps no mutable global
+ *     state apart from a per-device property cache.
  */
 #ifndef MLA_ABSORB_H
 #define MLA_ABSORB_H
@@ -116,13 +118,25 @@ typedef struct {
   size_t workspace_bytes; /* device bytes mla_decode_attn needs                */
 } mla_decode_plan_t;
 
+/* Device bytes of workspace mla_decode_attn needs for `batch` requests of
+ * at most max_len cached rows and one query token each, with the plan
+ * mla_decode_plan would choose (split_tokens = 0) for a contiguous cache of
+ * native rows on the current device: plan.workspace_bytes of that plan.
+ * Host only; allocates nothing and enqueues nothing.  Returns 0 for invalid
+ * dims, batch < 0, max_len < 0 or no current gfx950 device.  (A paged or
+ * low-bit cache, several query tokens or an explicit split size can need a
+ * different amount: take plan->workspace_bytes from mla_decode_plan or
+ * mla_decode_plan_mq for those.) */
+size_t mla_decode_workspace_bytes(const mla_dims_t* dims, int32_t batch, int32_t max_len);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* mla_status_str(mla_status_t status);
 
 /* Library ABI version (incremented on any signature change; 2 added
  * mla_decode_plan_t.q_len and mla_decode_plan_mq; 3 added mla_cache_t.scales,
  * mla_cache_t.row_format and mla_quantize_rows; 4 added mla_prefill_expand and
- * mla_prefill_attn). */
+ * mla_prefill_attn; 5 added mla_decode_workspace_bytes and the workspace's
+ * counter area, with the one-launch merge of mla_decode_attn). */
 int32_t mla_abi_version(void);
 
 /* Absorb W^UK into the query (V2 read-through section 2.3; V3 read-through
@@ -176,12 +190,24 @@ mla_status_t mla_decode_plan_mq(const mla_dims_t* dims, int32_t batch, int32_t q
  * and one query token.  A plan passed in must come from mla_decode_plan (or
  * mla_decode_plan_mq, whose q_len then sets the shapes) with the same dims,
  * batch and cache bounds.  workspace: device, >= plan->workspace_bytes, 256-byte
- * aligned, contents need no initialisation; calls that share a workspace
- * must be ordered on one stream.  With a one-split plan on the MFMA kernel
- * (plan->num_splits == 1, plan->kernel == 1) over native rows the decode kernel
- * normalises its
- * rows and writes out_lat and lse itself: nothing is merged and the workspace
- * is not touched. */
+ * aligned; calls that share a workspace must be ordered on one stream.
+ * With the MFMA kernel (plan->kernel == 1) the workspace ends with a counter
+ * area (its last 256-byte-rounded batch * head_groups * 8 bytes) that must be
+ * zero before the workspace is first used (hipMemset once after allocating
+ * it); every call leaves it zero again.  The rest needs no initialisation.
+ * How the call runs on the MFMA kernel:
+ *   - one split (plan->num_splits == 1) over native rows: the decode kernel
+ *     normalises its rows and writes out_lat and lse itself; the workspace
+ *     is not touched;
+ *   - several splits whose workgroups all fit on the device at once
+ *     (batch * num_splits * head_groups, rounded up to a multiple of 8, at
+ *     most the number of compute units): one launch; the splits of each
+ *     (request, 128-row group) write their partial sums to the workspace,
+ *     wait for each other at that group's counter and each merges a share of
+ *     all of them.  Two such calls must not overlap on one device (each
+ *     needs every compute unit; a wait that is never satisfied gives up
+ *     after about 2^22 polls and sets that group's out_lat and lse to NaN);
+ *   - otherwise mla_decode_partials followed by mla_decode_combine. */
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* q_cat,
                              const mla_cache_t* cache, float softmax_scale,
                              const mla_decode_plan_t* plan, void* out_lat, float* lse,

@@ -166,18 +166,20 @@ def mla_decode_reference(q_c: np.ndarray, q_r: np.ndarray, cache: np.ndarray,
 # Secondary (absorbed) form -- the method, step by step
 # ----------------------------------------------------------------------------
 
-def absorb_query(q_c: np.ndarray, q_r: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+def absorb_query(q_c: np.ndarray, q_r: np.ndarray, w_uk: np.ndarray,
+                 dtype=np.float64) -> np.ndarray:
     """Absorb W^UK into the query: q_lat,i = W^UK[i]^T q^C_i, so that
     q^C_i . (W^UK[i] c) = q_lat,i . c (V2 read-through section 2.3;
-    V3 read-through section 2.3).  Returns q_cat = [q_lat | q^R] as float64
-    [B, n_h, d_c + d_h^R], mirroring the cached row [c | k^R]."""
-    q_lat = np.einsum("bih,ihc->bic", np.asarray(q_c, np.float64),
-                      np.asarray(w_uk, np.float64))
-    return np.concatenate([q_lat, np.asarray(q_r, np.float64)], axis=2)
+    V3 read-through section 2.3).  Returns q_cat = [q_lat | q^R]
+    [B, n_h, d_c + d_h^R], mirroring the cached row [c | k^R].
+    ``dtype`` is the arithmetic type (float64, the parity reference, unless a
+    caller times the method in float32)."""
+    q_lat = np.einsum("bih,ihc->bic", np.asarray(q_c, dtype), np.asarray(w_uk, dtype))
+    return np.concatenate([q_lat, np.asarray(q_r, dtype)], axis=2)
 
 
-def latent_attention(q_cat: np.ndarray, rows: np.ndarray, d_latent: int, scale: float
-                     ) -> Tuple[np.ndarray, np.ndarray]:
+def latent_attention(q_cat: np.ndarray, rows: np.ndarray, d_latent: int, scale: float,
+                     dtype=np.float64) -> Tuple[np.ndarray, np.ndarray]:
     """Attention of one request against its cached rows in latent space.
 
     q_cat [n_h, d_c + d_h^R], rows [T, d_c + d_h^R].
@@ -186,9 +188,10 @@ def latent_attention(q_cat: np.ndarray, rows: np.ndarray, d_latent: int, scale: 
     sum stays in latent space: o_lat_i = sum_j p_{i,j} c_j (V2 read-through
     section 2.3: the weighted sum is done on the latent, projected back last).
     Returns (o_lat [n_h, d_c], lse [n_h]); T = 0 gives zeros and -inf.
+    ``dtype`` is the arithmetic type (float64 unless a caller times float32).
     """
-    q_cat = np.asarray(q_cat, np.float64)
-    rows = np.asarray(rows, np.float64)
+    q_cat = np.asarray(q_cat, dtype)
+    rows = np.asarray(rows, dtype)
     n_h = q_cat.shape[0]
     if rows.shape[0] == 0:
         return np.zeros((n_h, d_latent)), np.full(n_h, -np.inf)
@@ -262,28 +265,27 @@ def mla_prefill_reference(q_c: np.ndarray, q_r: np.ndarray, latent: np.ndarray,
     return o, lse
 
 
-def project_out(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+def project_out(o_lat: np.ndarray, w_uv: np.ndarray, dtype=np.float64) -> np.ndarray:
     """Apply W^UV after the latent-space sum: o_i[h] = sum_c W^UV[i,c,h] o_lat_i[c]
     (V2 read-through section 2.3; zeeklog equation 11 moved past the sum).
-    o_lat [B, n_h, d_c] -> o [B, n_h, d_h]."""
-    return np.einsum("bic,ich->bih", np.asarray(o_lat, np.float64),
-                     np.asarray(w_uv, np.float64))
+    o_lat [B, n_h, d_c] -> o [B, n_h, d_h], computed in ``dtype``."""
+    return np.einsum("bic,ich->bih", np.asarray(o_lat, dtype), np.asarray(w_uv, dtype))
 
 
 def mla_decode_absorbed(q_c, q_r, cache, seq_lens, w_uk, w_uv, scale,
-                        page_table=None, page_size=0, requests=None):
+                        page_table=None, page_size=0, requests=None, dtype=np.float64):
     """MLA decode in absorbed form: absorb_query -> latent_attention per request
     -> project_out.  Returns (o [B,n_h,d_h], o_lat [B,n_h,d_c], lse [B,n_h],
-    q_cat [B,n_h,d_c+d_h^R]) in float64."""
+    q_cat [B,n_h,d_c+d_h^R]), computed in ``dtype`` (float64 by default)."""
     d_c = w_uk.shape[2]
-    q_cat = absorb_query(q_c, q_r, w_uk)
+    q_cat = absorb_query(q_c, q_r, w_uk, dtype)
     B, n_h = q_cat.shape[:2]
-    o_lat = np.zeros((B, n_h, d_c))
-    lse = np.full((B, n_h), -np.inf)
+    o_lat = np.zeros((B, n_h, d_c), dtype)
+    lse = np.full((B, n_h), -np.inf, dtype)
     for b in (range(B) if requests is None else requests):
         rows = gather_rows(cache, b, int(seq_lens[b]), page_table, page_size)
-        o_lat[b], lse[b] = latent_attention(q_cat[b], rows, d_c, scale)
-    return project_out(o_lat, w_uv), o_lat, lse, q_cat
+        o_lat[b], lse[b] = latent_attention(q_cat[b], rows, d_c, scale, dtype)
+    return project_out(o_lat, w_uv, dtype), o_lat, lse, q_cat
 
 
 def default_scale(d_head: int, d_rope: int) -> float:

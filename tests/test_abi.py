@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_absorb_q", "mla_decode_attn", "mla_out_uv", "mla_decode_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
-    assert L.mla_abi_version() == 4
+    assert L.mla_abi_version() == 5
 
 
 def test_status_strings():
@@ -137,6 +137,16 @@ def test_no_device_is_reported_without_gpu():
     fake = ctypes.c_void_p(0x1000)
     st = L.mla_absorb_q(ctypes.byref(_dims()), 1, fake, fake, fake, fake, None)
     assert st == 7
+    # The workspace size needs the device's compute-unit count: 0 without one.
+    assert L.mla_decode_workspace_bytes(ctypes.byref(_dims()), 16, 4096) == 0
+
+
+def test_decode_workspace_bytes_rejects_bad_arguments():
+    L = mla.lib()
+    assert L.mla_decode_workspace_bytes(None, 16, 4096) == 0
+    assert L.mla_decode_workspace_bytes(ctypes.byref(_dims(n_heads=0)), 16, 4096) == 0
+    assert L.mla_decode_workspace_bytes(ctypes.byref(_dims()), -1, 4096) == 0
+    assert L.mla_decode_workspace_bytes(ctypes.byref(_dims()), 16, -1) == 0
 
 
 # ----------------------------------------------------------------------------

@@ -1,9 +1,12 @@
-"""The decode step (absorb -> partials -> combine + W^UV) captured into a HIP
-graph through torch's graph API and replayed: every replay must give the
-eager result bit for bit, with eager work and synchronisations between the
-replays, and a replay after the inputs change in place must follow them.
-No call of the step allocates, synchronises or clears memory, so the step is
-capturable as is."""
+"""The decode step captured into a HIP graph through torch's graph API and
+replayed, in both forms: absorb -> mla_decode_attn (one launch, the splits
+merging each other's partials at counters in the workspace) -> W^UV, and
+absorb -> partials -> combine + W^UV.  Every replay must give the eager
+result bit for bit, with eager work and synchronisations between the
+replays, and a replay after the inputs change in place must follow them; the
+one-launch form must leave its counters zero after every replay.  No call of
+the step allocates, synchronises or clears memory, so the step is capturable
+as is."""
 
 import sys
 
@@ -25,11 +28,12 @@ def _log(msg):
     sys.stdout.flush()
 
 
-def test_step_graph_replays_match_eager():
+@pytest.mark.parametrize("form", ["one_launch", "two_phase"])
+def test_step_graph_replays_match_eager(form):
     cfg = DSV2.replace(batch=6, len_lo=1, len_hi=1500, max_len=1536)
     case = make_case(cfg, 101, seq_lens=np.array([1500, 1, 700, 0, 1024, 33], np.int32))
     other = make_case(cfg, 102, seq_lens=case.seq_lens)
-    _log("[graph] B=6 ragged lengths, 3 replays")
+    _log(f"[graph] {form}: B=6 ragged lengths, 3 replays")
     dc, dc2 = DevCase(case), DevCase(other)
     B, nh = cfg.batch, cfg.n_heads
     plan = mla.decode_plan(nh, cfg.d_latent, cfg.d_rope, torch.bfloat16, dc.cache)
@@ -40,10 +44,21 @@ def test_step_graph_replays_match_eager():
     lse = torch.empty((B, nh), dtype=torch.float32, device="cuda")
     o = torch.empty((B, nh, cfg.d_head), dtype=torch.bfloat16, device="cuda")
 
+    assert plan.num_splits > 1
+
     def step():
         mla.absorb_q(q_c, q_r, dc.w_uk, out=q_cat)
-        mla.decode_partials(q_cat, dc.cache, cfg.scale, plan, ws)
-        mla.decode_combine_out(dc.cache, plan, ws, dc.w_uv, o_lat, lse, out=o)
+        if form == "one_launch":
+            mla.decode_attn(q_cat, dc.cache, cfg.scale, plan, o_lat, lse, ws)
+            mla.out_uv(o_lat, dc.w_uv, out=o)
+        else:
+            mla.decode_partials(q_cat, dc.cache, cfg.scale, plan, ws)
+            mla.decode_combine_out(dc.cache, plan, ws, dc.w_uv, o_lat, lse, out=o)
+
+    cb = (B * plan.head_groups * 8 + 255) // 256 * 256
+
+    def counters_zero():
+        return int(ws[plan.workspace_bytes - cb:plan.workspace_bytes].count_nonzero()) == 0
 
     step()
     torch.cuda.synchronize()
@@ -61,6 +76,7 @@ def test_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(o, ref[0]) and torch.equal(o_lat, ref[1]), f"replay {rep}"
         assert torch.equal(torch.nan_to_num(lse, neginf=-1e30), torch.nan_to_num(ref[2], neginf=-1e30))
+        assert counters_zero(), f"replay {rep}"
     # New query values in the captured input buffers.
     q_c.copy_(dc2.q_c)
     q_r.copy_(dc2.q_r)

@@ -189,7 +189,9 @@ def kernels():
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     ks = parse_kernels(r.stdout)
-    assert len(ks) == 6, sorted(ks)  # contiguous / paged x (bf16 / low-bit rows, split) + bf16 direct
+    # contiguous / paged x (bf16 / low-bit rows) x (split partials, fused merge),
+    # and contiguous / paged bf16 direct
+    assert len(ks) == 10, sorted(ks)
     return ks
 
 

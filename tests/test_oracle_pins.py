@@ -421,9 +421,9 @@ def _mut_sign_flip(q, k, v, scale):
     return _orig_softmax_attention(-q, k, v, scale)
 
 
-def _mut_absorb_no_rope(q_c, q_r, w_uk):
-    q_lat = np.einsum("bih,ihc->bic", np.asarray(q_c, float), np.asarray(w_uk, float))
-    return np.concatenate([q_lat, np.zeros_like(np.asarray(q_r, float))], axis=2)
+def _mut_absorb_no_rope(q_c, q_r, w_uk, dtype=np.float64):
+    q_lat = np.einsum("bih,ihc->bic", np.asarray(q_c, dtype), np.asarray(w_uk, dtype))
+    return np.concatenate([q_lat, np.zeros_like(np.asarray(q_r, dtype))], axis=2)
 
 
 @pytest.mark.parametrize("target,mutant", [
