@@ -2,18 +2,20 @@
 """Benchmark: MLA absorbed decode on one MI355X (default: DeepSeek-V2 shape B=16, T=4096).
 
 A step is one whole decode step of one layer on one batch of synthetic input:
-    mla_absorb_q -> mla_decode_attn -> mla_out_uv
-(mla_decode_attn is one launch whenever its workgroups all fit on the device:
-the split partitions merge each other's partials inside the decode kernel).  For the
+    mla_absorb_q -> mla_decode_partials -> mla_decode_combine_out
+(the last merges the split partials and applies W^UV in one kernel; it does
+exactly what mla_decode_combine followed by mla_out_uv does; with one split
+per request the step is mla_absorb_q -> mla_decode_attn -> mla_out_uv, the
+decode kernel writing o_lat itself).  For the
 60-layer workload a step is the 60 layers back to back, each with its own
 weights and cache.  Inputs are resident in HBM before the timed region.  A
 single-layer step uses the next entry of a rotating pool of independently
 seeded (cache, W^UK, W^UV, q) sets totalling > 512 MB, twice the 256 MB
 Infinity Cache, so the cache bytes really come from HBM.
 
-Beside the step, the attention alone (mla_decode_attn) is timed back to back
-over the same inputs and set against its roofline, and so is its two-phase
-form (mla_decode_partials followed by mla_decode_combine) for comparison.
+Beside the step, the attention alone (mla_decode_attn: the decode kernel and
+the split combine, one C call) is timed back to back over the same inputs and
+set against its roofline.
 
 Prints ONE JSON line on stdout (everything else goes to stderr).
 """
@@ -422,15 +424,7 @@ def main():
     o = torch.empty(lead + (nh, cfg.d_head), dtype=torch.bfloat16, device=dev)
     q_rows = q_cat.view(B * ql, nh, row)
     direct = plan.num_splits == 1
-    # mla_decode_attn runs as one launch when its workgroups all fit on the
-    # device (one split: the decode kernel writes o_lat itself; several: the
-    # splits merge each other's partials in the same launch), else as the
-    # partials kernel followed by the combine kernel.
-    grid = -(-B * plan.num_splits * plan.head_groups // 8) * 8
-    one_launch = direct or grid <= torch.cuda.get_device_properties(0).multi_processor_count
-    attn_form = ("one launch, one split: the decode kernel writes o_lat and lse" if direct else
-                 "one launch: split partials merged inside the decode kernel" if one_launch else
-                 "decode partials kernel + split combine kernel")
+    form = f"{128 if plan.kernel == 1 else 64} query rows per workgroup"
     stream = torch.cuda.current_stream()
 
     def layer(e: Entry, ev=None):
@@ -440,11 +434,19 @@ def main():
                      e.w_uk, out=q_rows)
         if ev is not None:
             ev[1].record(stream)
-        mla.decode_attn(q_cat, e.cache, cfg.scale, plan, o_lat, lse, ws)
-        if ev is not None:
-            ev[2].record(stream)
-        mla.out_uv(o_lat.view(B * ql, nh, cfg.d_latent), e.w_uv,
-                   out=o.view(B * ql, nh, cfg.d_head))
+        if direct:
+            # One split per request: mla_decode_attn's decode kernel writes
+            # o_lat and lse itself, then the per-head W^UV product.
+            mla.decode_attn(q_cat, e.cache, cfg.scale, plan, o_lat, lse, ws)
+            if ev is not None:
+                ev[2].record(stream)
+            mla.out_uv(o_lat.view(B * ql, nh, cfg.d_latent), e.w_uv,
+                       out=o.view(B * ql, nh, cfg.d_head))
+        else:
+            mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws)
+            if ev is not None:
+                ev[2].record(stream)
+            mla.decode_combine_out(e.cache, plan, ws, e.w_uv, o_lat, lse, out=o)
         if ev is not None:
             ev[3].record(stream)
 
@@ -532,40 +534,40 @@ def main():
             layer(e, evs[i][1:])
         torch.cuda.synchronize()
         phase = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(4)] for ev in evs])
-        append_us, absorb_us, attn_ph_us, tail_us = (float(x) for x in phase.mean(axis=0) * 1e3)
-        kernels_us = {"absorb_q": absorb_us, "decode_attn": attn_ph_us, "out_uv": tail_us,
-                      "cache_append": append_us}
+        append_us, absorb_us, partials_us, tail_us = (float(x) for x in phase.mean(axis=0) * 1e3)
+        if direct:
+            kernels_us = {"absorb_q": absorb_us, "decode_attn_direct": partials_us,
+                          "out_uv": tail_us, "cache_append": append_us}
+        else:
+            kernels_us = {"absorb_q": absorb_us, "decode_partials": partials_us,
+                          "decode_combine_out": tail_us, "cache_append": append_us}
         log(f"[bench] step {ms_per_step*1e3:.1f} us: absorb {absorb_us:.1f}, "
-            f"decode_attn {attn_ph_us:.1f}, out_uv {tail_us:.1f}")
+            f"{'decode (direct)' if direct else 'partials'} {partials_us:.1f}, "
+            f"{'out_uv' if direct else 'combine+out_uv'} {tail_us:.1f}")
     else:
         log(f"[bench] step ({cfg.layers} layers) {ms_per_step*1e3:.1f} us")
 
-    # mla_decode_attn alone, back to back on the same stream over the same
-    # inputs: its average duration per layer, free of the event records that
-    # split the phases above.  In its one-launch form this is the decode
-    # kernel's own launch duration, the roofline's time.
+    # The decode kernel alone, launched back to back on the same stream over
+    # the same inputs: its average launch duration, free of the event records
+    # that split the phases above.  This is the roofline's time.  With one
+    # split the kernel runs in the form that writes o_lat directly (through
+    # mla_decode_attn, which then launches nothing else).
     n_dec = args.steps * (cfg.layers if layered else 1)
-    decode_us = timed(lambda i: mla.decode_attn(
-        q_cat, pool[i % n_pool].cache, cfg.scale, plan, o_lat, lse, ws), n_dec)
-    log(f"[bench] mla_decode_attn back to back: {decode_us:.1f} us per launch ({attn_form})")
-    attn_us = decode_us * (cfg.layers if layered else 1)
-    # For comparison, the two-phase form of the same call (the partials
-    # kernel, then the separate combine kernel), and the partials kernel alone.
-    two_phase = {}
-    if not direct:
-        ws2 = mla.workspace_for(plan, dev)
+    if direct:
+        decode_us = timed(lambda i: mla.decode_attn(
+            q_cat, pool[i % n_pool].cache, cfg.scale, plan, o_lat, lse, ws), n_dec)
+    else:
+        decode_us = timed(lambda i: mla.decode_partials(
+            q_cat, pool[i % n_pool].cache, cfg.scale, plan, ws), n_dec)
+    log(f"[bench] decode kernel back to back: {decode_us:.1f} us per launch ({form})")
 
-        def two(i):
-            e = pool[i % n_pool]
-            mla.decode_partials(q_cat, e.cache, cfg.scale, plan, ws2)
-            mla.decode_combine(e.cache, nh, plan, ws2, o_lat, lse)
-        two_phase = {
-            "partials_us": timed(lambda i: mla.decode_partials(
-                q_cat, pool[i % n_pool].cache, cfg.scale, plan, ws2), n_dec),
-            "partials_plus_combine_us": timed(two, n_dec),
-        }
-        log(f"[bench] two-phase form: partials {two_phase['partials_us']:.1f} us, "
-            f"+ combine {two_phase['partials_plus_combine_us']:.1f} us")
+    # mla_decode_attn (the decode kernel, then the split combine unless one
+    # split), back to back, per step: one C call per layer.
+    def attn(i):
+        for e in entries(i):
+            mla.decode_attn(q_cat, e.cache, cfg.scale, plan, o_lat, lse, ws)
+    attn_us = timed(attn, args.steps)
+    log(f"[bench] mla_decode_attn back to back: {attn_us:.1f} us per step")
 
     # Algorithmic work per step (split partials excluded), averaged over the
     # entries the timed steps used.
@@ -585,10 +587,10 @@ def main():
     attn_bytes = cache_bytes + q_bytes + olat_bytes
     t_roof_attn_us = max(attn_bytes / (HBM_PEAK_GBPS * 1e9),
                          flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
-    # The dominant kernel's algorithmic bytes: in the one-launch form it reads
-    # the cache and the query and writes o_lat and lse; the partials kernel
-    # of the two-phase form writes only (non-algorithmic) partials.
-    k2_bytes = (attn_bytes if one_launch else cache_bytes + q_bytes) / layers_per_step
+    # The decode kernel's algorithmic bytes: the cache and the query (its
+    # split partials are not algorithmic); in the direct form also o_lat and
+    # lse, which it writes itself.
+    k2_bytes = (attn_bytes if direct else cache_bytes + q_bytes) / layers_per_step
     k2_gbps = k2_bytes / (decode_us * 1e-6) / 1e9
     k2_tflops = flops / layers_per_step / (decode_us * 1e-6) / 1e12
     # The decode kernel's bound: HBM, unless its products take longer at the
@@ -639,7 +641,9 @@ def main():
         "step_roofline_us": t_roof_us,
         "step_pct_roofline": 100.0 * t_roof_us / (ms_per_step * 1e3),
         "attn": {
-            "what": f"mla_decode_attn back to back ({attn_form})",
+            "what": ("mla_decode_attn, one split: the decode kernel writes o_lat and lse "
+                     "directly" if direct else
+                     "mla_decode_attn = decode kernel + split combine (one C call), back to back"),
             "us_per_step": attn_us,
             "roofline_us": t_roof_attn_us,
             "pct_roofline": 100.0 * t_roof_attn_us / attn_us,
@@ -648,11 +652,10 @@ def main():
         },
         "latent_cache_GBps": cache_bytes / layers_per_step / (decode_us * 1e-6) / 1e9,
         "tokens_per_layer": tokens_layer,
-        "kernels_us": dict(kernels_us, decode_attn_back_to_back=decode_us,
-                           **{f"two_phase_{k}": v for k, v in two_phase.items()}),
+        "kernels_us": dict(kernels_us, decode_kernel_back_to_back=decode_us),
         "roofline": {
-            "kernel": (f"decode_mfma_kernel (mla_decode_attn, {attn_form})" if one_launch
-                       else "decode_mfma_kernel (mla_decode_partials)"),
+            "kernel": (f"decode_mfma_kernel (mla_decode_attn, one split, direct output, {form})"
+                       if direct else f"decode_mfma_kernel (mla_decode_partials, {form})"),
             "bound": "mfma" if k2_mfma_bound else "hbm",
             "achieved": k2_tflops if k2_mfma_bound else k2_gbps,
             "peak": MFMA_BF16_PEAK_TFLOPS if k2_mfma_bound else HBM_PEAK_GBPS,

@@ -48,7 +48,7 @@ class Plan(ctypes.Structure):
 
     def __repr__(self):
         return (f"Plan(split_tokens={self.split_tokens}, num_splits={self.num_splits}, "
-                f"kernel={'mfma' if self.kernel == 1 else 'generic'}, "
+                f"kernel={ {0: 'generic', 1: 'mfma-128rows', 2: 'mfma-64rows'}.get(self.kernel, self.kernel)}, "
                 f"head_groups={self.head_groups}, q_len={self.q_len}, "
                 f"workspace_bytes={self.workspace_bytes})")
 
@@ -262,11 +262,9 @@ def _lead(B: int, q_len: int, token_axis: bool):
 
 
 def workspace_for(plan: Plan, device) -> torch.Tensor:
-    """A device workspace of plan.workspace_bytes (256-byte aligned), zeroed:
-    the MFMA plans keep the counters of the one-launch merge at its end, which
-    must start at zero (every call leaves them zero again)."""
+    """A device workspace of plan.workspace_bytes (256-byte aligned)."""
     n = max(int(plan.workspace_bytes), 256)
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def decode_workspace_bytes(n_heads: int, d_latent: int, d_rope: int, dtype, batch: int,

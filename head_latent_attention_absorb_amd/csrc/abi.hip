@@ -87,8 +87,7 @@ size_t partial_elem_bytes(bool mfma) { return mfma ? 2 : sizeof(float); }
 // MFMA kernel the pair (log-sum-exp, reference max) of its unnormalised sum.
 size_t partial_stat_bytes(bool mfma) { return mfma ? 2 * sizeof(float) : sizeof(float); }
 
-// Workspace layout: partial rows, then their statistics, then (MFMA plans)
-// one pair of int32 counters per (request, head group) for the fused merge.
+// Workspace layout: partial rows, then their statistics.
 size_t partials_bytes(const mla_dims_t* d, int batch, int q_len, int num_splits, bool mfma) {
   const size_t parts = static_cast<size_t>(batch) * num_splits * q_len * d->n_heads;
   return round256(parts * d->d_latent * partial_elem_bytes(mfma));
@@ -97,53 +96,76 @@ size_t stats_bytes(const mla_dims_t* d, int batch, int q_len, int num_splits, bo
   const size_t parts = static_cast<size_t>(batch) * num_splits * q_len * d->n_heads;
   return round256(parts * partial_stat_bytes(mfma));
 }
-size_t counter_bytes(int batch, int head_groups, bool mfma) {
-  return mfma ? round256(static_cast<size_t>(batch) * head_groups * 2 * sizeof(int32_t)) : 0;
-}
-size_t workspace_for(const mla_dims_t* d, int batch, int q_len, int num_splits, int head_groups,
-                     bool mfma) {
+size_t workspace_for(const mla_dims_t* d, int batch, int q_len, int num_splits, bool mfma) {
   return partials_bytes(d, batch, q_len, num_splits, mfma) +
-         stats_bytes(d, batch, q_len, num_splits, mfma) +
-         counter_bytes(batch, head_groups, mfma);
+         stats_bytes(d, batch, q_len, num_splits, mfma);
 }
 
+// form: -1 lets the planner choose the kernel form; 0, 1 or 2 asks for that
+// plan->kernel (a caller's plan being checked), MLA_ERR_DIMS if these dims
+// cannot run it.
 mla_status_t make_plan(const mla_dims_t* d, int batch, int q_len, const mla_cache_t* c,
-                       int split_req, const DeviceInfo& dev, mla_decode_plan_t* plan) {
+                       int split_req, const DeviceInfo& dev, mla_decode_plan_t* plan,
+                       int form = -1) {
   if (q_len < 1 || q_len > kMaxQueryLen) return MLA_ERR_DIMS;
+  if (split_req < 0) return MLA_ERR_DIMS;
   const bool mfma = use_mfma(d, c);
   const int granule = mfma ? mla::kMfmaTokenGranule : 1;
-  // Head groups count the query rows of all q_len tokens of a request.
-  const int groups = mfma ? q_len * d->n_heads / mla::kMfmaHeadsPerGroup : q_len * d->n_heads;
   const int max_len = c->max_len;
   const int len_cap = max_len > 0 ? (max_len + granule - 1) / granule * granule : granule;
-  int split;
-  if (split_req < 0) return MLA_ERR_DIMS;
-  if (split_req > 0) {
-    split = (split_req + granule - 1) / granule * granule;
-  } else {
-    // About one workgroup per compute unit when every request is at max_len.
-    const long long per_split = static_cast<long long>(batch > 0 ? batch : 1) * groups;
-    const long long target = mfma ? dev.cus : 2LL * dev.cus;
-    const long long splits = (target + per_split - 1) / per_split;
-    const long long raw = (max_len + splits - 1) / (splits > 0 ? splits : 1);
-    split = static_cast<int>((raw + granule - 1) / granule * granule);
-    const int floor_tokens = mfma ? 2 * granule : 64;
-    if (split < floor_tokens) split = floor_tokens;
+  // Split length for `groups` row groups per request: the caller's, or about
+  // one workgroup per compute unit when every request is at max_len.
+  auto choose_split = [&](int groups) {
+    int split;
+    if (split_req > 0) {
+      split = (split_req + granule - 1) / granule * granule;
+    } else {
+      const long long per_split = static_cast<long long>(batch > 0 ? batch : 1) * groups;
+      const long long target = mfma ? dev.cus : 2LL * dev.cus;
+      const long long splits = (target + per_split - 1) / per_split;
+      const long long raw = (max_len + splits - 1) / (splits > 0 ? splits : 1);
+      split = static_cast<int>((raw + granule - 1) / granule * granule);
+      const int floor_tokens = mfma ? 2 * granule : 64;
+      if (split < floor_tokens) split = floor_tokens;
+    }
+    if (split > len_cap) split = len_cap;
+    if (mfma && c->page_table != nullptr) {
+      // The MFMA kernel keeps a partition's page ids in one register per
+      // lane: a partition may touch at most 64 pages.
+      const int max_split = (63 * c->page_size) / granule * granule;
+      if (split > max_split) split = max_split;
+    }
+    return split;
+  };
+  auto splits_of = [&](int split) { return max_len > 0 ? (max_len + split - 1) / split : 1; };
+  // MFMA: 128 query rows per workgroup, or 64 when the 128-row plan has
+  // several splits of at most kMfmaHalfGroupMaxSplit tokens (bf16 rows
+  // only): half the query and partial bytes per split for twice the
+  // workgroups per request, which pays where each workgroup runs few steps.
+  // Head groups count the query rows of all q_len tokens of a request.
+  int rows = 1, kernel = 0;
+  if (mfma) {
+    kernel = 1;
+    if (form >= 0) {
+      if (form != 1 && (form != 2 || c->row_format != MLA_ROWS_NATIVE)) return MLA_ERR_DIMS;
+      kernel = form;
+    } else if (c->row_format == MLA_ROWS_NATIVE) {
+      const int split128 = choose_split(q_len * d->n_heads / mla::kMfmaHeadsPerGroup);
+      if (splits_of(split128) > 1 && split128 <= mla::kMfmaHalfGroupMaxSplit) kernel = 2;
+    }
+    rows = kernel == 2 ? mla::kMfmaHalfGroup : mla::kMfmaHeadsPerGroup;
+  } else if (form > 0) {
+    return MLA_ERR_DIMS;
   }
-  if (split > len_cap) split = len_cap;
-  if (mfma && c->page_table != nullptr) {
-    // The MFMA kernel keeps a partition's page ids in one register per lane:
-    // a partition may touch at most 64 pages.
-    const int max_split = (63 * c->page_size) / granule * granule;
-    if (split > max_split) split = max_split;
-  }
-  const int num_splits = max_len > 0 ? (max_len + split - 1) / split : 1;
+  const int groups = q_len * d->n_heads / rows;
+  const int split = choose_split(groups);
+  const int num_splits = splits_of(split);
   plan->split_tokens = split;
   plan->num_splits = num_splits;
-  plan->kernel = mfma ? 1 : 0;
+  plan->kernel = kernel;
   plan->head_groups = groups;
   plan->q_len = q_len;
-  plan->workspace_bytes = workspace_for(d, batch, q_len, num_splits, groups, mfma);
+  plan->workspace_bytes = workspace_for(d, batch, q_len, num_splits, mfma);
   return MLA_OK;
 }
 
@@ -245,11 +267,6 @@ size_t mla_decode_workspace_bytes(const mla_dims_t* dims, int32_t batch, int32_t
 namespace {
 
 enum DecodePart { kPartials = 1, kCombine = 2 };
-// The one-launch merge of mla_decode_attn.  Off: at 128 heads per workgroup
-// its partial sums (128 KiB per split) make the in-launch write and re-read
-// slower than the separate combine kernel (57 against 46 us at B=16,
-// T=4096 on MI355X).
-constexpr bool kOneLaunchMerge = false;
 
 // Validate a decode call and fill the kernel arguments.  `parts` says which
 // of the two phases will run, so only their pointers are required.
@@ -279,8 +296,8 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
     if ((st = make_plan(dims, batch, 1, cache, 0, dev, plan_out)) != MLA_OK) return st;
   } else {
     // A caller's plan must be one this library would produce for these sizes.
-    if ((st = make_plan(dims, batch, plan->q_len, cache, plan->split_tokens, dev, plan_out)) !=
-        MLA_OK)
+    if ((st = make_plan(dims, batch, plan->q_len, cache, plan->split_tokens, dev, plan_out,
+                        plan->kernel)) != MLA_OK)
       return st;
     if (plan_out->split_tokens != plan->split_tokens ||
         plan_out->num_splits != plan->num_splits || plan_out->kernel != plan->kernel ||
@@ -313,29 +330,27 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
   a->split_tokens = plan_out->split_tokens;
   a->num_splits = plan_out->num_splits;
   a->head_groups = plan_out->head_groups;
+  a->group_rows = plan_out->kernel == 2 ? mla::kMfmaHalfGroup : mla::kMfmaHeadsPerGroup;
   a->out_lat = out_lat;
   a->lse = lse;
-  const bool mfma = plan_out->kernel == 1;
+  const bool mfma = plan_out->kernel >= 1;
   uint8_t* ws = static_cast<uint8_t*>(const_cast<void*>(workspace));
   const size_t pb = partials_bytes(dims, batch, plan_out->q_len, plan_out->num_splits, mfma);
-  const size_t sb = stats_bytes(dims, batch, plan_out->q_len, plan_out->num_splits, mfma);
   (void)parts_n;
   a->part_o = ws;
   a->part_lse = reinterpret_cast<float*>(ws + pb);
-  a->counters = mfma ? reinterpret_cast<int*>(ws + pb + sb) : nullptr;
-  a->resident_workgroups = dev.cus;
   a->stream = static_cast<hipStream_t>(stream);
   return MLA_OK;
 }
 
 mla_status_t run_partials(const DecodeArgs& a, const mla_decode_plan_t& plan) {
-  const hipError_t e = plan.kernel == 1 ? mla::launch_partials_mfma(a)
+  const hipError_t e = plan.kernel >= 1 ? mla::launch_partials_mfma(a)
                                         : mla::launch_partials_generic(a);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 mla_status_t run_combine(const DecodeArgs& a, const mla_decode_plan_t& plan) {
-  const hipError_t e = mla::launch_combine(a, plan.kernel == 1);
+  const hipError_t e = mla::launch_combine(a, plan.kernel >= 1);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
@@ -382,14 +397,9 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* 
   if (st != MLA_OK || batch == 0) return st;
   (void)hipGetLastError();
   // One split per request: the MFMA kernel normalises its rows itself and
-  // writes o_lat and lse, so there is nothing to merge.  Several splits
-  // whose workgroups all fit on the device at once: the splits of a row
-  // group merge each other's partials in the same launch (fused form).
-  // Otherwise the partials kernel and the combine kernel run in turn.
-  a.direct = p.kernel == 1 && p.num_splits == 1 && cache->row_format == MLA_ROWS_NATIVE;
-  const long long grid = (static_cast<long long>(batch) * p.num_splits * p.head_groups + 7) / 8 * 8;
-  a.fused = kOneLaunchMerge && p.kernel == 1 && !a.direct && grid <= a.resident_workgroups;
-  if ((st = run_partials(a, p)) != MLA_OK || a.direct || a.fused) return st;
+  // writes o_lat and lse, so there is nothing to merge.
+  a.direct = p.kernel >= 1 && p.num_splits == 1 && cache->row_format == MLA_ROWS_NATIVE;
+  if ((st = run_partials(a, p)) != MLA_OK || a.direct) return st;
   return run_combine(a, p);
 }
 
@@ -419,7 +429,7 @@ mla_status_t mla_decode_combine_out(const mla_dims_t* dims, int32_t batch,
   // combine and the weight-streaming projection are faster (measured at
   // n_heads 128, d_latent 512: 18.0 vs 18.9 us at 32 requests, 30.0 vs 21.4
   // at 64).
-  if (p.kernel == 1 && batch * p.q_len <= kFusedTailMaxBatch &&
+  if (p.kernel >= 1 && batch * p.q_len <= kFusedTailMaxBatch &&
       mla::combine_out_fusable(dims->d_latent, dims->d_head)) {
     const hipError_t e = mla::launch_combine_rows(a, w_uv, out, dims->d_head);
     return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;

@@ -92,6 +92,8 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4)
 // s_waitcnt immediate: wait until no LDS access is outstanding; vmcnt and
 // expcnt are left at their maxima (no wait).
 constexpr int kLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+// Both: at most `n` vector-memory loads and no LDS access outstanding.
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
 
 struct MfmaParams {
   const uint16_t* q_cat;  // [B, n_rows, 576] bf16
@@ -102,37 +104,12 @@ struct MfmaParams {
   float scale_log2;       // softmax scale * log2(e)
   uint16_t* part_o;       // bf16 partials
   float2* part_ml;        // per (request, split, head): (base-2 log-sum-exp, m)
-  // Direct and fused forms: the normalised rows ([B, n_rows, 512] bf16) and
-  // the natural-log lse (if set).
+  // One split only: when set, the kernel writes the normalised rows here
+  // ([B, n_rows, 512] bf16) and the natural-log lse to lse_out (if set)
+  // instead of partials.
   uint16_t* out_lat;
   float* lse_out;
-  // Fused form: per row group (request, 128 query rows) an (arrive, depart)
-  // pair of counters, zero between calls.
-  int* counters;
 };
-
-// What a workgroup does with its partition's result.
-//  kEpiPartials: bf16 partial rows for a separate merge kernel.
-//  kEpiDirect:   one partition per request: normalised rows and lse.
-//  kEpiFused:    the partitions of a row group meet at a counter and merge
-//                each other's partials in the same launch (every workgroup
-//                of the grid must be resident at once).
-constexpr int kEpiPartials = 0, kEpiDirect = 1, kEpiFused = 2;
-
-// Fused merge.  The 128 rows x 512 latents of a row group are cut into 512
-// units of one head octet (8 rows) x one 16-byte chunk per lane (32 chunks):
-// unit (octet o, chunk c) of split s holds 16 lanes x 8 bf16 = 256 bytes at
-// element ((s_index * 16 + o) * 32 + c) * 128 + j * 8 of its row group's run,
-// j = 2 * (row % 8) + half being the lane's position in the octet.  Lane
-// (wave w, l32, half) of the decode kernel owns row 32 w + l32 and, for
-// latent block cb, the columns cb * 32 + 8 k + 4 half + (0..3), k = 0..3: its
-// chunk c = 2 cb + pp holds the columns with k = 2 pp and k = 2 pp + 1.
-constexpr int kUnits = 512;
-constexpr int kOctetElems = 32 * 128;
-// Polls of a split's arrival counter before the wait gives up and the row
-// group's output is set to NaN (only reachable if the grid's workgroups
-// are not all resident at once, which the launcher rules out).
-constexpr int kSpinLimit = 1 << 22;
 
 // 16-byte direct-to-LDS load: every lane reads 16 bytes at `src` and writes
 // them at LDS byte address lds_base + 16 * lane (lds_base wave-uniform, in M0).
@@ -262,242 +239,41 @@ __device__ __forceinline__ int swz(int n, int chunk) {
   return (((chunk >> 3) * kTile + n) << 7) + (((chunk & 7) ^ swz_key(n)) << 4);
 }
 
-// Weighted sums of kUB units x kKB partitions per batch of loads for one
-// thread of the fused merge (kUB * kKB = 32 sixteen-byte loads in flight).
-// The thread's units are ui0, ui0 + 16, ... (relative to u0, fewer than
-// n_units of them) and its partitions ph, ph + phases, ... < P.
-template <int kUB, int kKB>
-__device__ __forceinline__ void merge_units(const MfmaParams& p, const uint16_t* group_part,
-                                            const float* wts, const float* dens, int u0, int o0,
-                                            int n_units, int ui0, int ph, int phases, int P,
-                                            int j, size_t row0, float nan_or_one, float* red,
-                                            int slot) {
-  const int my_units = ui0 < n_units ? (phases == 1 ? (n_units - ui0 + 15) / 16 : 1) : 0;
-  const int my_splits = (P - ph + phases - 1) / phases;
-  // Idle threads address a valid unit (weight 0).  With several phases every
-  // thread makes exactly one pass, so all of them reach the barrier.
-  const int ui = min(ui0, n_units - 1);
-  const int last = max(my_units - 1, 0);
-  const int passes = phases > 1 ? 1 : (my_units + kUB - 1) / kUB;
-  for (int pass = 0; pass < passes; ++pass) {
-    const int ub = pass * kUB;
-    float a[kUB][8];
-#pragma unroll
-    for (int i = 0; i < kUB; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[i][e] = 0.f;
-    // Units past the thread's last re-read its last one with weight 0.
-    int uo[kUB], urow[kUB];
-#pragma unroll
-    for (int i = 0; i < kUB; ++i) {
-      const int u = u0 + ui + 16 * min(ub + i, last);
-      uo[i] = (u >> 5) * kOctetElems + (u & 31) * 128 + j * 8;
-      urow[i] = ((u >> 5) - o0) * 8 + (j >> 1);
-    }
-    for (int k0 = 0; k0 < my_splits; k0 += kKB) {
-      bf16x8_t v[kUB][kKB];
-      float w[kUB][kKB];
-#pragma unroll
-      for (int kk = 0; kk < kKB; ++kk) {
-        const int ki = k0 + kk;
-        const int k = ph + phases * min(ki, max(my_splits - 1, 0));
-#pragma unroll
-        for (int i = 0; i < kUB; ++i) {
-          v[i][kk] = *reinterpret_cast<const bf16x8_t*>(
-              group_part + static_cast<size_t>(k) * 16 * kOctetElems + uo[i]);
-          w[i][kk] = (ki < my_splits && ub + i < my_units) ? wts[urow[i] * P + k] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < kKB; ++kk)
-#pragma unroll
-        for (int i = 0; i < kUB; ++i)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a[i][e] = fmaf(w[i][kk], static_cast<float>(v[i][kk][e]), a[i][e]);
-    }
-    // Several phases of one unit: their sums meet in LDS and phase 0 adds
-    // them up (phases > 1 only when each thread has one unit).
-    if (phases > 1) {
-      float* mine = red + (slot * 16 + j) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mine[e] = a[0][e];
-    }
-    if (phases > 1) {
-      __syncthreads();
-      if (ph == 0 && my_units > 0) {
-        for (int q = 1; q < phases; ++q) {
-          const float* other = red + ((slot + q) * 16 + j) * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a[0][e] += other[e];
-        }
-      }
-    }
-    if (ph != 0) continue;
-    // Normalised row pieces: chunk c of lane j holds, for latent block
-    // cb = c / 2, the columns cb*32 + 8k + 4*(j%2) + (0..3) with k = 2(c%2)
-    // and 2(c%2) + 1.
-#pragma unroll
-    for (int i = 0; i < kUB; ++i) {
-      if (ub + i >= my_units) break;
-      const int u = u0 + ui + 16 * (ub + i);
-      const int c = u & 31;
-      const float inv = nan_or_one / dens[urow[i]];
-      bf16x4_t lo, hi;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[e] = static_cast<__bf16>(a[i][e] * inv);
-        hi[e] = static_cast<__bf16>(a[i][4 + e] * inv);
-      }
-      const size_t row = row0 + (u >> 5) * 8 + (j >> 1);
-      uint16_t* o = p.out_lat + row * 512 + (c >> 1) * 32 + (c & 1) * 16 + (j & 1) * 4;
-      *reinterpret_cast<bf16x4_t*>(o) = lo;
-      *reinterpret_cast<bf16x4_t*>(o + 8) = hi;
-    }
-  }
-}
-
-// Fused form, more than one partition with tokens in the row group (request
-// b, rows g*128 ..): this partition's unnormalised sums go to the workspace
-// (layout at kUnits), the workgroup arrives at the row group's counter and
-// waits for the other n_used - 1 partitions, and then merges units
-// [s * 512 / n_used, (s + 1) * 512 / n_used) of all of them:
-//   o_lat = sum_s 2^(m_s - L) U_s / sum_s 2^(lse_s - L),  L = max_s lse_s
-// (the split combine, in base-2 log units) and lse = ln 2 (L + log2 of the
-// denominator).  The last partition to leave the counter resets it.
-__device__ __forceinline__ void fused_merge(const MfmaParams& p, const f32x16_t (&acc)[kCBlocks],
-                                            float m, float l, int b, int g, int s, int n_used,
-                                            uint8_t* lds) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int half = lane >> 5, l32 = lane & 31;
-  const int S = p.num_splits;
-  const size_t bg = static_cast<size_t>(b) * p.head_groups + g;
-  const size_t row0 = static_cast<size_t>(b) * p.n_rows + g * kMfmaHeadsPerGroup;
-  const uint16_t* group_part = p.part_o + bg * S * 16 * kOctetElems;
-  // 1. This partition's sums, straight from the accumulators: lane
-  //    (w, l32, half) is lane j = 2 (l32 % 8) + half of octet 4w + l32 / 8.
-  {
-    const int oct = wave * 4 + (l32 >> 3);
-    const int j = ((l32 & 7) << 1) + half;
-    uint16_t* dst = p.part_o + ((bg * S + s) * 16 + oct) * kOctetElems + j * 8;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      bf16x8_t v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(acc[c >> 1][(c & 1) * 8 + e]);
-      *reinterpret_cast<bf16x8_t*>(dst + c * 128) = v;
-    }
-    if (half == 0) p.part_ml[(row0 + wave * 32 + l32) * S + s] = make_float2(m + __log2f(l), m);
-  }
-  // 2. Every wave's stores have completed (vmcnt counts stores too); one
-  //    thread publishes them at agent scope and waits for the others.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
-  int* flag = reinterpret_cast<int*>(lds);
-  if (tid == 0) {
-    int* arrive = p.counters + 2 * bg;
-    __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    int polls = 0;
-    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_used &&
-           polls < kSpinLimit) {
-      __builtin_amdgcn_s_sleep(1);
-      ++polls;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (__hip_atomic_fetch_add(arrive + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        n_used - 1) {
-      __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(arrive + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    *flag = polls < kSpinLimit;
-  }
-  __syncthreads();
-  const float nan_or_one = *flag ? 1.f : __builtin_nanf("");
-
-  // 3. This partition's units and the rows they touch.
-  const int P = n_used;
-  const int u0 = s * kUnits / P, u1 = (s + 1) * kUnits / P, n_units = u1 - u0;
-  const int o0 = u0 >> 5, nrow = (((u1 - 1) >> 5) - o0 + 1) * 8;
-  float* Ls = reinterpret_cast<float*>(lds + 256);   // [128] L per row
-  float* Ds = Ls + 128;                               // [128] denominator per row
-  float* red = Ds + 128;                              // [16 * 16 * 8] phase sums
-  float* wts = red + 16 * 16 * 8;                     // [nrow * P] 2^(m_s - L)
-  const float2* st = p.part_ml + (row0 + o0 * 8) * S;
-  {
-    // 3a. L and the denominator of every row, tph threads per row.
-    int tph = 1;
-    while (tph < 32 && tph * 2 * nrow <= 256) tph *= 2;
-    const int r = tid / tph, q = tid % tph;
-    float L = -INFINITY, D = 0.f;
-    if (r < nrow) {
-      for (int k = q; k < P; k += tph) {
-        const float x = st[static_cast<size_t>(r) * S + k].x;
-        if (x > L) {
-          D = D * __builtin_amdgcn_exp2f(L - x) + 1.f;
-          L = x;
-        } else {
-          D += __builtin_amdgcn_exp2f(x - L);
-        }
-      }
-    }
-    for (int off = 1; off < tph; off <<= 1) {
-      const float L2 = __shfl_xor(L, off, 64), D2 = __shfl_xor(D, off, 64);
-      const float Ln = fmaxf(L, L2);
-      D = (L == -INFINITY ? 0.f : D * __builtin_amdgcn_exp2f(L - Ln)) +
-          (L2 == -INFINITY ? 0.f : D2 * __builtin_amdgcn_exp2f(L2 - Ln));
-      L = Ln;
-    }
-    if (r < nrow && q == 0) {
-      Ls[r] = L;
-      Ds[r] = D;
-      if (p.lse_out != nullptr && ((o0 * 8 + r) >> 3) * 32 >= u0 && (((o0 * 8 + r) >> 3) * 32) < u1)
-        p.lse_out[row0 + o0 * 8 + r] = (L + __log2f(D)) * kLn2 * nan_or_one;
-    }
-  }
-  __syncthreads();
-  // 3b. The weights 2^(m_s - L) of every (row, partition).
-  for (int idx = tid; idx < nrow * P; idx += 256) {
-    const int r = idx / P, k = idx - r * P;
-    wts[idx] = __builtin_amdgcn_exp2f(st[static_cast<size_t>(r) * S + k].y - Ls[r]);
-  }
-  __syncthreads();
-  // 3c. Units: 16 slots of 16 lanes.  With at least 16 units a slot takes
-  //     units slot, slot + 16, ... over every partition; with fewer, each
-  //     unit is shared by `phases` slots, one residue class of partitions each.
-  const int j = tid & 15, slot = tid >> 4;
-  const int phases = n_units >= 16 ? 1 : 16 / n_units;
-  const int ui0 = n_units >= 16 ? slot : slot / phases;
-  const int ph = n_units >= 16 ? 0 : slot % phases;
-  // kUB * kKB <= 32 loads per batch, fitted to P (more would spill).
-  if (P <= 2)
-    merge_units<8, 2>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
-                      nan_or_one, red, slot);
-  else if (P <= 4)
-    merge_units<4, 4>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
-                      nan_or_one, red, slot);
-  else if (P <= 8)
-    merge_units<2, 8>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
-                      nan_or_one, red, slot);
-  else if (P <= 16)
-    merge_units<2, 16>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
-                       nan_or_one, red, slot);
-  else
-    merge_units<1, 16>(p, group_part, wts, Ds, u0, o0, n_units, ui0, ph, phases, P, j, row0,
-                       nan_or_one, red, slot);
-}
-
-// kEpi: what is written (kEpiPartials, kEpiDirect or kEpiFused); each form
-// is its own instantiation so that the split kernels keep a lean epilogue.
-template <bool kPaged, bool kFp8, int kEpi>
+// kDirect: one split, the rows are normalised and written to out_lat (with
+// lse) instead of partials; a separate instantiation keeps that epilogue out
+// of the split kernels.
+// kGH: query rows per workgroup.  128: wave w owns rows 32w..32w+31 over the
+// whole score contraction and the whole latent output.  64: the two waves of
+// head block hb = w % 2 split the work by kh = w / 2: wave kh takes the score
+// k-steps 4i + 2kh and 4i + 2kh + 1 (i < 9; half of the 576-long contraction,
+// RoPE columns included) and latent blocks 8kh .. 8kh + 7 of the output;
+// after each tile's products the two partial score sums meet in LDS (fp32,
+// added in the same order by both waves, so both hold the same scores, take
+// the same softmax and keep the same running max and sum).  Half the query
+// and half the partial sums per workgroup, for twice the workgroups per
+// request.
+template <bool kPaged, bool kFp8, bool kDirect, int kGH>
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
+  constexpr bool kHalf = kGH == 64;
+  static_assert(kGH == 128 || (kGH == 64 && !kFp8), "64-row groups: bf16 rows only");
+  // Score k-steps, latent blocks and PV products per wave and tile.
+  constexpr int kWK = kHalf ? kKSteps / 2 : kKSteps;
+  constexpr int kWCB = kHalf ? kCBlocks / 2 : kCBlocks;
+  constexpr int kWPv = 2 * kWCB;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   // Low-bit rows: the scales of the tile in each ring stage.
   __shared__ __attribute__((aligned(16))) uint8_t sc_lds[kFp8 ? kStages * kFp8ScaleBytes : 16];
+  // 64-row groups: each wave's partial scores of the next tile (16 fp32 per
+  // lane, four 16-byte chunks: chunk k of lane l at (k * 64 + l) * 16).
+  __shared__ __attribute__((aligned(16))) uint8_t xch[kHalf ? 4 * 4096 : 16];
   // Loads per wave per tile, and cache bytes per row.
   constexpr int kLoads = kFp8 ? kFp8Loads : kGroups;
   constexpr int kSrcRowBytes = kFp8 ? kFp8RowBytes : kRowBytes;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
+  const int hb = kHalf ? (wave & 1) : wave;  // head block of 32 rows in the group
+  const int kh = kHalf ? (wave >> 1) : 0;     // score / latent half (64-row groups)
 
   // XCD-aware work mapping: workgroup x runs on XCD x % 8; give every XCD a
   // contiguous range of work ids (the partitions of a request stay together).
@@ -509,33 +285,34 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   const int s = rest % p.num_splits;
   const int b = rest / p.num_splits;
 
-  // Query token j of the request (head group g covers rows g*128 ..) sees
+  // Query token j of the request (head group g covers rows g*kGH ..) sees
   // the rows up to its own position: q_len - 1 - j fewer than the request.
-  const int len = p.cache.seq_lens[b] -
-                  (p.q_len - 1 - g * kMfmaHeadsPerGroup / p.heads_per_token);
+  const int len = p.cache.seq_lens[b] - (p.q_len - 1 - g * kGH / p.heads_per_token);
   const int t0 = s * p.split_tokens;
   const int t1 = min(t0 + p.split_tokens, len);
-  const int hblock = g * 4 + wave;
+  const int hblock = g * (kGH / 32) + hb;
   const int head = hblock * 32 + l32;
   if (t0 >= t1) {
     // The combine never reads partitions past the length.  Written directly,
-    // a row with nothing visible is o = 0, lse = -inf (in the fused form by
-    // the first partition's workgroup: no other one has tokens either).
-    if (kEpi != kEpiPartials && s == 0) {
-      uint16_t* z = p.out_lat + (static_cast<size_t>(b) * p.n_rows + hblock * 32) * 512 + lane * 8;
+    // a row with nothing visible is o = 0, lse = -inf.
+    if constexpr (kDirect) {
+      constexpr int kZRows = kHalf ? 16 : 32;  // rows of the head block this wave clears
+      uint16_t* z = p.out_lat +
+                    (static_cast<size_t>(b) * p.n_rows + hblock * 32 + kh * kZRows) * 512 +
+                    lane * 8;
       bf16x8_t zero;
 #pragma unroll
       for (int e = 0; e < 8; ++e) zero[e] = static_cast<__bf16>(0.f);
-      for (int r = 0; r < 32; ++r) *reinterpret_cast<bf16x8_t*>(z + r * 512) = zero;
-      if (p.lse_out != nullptr && half == 0)
+      for (int r = 0; r < kZRows; ++r) *reinterpret_cast<bf16x8_t*>(z + r * 512) = zero;
+      if (p.lse_out != nullptr && half == 0 && kh == 0)
         p.lse_out[static_cast<size_t>(b) * p.n_rows + head] = -INFINITY;
     }
     return;
   }
 
-  f32x16_t acc[kCBlocks];
+  f32x16_t acc[kWCB];
 #pragma unroll
-  for (int cb = 0; cb < kCBlocks; ++cb)
+  for (int cb = 0; cb < kWCB; ++cb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
   float m = -INFINITY, l = 0.f;
@@ -707,26 +484,33 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // different XOR keys): voff[hi * 2 + cb % 2] + (cb / 2) * 4096 + kk * 2048.  The transposing read of lane (16-lane group G,
   // index r) addresses token {0,8} + (G/2)*4 + r/4 at latent column
   // 16*(G%2) + 4*(r%4) of its block.
+  // 64-row groups: local score k-step i of wave kh is global k-step
+  // 4 (i / 2) + 2 kh + i % 2, i.e. offsets qoff[i % 2] + (i / 2) * 4096 with
+  // qoff[q] = the 128-row form's qoff[2 kh + q]; its latent blocks start at
+  // 8 kh (16384 bytes further into the tile).
+  constexpr int kQP = kHalf ? 2 : 4;  // period of the score-operand offsets
   const int tr_tok = (half << 2) + ((lane >> 2) & 3);
   const int tr_col = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
   int qoff0[4], voff0[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) qoff0[q] = lds_address(lds) + swz(l32, q * 2 + half);
+  for (int q = 0; q < kQP; ++q) qoff0[q] = lds_address(lds) + swz(l32, (q + 2 * kh) * 2 + half);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int c = (q & 1) * 32 + tr_col;
-    voff0[q] = lds_address(lds) + swz(tr_tok + (q >> 1) * 8, c >> 3) + (c & 7) * 2;
+    voff0[q] = lds_address(lds) + swz(tr_tok + (q >> 1) * 8, c >> 3) + (c & 7) * 2 +
+               kh * (kWCB / 2) * 4096;
   }
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
 
-  // Operand reads.  Score operand of K-step ks of the tile whose offsets are
-  // in `qoff`; PV operand i = kk * 16 + cb of the tile whose offsets are in
-  // `voff` (consecutive PV MFMAs then update different accumulators).
+  // Operand reads.  Score operand of local K-step ks of the tile whose
+  // offsets are in `qoff`; PV operand i = kk * kWCB + cb of the tile whose
+  // offsets are in `voff` (consecutive PV MFMAs then update different
+  // accumulators).
   auto read_k = [&](const int (&qoff)[4], int ks) {
-    return *(MLA_LDS const bf16x8_t*)(uintptr_t)(qoff[ks & 3] + (ks >> 2) * 4096);
+    return *(MLA_LDS const bf16x8_t*)(uintptr_t)(qoff[ks % kQP] + (ks / kQP) * 4096);
   };
   auto read_v = [&](const int (&voff)[4], int i) {
-    const int kk = i >> 4, cb = i & 15;
+    const int kk = i / kWCB, cb = i % kWCB;
     const unsigned a = (cb >> 1) * 4096 + kk * 2048;
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (MLA_LDS i16x4_t*)(uintptr_t)(voff[cb & 1] + a));
@@ -738,7 +522,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // precomputing every operand address of every stage.
   auto k_offsets = [&](int stage, int (&qoff)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) qoff[q] = qoff0[q] + stage * kTileBytes;
+    for (int q = 0; q < 4; ++q) qoff[q] = q < kQP ? qoff0[q] + stage * kTileBytes : 0;
     asm volatile("" : "+v"(qoff[0]), "+v"(qoff[1]), "+v"(qoff[2]), "+v"(qoff[3]));
   };
   auto v_offsets = [&](int stage, int (&voff)[4]) {
@@ -758,39 +542,65 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // 2 and 3 (read by waves 2 and 3), round 1 head blocks 0 and 1.  The
   // barrier closing each round waits for LDS reads only, never for the tile
   // loads still in flight.
+  // 64-row groups: one round, head blocks 0 and 1 into stages 2 and 3 while
+  // tiles 0 and 1 stream into stages 0 and 1; every wave reads its own k-steps
+  // of its head block.
   static_assert(kStages == 4 && kMfmaHeadsPerGroup == kStages * kTile, "query fills the ring");
-  bf16x8_t qf[kKSteps];
+  bf16x8_t qf[kWK];
   {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(p.q_cat) +
-                          (static_cast<size_t>(b) * p.n_rows + g * kMfmaHeadsPerGroup + n_load) *
-                              kRowBytes + chunk_off;
-    for (int round = 0; round < 2; ++round) {
-      const int hb0 = 2 - 2 * round;  // first head block of this round
-      load_row_groups(qsrc + hb0 * kTile * kRowBytes, tile_dst(2),
+                          (static_cast<size_t>(b) * p.n_rows + g * kGH + n_load) * kRowBytes +
+                          chunk_off;
+    if constexpr (kHalf) {
+      load_row_groups(qsrc, tile_dst(2), std::make_integer_sequence<int, kGroups>{});
+      load_row_groups(qsrc + kTile * kRowBytes, tile_dst(3),
                       std::make_integer_sequence<int, kGroups>{});
-      load_row_groups(qsrc + (hb0 + 1) * kTile * kRowBytes, tile_dst(3),
-                      std::make_integer_sequence<int, kGroups>{});
-      // Tile 0 follows the first round's query loads and tile 1 the second
-      // round's, so the second wait need not cover tile 1: when every
-      // workgroup starts at once, the query and tile 0 arrive sooner with
-      // tile 1 not yet competing for the memory system.  Loads complete in
-      // issue order, so vmcnt(kLoads) means: everything but the tile just
-      // issued has landed.
-      issue_tile(round, t0 + round * kTile);
+      issue_tile(0, t0);
+      issue_tile(1, t0 + kTile);
+      // Loads complete in issue order: the query has landed, tiles 0 and 1
+      // may be in flight.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoads));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      int qo[4];
+      k_offsets(2 + hb, qo);
+#pragma unroll
+      for (int ks = 0; ks < kWK; ++ks) qf[ks] = read_k(qo, ks);
+      // Every wave's reads of stages 2 and 3 are done before they are
+      // refilled, and tile 0 has landed (tile 1 may be in flight).
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if ((wave & 2) == hb0) {
-        int qo[4];
-        k_offsets(2 + (wave & 1), qo);
+    } else {
+      for (int round = 0; round < 2; ++round) {
+        const int hb0 = 2 - 2 * round;  // first head block of this round
+        load_row_groups(qsrc + hb0 * kTile * kRowBytes, tile_dst(2),
+                        std::make_integer_sequence<int, kGroups>{});
+        load_row_groups(qsrc + (hb0 + 1) * kTile * kRowBytes, tile_dst(3),
+                        std::make_integer_sequence<int, kGroups>{});
+        // Tile 0 follows the first round's query loads and tile 1 the second
+        // round's, so the second wait need not cover tile 1: when every
+        // workgroup starts at once, the query and tile 0 arrive sooner with
+        // tile 1 not yet competing for the memory system.  Loads complete in
+        // issue order, so vmcnt(kLoads) means: everything but the tile just
+        // issued has landed.
+        issue_tile(round, t0 + round * kTile);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if ((wave & 2) == hb0) {
+          int qo[4];
+          k_offsets(2 + (wave & 1), qo);
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = read_k(qo, ks);
+          for (int ks = 0; ks < kWK; ++ks) qf[ks] = read_k(qo, ks);
+        }
+        // Every wave's reads of stages 2 and 3 are done before they are
+        // refilled.
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
       }
-      // Every wave's reads of stages 2 and 3 are done before they are
-      // refilled.
-      __builtin_amdgcn_s_waitcnt(kLgkm0);
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
     }
   }
   // The softmax takes its max on raw scores and folds the scale into the
@@ -800,7 +610,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   if (p.scale_log2 < 0.f) {
     typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
+    for (int ks = 0; ks < kWK; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, qf[ks]) ^ 0x80008000u);
   }
 
@@ -808,8 +618,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // 32x32x16 product that accumulates onto the previous one's result still
   // issues every 32 cycles).
   f32x16_t sc;
-  auto qk = [&](bf16x8_t (&ta)[kKSteps], const int (&qoff)[4], int ks) {
-    if (ks + kKWindow < kKSteps) ta[ks + kKWindow] = read_k(qoff, ks + kKWindow);
+  auto qk = [&](bf16x8_t (&ta)[kWK], const int (&qoff)[4], int ks) {
+    if (ks + kKWindow < kWK) ta[ks + kKWindow] = read_k(qoff, ks + kKWindow);
     if (ks == 0)
       mfma_first(sc, ta[ks], qf[ks]);
     else
@@ -830,9 +640,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   {
     int qoff[4];
     k_offsets(0, qoff);
-    bf16x8_t ta[kKSteps];
+    // Tile 0's score operands run eight reads ahead (the loop keeps three:
+    // there the softmax arithmetic fills the gaps, here nothing does).
+    bf16x8_t ta[kWK];
+    constexpr int kW0 = 8;
 #pragma unroll
-    for (int ks = 0; ks < kKWindow; ++ks) ta[ks] = read_k(qoff, ks);
+    for (int ks = 0; ks < kW0; ++ks) ta[ks] = read_k(qoff, ks);
     const uint8_t* src2 = kFp8 ? nullptr : tile_src(t0 + 2 * kTile);
     const unsigned dst2 = tile_dst(2);
     Fp8Tile f2{};
@@ -840,9 +653,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       f2 = fp8_tile(t0 + 2 * kTile, 2);
       fp8_extra(f2);
     }
-    static_for<kKSteps>([&](auto K) {
+    static_for<kWK>([&](auto K) {
       constexpr int ks = decltype(K)::value;
-      qk(ta, qoff, ks);
+      if constexpr (ks + kW0 < kWK) ta[ks + kW0] = read_k(qoff, ks + kW0);
+      if constexpr (ks == 0)
+        mfma_first(sc, ta[ks], qf[ks]);
+      else
+        mfma_v(sc, ta[ks], qf[ks]);
       if constexpr (kFp8) {
         if constexpr (ks < 4) fp8_piece(f2, ks);
       } else if constexpr (ks < kGroups) {
@@ -853,6 +670,28 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   }
   float s_next[16];
   take_scores(s_next, sc);
+
+  // 64-row groups: this wave's partial scores of the next tile go to its
+  // slot of xch; after the next barrier the partner wave (same head block,
+  // other half) adds them to its own.  A slot is rewritten only after a
+  // second barrier that follows the partner's read of it.
+  auto put_partial = [&](const float (&sp)[16]) {
+    if constexpr (kHalf) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *(MLA_LDS f32x4_t*)(uintptr_t)(lds_address(xch) + wave * 4096 + (k * 64 + lane) * 16) =
+            f32x4_t{sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
+    }
+  };
+  auto get_partial = [&](f32x4_t (&pp)[4]) {
+    if constexpr (kHalf) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        pp[k] = *(MLA_LDS const f32x4_t*)(uintptr_t)(lds_address(xch) + (wave ^ 2) * 4096 +
+                                                       (k * 64 + lane) * 16);
+    }
+  };
+  put_partial(s_next);
 
   // One step.  The softmax arithmetic of tile t (stage t % 4) is spread over
   // the first kSoftSlots score MFMAs of tile t+1 (stage (t+1) % 4), a few VALU
@@ -875,9 +714,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     // prefetch.  The compiler fence keeps LDS accesses on their side of the
     // barrier.  After it every wave is past step t-1, so the stage of tile
     // t-1, (t+3) % 4, is refilled with tile t+3.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
+    // (64-row groups: this wave's partial scores of tile t, written at the
+    // end of the previous step, are complete too.)
+    __builtin_amdgcn_s_waitcnt(kHalf ? vmcnt_lgkm0_imm(kLoads) : vmcnt_imm(kLoads));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    f32x4_t pp[4];
+    get_partial(pp);
     // Low-bit rows: tile t+1, read by this step's score products, is
     // converted now (tile t was converted one step earlier).
     if constexpr (kFp8 && kNext) fp8_convert((t + 1) & (kStages - 1));
@@ -896,13 +739,21 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       fp8_extra(fn);
     }
 
-    bf16x8_t ta[kKSteps];
+    bf16x8_t ta[kWK];
     if constexpr (kNext) {
 #pragma unroll
       for (int ks = 0; ks < kKWindow; ++ks) ta[ks] = read_k(qoff, ks);
     }
     auto qk_at = [&](int ks) {
       if constexpr (kNext) qk(ta, qoff, ks);
+      if constexpr (kHalf && !kFp8) {
+        // Tile t+3's first four column groups (every step issues them, as it
+        // issues the other five, so vmcnt counts stay uniform).
+        if (ks == 3) issue_load(std::integral_constant<int, 0>{}, next_src, next_dst);
+        if (ks == 7) issue_load(std::integral_constant<int, 1>{}, next_src, next_dst);
+        if (ks == 11) issue_load(std::integral_constant<int, 2>{}, next_src, next_dst);
+        if (ks == 15) issue_load(std::integral_constant<int, 3>{}, next_src, next_dst);
+      }
     };
 
     // Accumulator row of register v in this lane: token (v/4)*8 + half*4 +
@@ -913,17 +764,33 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     // not hoist its comparisons into every full tile.)
     const bool partial = nvalid < kTile;
     const int lim = nvalid - half * 4;
-    if (partial) {
-      int lim_p = lim;
-      launder(lim_p);
+    auto mask_partial = [&]() {
+      if (partial) {
+        int lim_p = lim;
+        launder(lim_p);
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if ((v >> 2) * 8 + (v & 3) >= lim_p) sv[v] = -INFINITY;
-    }
+        for (int v = 0; v < 16; ++v)
+          if ((v >> 2) * 8 + (v & 3) >= lim_p) sv[v] = -INFINITY;
+      }
+    };
+    if constexpr (!kHalf) mask_partial();
 
     // Tile max of the raw scores (the scale is >= 0 here, so it commutes with
     // the max), over both lane halves, then scaled to exp2 units.
     qk_at(0);
+    if constexpr (kHalf) {
+      // The partner's half of the scores (fp32 addition commutes, so both
+      // waves hold the same sums).  The second barrier:
+      // every wave has read its partner's slot before any slot is rewritten
+      // at the end of this step.
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sv[v] += pp[v >> 2][v & 3];
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) anchor(sv[v], sv[v + 1]);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      mask_partial();
+    }
 #pragma unroll
     for (int v = 0; v < 12; ++v) launder(sv[v]);
     const float a0 = fmax3(sv[0], sv[1], sv[2]), a1 = fmax3(sv[3], sv[4], sv[5]);
@@ -974,11 +841,15 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       s4[k] = (pv[4 * k] + pv[4 * k + 1]) + (pv[4 * k + 2] + pv[4 * k + 3]);
       anchor(s4[k]);
     }
+    // The PV operand is complete before the last softmax-phase score product:
+    // at least that product separates its VALU writes from the first PV
+    // product that reads it (two wait states needed).
+    asm volatile("" ::"v"(pb[0]), "v"(pb[1]));
     qk_at(16);
     const float psum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     static_assert(kSoftSlots == 17, "the softmax above occupies score products 0..16");
 
-    bf16x8_t va[kPv];
+    bf16x8_t va[kWPv];
 #pragma unroll
     for (int i = 0; i < kVWindow; ++i) va[i] = read_v(voff, i);
 
@@ -992,7 +863,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       // s_nops cover the MFMA-to-read wait states regardless.
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
 #pragma unroll
-      for (int cb = 0; cb < kCBlocks; ++cb)
+      for (int cb = 0; cb < kWCB; ++cb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float x = acc[cb][v], tmp;
@@ -1011,24 +882,36 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
 
     // PV of tile t; the first ones paired with the remaining score MFMAs of
     // tile t+1, every second one followed by one column group of tile t+3.
-    static_for<kPv>([&](auto I) {
+    // (64-row groups: half as many PV products per wave; four of the nine
+    // tile loads go between the score products of the softmax phase, the
+    // other five after every third PV product, so that the four waves' loads
+    // do not queue at the address unit at once.)
+    static_for<kWPv>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      if constexpr (i + kVWindow < kPv) va[i + kVWindow] = read_v(voff, i + kVWindow);
-      mfma_a(acc[i & 15], va[i], pb[i >> 4]);
-      if constexpr (kNext && kSoftSlots + i < kKSteps) qk(ta, qoff, kSoftSlots + i);
+      if constexpr (i + kVWindow < kWPv) va[i + kVWindow] = read_v(voff, i + kVWindow);
+      mfma_a(acc[i % kWCB], va[i], pb[i / kWCB]);
+      if constexpr (kNext && kSoftSlots + i < kWK) qk(ta, qoff, kSoftSlots + i);
       if constexpr (kFp8) {
         if constexpr (i % 2 == 0 && i / 2 < 4) fp8_piece(fn, i / 2);
+      } else if constexpr (kHalf) {
+        if constexpr (i % 3 == 1 && i / 3 < kGroups - 4)
+          issue_load(std::integral_constant<int, 4 + i / 3>{}, next_src, next_dst);
       } else if constexpr (i % 2 == 0 && i / 2 < kGroups) {
         issue_load(std::integral_constant<int, i / 2>{}, next_src, next_dst);
       }
     });
-    static_assert(kKSteps - kSoftSlots <= kPv, "every score MFMA is paired");
+    static_assert(kWK - kSoftSlots <= kWPv, "every score MFMA is paired");
+    static_assert(!kHalf || (kGroups - 4 <= (kWPv + 1) / 3 && kSoftSlots > 15),
+                  "every column group of tile t+3 is issued once per step");
     // The scores of tile t+1 leave the accumulator behind the last PV
     // products, which issue after the last score product: it has retired by
     // then, with far more than the 18 wait states a VALU read of an MFMA
     // result needs.
-    static_assert(kPv - (kKSteps - kSoftSlots) >= 4, "PV products behind the last score product");
-    if constexpr (kNext) take_scores(s_next, sc);
+    static_assert(kWPv - (kWK - kSoftSlots) >= 4, "PV products behind the last score product");
+    if constexpr (kNext) {
+      take_scores(s_next, sc);
+      put_partial(s_next);
+    }
   };
 
   for (int t = 0; t + 1 < ntiles; ++t) step(t, std::true_type{});
@@ -1038,80 +921,63 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-  for (int cb = 0; cb < kCBlocks; ++cb) asm volatile("" : "+a"(acc[cb]));
+  for (int cb = 0; cb < kWCB; ++cb) asm volatile("" : "+a"(acc[cb]));
 
   // Softmax sum over both lane halves (each half saw half of the tokens).
   l = halves_sum(l);
 
-  // One partition with tokens in the row group: its rows are the result.
-  bool direct = kEpi == kEpiDirect;
-  if constexpr (kEpi == kEpiFused) {
-    const int n_used = (len + p.split_tokens - 1) / p.split_tokens;
-    direct = n_used == 1;
-    if (!direct) {
-      fused_merge(p, acc, m, l, b, g, s, n_used, lds);
-      return;
-    }
-  }
+  constexpr bool direct = kDirect;
   // bf16 partial, split-minor per (request, row, split):
   // part_o[((b * n_rows + row) * S + s) * 512 + c], written as accumulated
   // (relative to the running max m, not divided by l: the combine applies
   // both factors as one weight, which saves a multiply per element here).
-  // Register v of latent
-  // block cb holds column cb*32 + (v/4)*8 + half*4 + v%4.  The rows pass
-  // through LDS (free once every wave is past its last step) so that each
-  // global store writes a whole 1 KiB row: wave w owns rows w*32 .. w*32+31,
-  // kOutStride bytes apart.
+  // Register v of latent block cb holds column cb*32 + (v/4)*8 + half*4 +
+  // v%4.  The rows pass through LDS (free once every wave is past its last
+  // step) so that each global store writes a whole 1 KiB row: head block hb
+  // owns rows hb*32 .. hb*32+31, kOutStride bytes apart (64-row groups: the
+  // two waves of a head block write the two latent halves of its rows, then
+  // each stores 16 of them).
   constexpr int kOutStride = 1024 + 16;
   static_assert(4 * 32 * kOutStride <= kLdsBytes, "epilogue rows fit in the ring");
   __syncthreads();
-  uint8_t* rows = lds + wave * 32 * kOutStride;
-  if (direct) {
-    // Written directly (one split): each lane's row is its head's, divided
-    // by that head's softmax sum.
-    const float inv_l = 1.f / l;
+  uint8_t* rows = lds + hb * 32 * kOutStride;
+  const float inv_l = direct ? 1.f / l : 1.f;
 #pragma unroll
-    for (int cb = 0; cb < kCBlocks; ++cb)
+  for (int cb = 0; cb < kWCB; ++cb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4_t v4;
+    for (int gq = 0; gq < 4; ++gq) {
+      bf16x4_t v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][g * 4 + e] * inv_l);
-        *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride + (cb * 32 + g * 8 + half * 4) * 2) = v4;
-      }
-  } else {
-#pragma unroll
-    for (int cb = 0; cb < kCBlocks; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4_t v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][g * 4 + e]);
-        *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride + (cb * 32 + g * 8 + half * 4) * 2) = v4;
-      }
-  }
+      for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(acc[cb][gq * 4 + e] * inv_l);
+      *reinterpret_cast<bf16x4_t*>(rows + l32 * kOutStride +
+                                   ((kh * kWCB + cb) * 32 + gq * 8 + half * 4) * 2) = v4;
+    }
+  if constexpr (kHalf) __syncthreads();
   // Split-minor layout: the S partial rows of one (request, row) are
   // contiguous, so the combine reads each merge as one run.  With one split
   // that is also the layout of out_lat.
+  constexpr int kStRows = kHalf ? 16 : 32;  // rows this wave stores
   const int splits = direct ? 1 : p.num_splits;
   uint16_t* dst = (direct ? p.out_lat : p.part_o) +
-                  ((static_cast<size_t>(b) * p.n_rows + hblock * 32) * splits + (direct ? 0 : s)) *
-                      512 +
+                  ((static_cast<size_t>(b) * p.n_rows + hblock * 32 + kh * kStRows) * splits +
+                   (direct ? 0 : s)) * 512 +
                   lane * 8;
   const size_t row_stride = static_cast<size_t>(splits) * 512;
   // Plain stores: the combine that reads the partials right after this
   // kernel finds them in the last-level cache (non-temporal stores make this
   // kernel slightly faster but the whole step slower).
 #pragma unroll 8
-  for (int r = 0; r < 32; ++r)
+  for (int r = 0; r < kStRows; ++r)
     *reinterpret_cast<bf16x8_t*>(dst + r * row_stride) =
-        *reinterpret_cast<const bf16x8_t*>(rows + r * kOutStride + lane * 16);
-  if (direct) {
-    if (p.lse_out != nullptr && half == 0)
-      p.lse_out[static_cast<size_t>(b) * p.n_rows + head] = (m + __log2f(l)) * kLn2;
-  } else if (half == 0) {
-    p.part_ml[(static_cast<size_t>(b) * p.n_rows + head) * p.num_splits + s] =
-        make_float2(m + __log2f(l), m);
+        *reinterpret_cast<const bf16x8_t*>(rows + (kh * kStRows + r) * kOutStride + lane * 16);
+  if (half == 0 && kh == 0) {
+    if (direct) {
+      if (p.lse_out != nullptr)
+        p.lse_out[static_cast<size_t>(b) * p.n_rows + head] = (m + __log2f(l)) * kLn2;
+    } else {
+      p.part_ml[(static_cast<size_t>(b) * p.n_rows + head) * p.num_splits + s] =
+          make_float2(m + __log2f(l), m);
+    }
   }
 }
 
@@ -1133,34 +999,29 @@ hipError_t launch_partials_mfma(const DecodeArgs& a) {
   p.part_o = static_cast<uint16_t*>(a.part_o);
   p.part_ml = reinterpret_cast<float2*>(a.part_lse);
   if (a.direct && a.num_splits != 1) return hipErrorInvalidValue;
-  if (a.direct && a.fused) return hipErrorInvalidValue;
-  const bool writes_out = a.direct || a.fused;
-  p.out_lat = writes_out ? static_cast<uint16_t*>(a.out_lat) : nullptr;
-  p.lse_out = writes_out ? a.lse : nullptr;
-  p.counters = a.counters;
+  p.out_lat = a.direct ? static_cast<uint16_t*>(a.out_lat) : nullptr;
+  p.lse_out = a.direct ? a.lse : nullptr;
   const int grid = (p.work_items + 7) / 8 * 8;  // multiple of the 8 XCDs
-  // The fused form needs every workgroup resident at once: one per compute
-  // unit (the kernel's LDS and registers allow no second one).
-  if (a.fused && (grid > a.resident_workgroups || a.counters == nullptr))
-    return hipErrorInvalidValue;
   const bool paged = a.cache.page_table != nullptr, fp8 = a.cache.fp8 != 0;
-  // The direct form exists for bf16 rows only (the low-bit one would spill).
+  // The direct form exists for bf16 rows only (the low-bit one would spill),
+  // and so does the 64-row form.
   if (a.direct && fp8) return hipErrorInvalidValue;
+  if (a.group_rows != 128 && (a.group_rows != 64 || fp8)) return hipErrorInvalidValue;
   using Kernel = void (*)(MfmaParams);
   Kernel kernel;
-  if (a.direct)
-    kernel = paged ? decode_mfma_kernel<true, false, kEpiDirect>
-                   : decode_mfma_kernel<false, false, kEpiDirect>;
-  else if (a.fused)
-    kernel = paged ? (fp8 ? decode_mfma_kernel<true, true, kEpiFused>
-                          : decode_mfma_kernel<true, false, kEpiFused>)
-                   : (fp8 ? decode_mfma_kernel<false, true, kEpiFused>
-                          : decode_mfma_kernel<false, false, kEpiFused>);
+  if (a.group_rows == 64)
+    kernel = a.direct ? (paged ? decode_mfma_kernel<true, false, true, 64>
+                               : decode_mfma_kernel<false, false, true, 64>)
+                      : (paged ? decode_mfma_kernel<true, false, false, 64>
+                               : decode_mfma_kernel<false, false, false, 64>);
+  else if (a.direct)
+    kernel = paged ? decode_mfma_kernel<true, false, true, 128>
+                   : decode_mfma_kernel<false, false, true, 128>;
   else
-    kernel = paged ? (fp8 ? decode_mfma_kernel<true, true, kEpiPartials>
-                          : decode_mfma_kernel<true, false, kEpiPartials>)
-                   : (fp8 ? decode_mfma_kernel<false, true, kEpiPartials>
-                          : decode_mfma_kernel<false, false, kEpiPartials>);
+    kernel = paged ? (fp8 ? decode_mfma_kernel<true, true, false, 128>
+                          : decode_mfma_kernel<true, false, false, 128>)
+                   : (fp8 ? decode_mfma_kernel<false, true, false, 128>
+                          : decode_mfma_kernel<false, false, false, 128>);
   kernel<<<grid, 256, 0, a.stream>>>(p);
   return hipGetLastError();
 }

@@ -40,6 +40,9 @@ struct DecodeArgs {
   CacheView cache;
   float softmax_scale;
   int32_t split_tokens, num_splits, head_groups;
+  // MFMA kernel: query rows per workgroup, 128 or 64 (head_groups = q_len *
+  // n_heads / group_rows).
+  int32_t group_rows = 128;
   void* out_lat;
   float* lse;           // may be nullptr
   void* part_o;         // workspace: fp32 (generic kernel) or bf16 (MFMA kernel)
@@ -48,15 +51,6 @@ struct DecodeArgs {
   // MFMA kernel with one split: write out_lat and lse directly (no partials,
   // no combine).
   bool direct = false;
-  // MFMA kernel, several splits merged in the same launch (the fused form):
-  // the partitions of each (request, 128-row group) meet at a pair of
-  // counters, counters[2 * (b * head_groups + g) + {0, 1}], which must be
-  // zero before the launch and are zero again after it.  Allowed only when
-  // the grid (work items rounded up to a multiple of 8) is at most
-  // resident_workgroups.
-  bool fused = false;
-  int* counters = nullptr;
-  int resident_workgroups = 0;
 };
 
 // Launchers return the hipError_t of the launch (hipSuccess when nothing
@@ -113,7 +107,12 @@ hipError_t launch_quantize_rows(int src_dtype, int64_t n_rows, int width, const 
                                 void* dst, float* scales, hipStream_t stream);
 
 // Constants of the MFMA decode kernel that the planner needs.
-constexpr int kMfmaHeadsPerGroup = 128;  // heads handled by one workgroup
+constexpr int kMfmaHeadsPerGroup = 128;  // query rows of a workgroup (128-row form)
+constexpr int kMfmaHalfGroup = 64;       // query rows of a workgroup (64-row form)
 constexpr int kMfmaTokenGranule = 32;    // tokens consumed per workgroup iteration
+// The 64-row form is chosen when the 128-row plan would give each
+// workgroup at most this many tokens (8 steps): there the partial sums
+// written per split weigh most against the steps.
+constexpr int kMfmaHalfGroupMaxSplit = 256;
 
 }  // namespace mla

@@ -35,10 +35,8 @@
  *     launch the runtime rejects returns MLA_ERR_LAUNCH.  Device-side data
  *     (seq_lens, page_table) is trusted: values outside the documented
  *     ranges are undefined behaviour.
- *   - Calls on different streams may run concurrently, with one exception:
- *     two mla_decode_attn calls that take the one-launch merge (see there)
- *     must not overlap on one device.  The library keeps no mutable global
- *     state apart from a per-device property cache.
+ *   - Calls on different streams may run concurrently; the library keeps no
+ *     mutable global state apart from a per-device property cache.
  */
 #ifndef MLA_ABSORB_H
 #define MLA_ABSORB_H
@@ -111,7 +109,11 @@ typedef struct {
 typedef struct {
   int32_t split_tokens;   /* tokens per partition                              */
   int32_t num_splits;     /* partitions per request, ceil(max_len/split_tokens) */
-  int32_t kernel;         /* 0 = generic fp32-VALU kernel, 1 = bf16 MFMA kernel */
+  int32_t kernel;         /* 0 = generic fp32-VALU kernel; bf16 MFMA kernel with
+                             1 = 128 or 2 = 64 query rows per workgroup (2:
+                             chosen for several splits of at most 256 tokens;
+                             the four waves then split the score contraction
+                             and the latent output in halves)                 */
   int32_t head_groups;    /* query rows (q_len * n_heads) are processed in this
                              many groups                                      */
   int32_t q_len;          /* query tokens per request (1 = plain decode)       */
@@ -135,8 +137,8 @@ const char* mla_status_str(mla_status_t status);
 /* Library ABI version (incremented on any signature change; 2 added
  * mla_decode_plan_t.q_len and mla_decode_plan_mq; 3 added mla_cache_t.scales,
  * mla_cache_t.row_format and mla_quantize_rows; 4 added mla_prefill_expand and
- * mla_prefill_attn; 5 added mla_decode_workspace_bytes and the workspace's
- * counter area, with the one-launch merge of mla_decode_attn). */
+ * mla_prefill_attn; 5 added mla_decode_workspace_bytes and the 64-row form of
+ * the MFMA kernel, plan->kernel 2). */
 int32_t mla_abi_version(void);
 
 /* Absorb W^UK into the query (V2 read-through section 2.3; V3 read-through
@@ -190,24 +192,12 @@ mla_status_t mla_decode_plan_mq(const mla_dims_t* dims, int32_t batch, int32_t q
  * and one query token.  A plan passed in must come from mla_decode_plan (or
  * mla_decode_plan_mq, whose q_len then sets the shapes) with the same dims,
  * batch and cache bounds.  workspace: device, >= plan->workspace_bytes, 256-byte
- * aligned; calls that share a workspace must be ordered on one stream.
- * With the MFMA kernel (plan->kernel == 1) the workspace ends with a counter
- * area (its last 256-byte-rounded batch * head_groups * 8 bytes) that must be
- * zero before the workspace is first used (hipMemset once after allocating
- * it); every call leaves it zero again.  The rest needs no initialisation.
- * How the call runs on the MFMA kernel:
- *   - one split (plan->num_splits == 1) over native rows: the decode kernel
- *     normalises its rows and writes out_lat and lse itself; the workspace
- *     is not touched;
- *   - several splits whose workgroups all fit on the device at once
- *     (batch * num_splits * head_groups, rounded up to a multiple of 8, at
- *     most the number of compute units): one launch; the splits of each
- *     (request, 128-row group) write their partial sums to the workspace,
- *     wait for each other at that group's counter and each merges a share of
- *     all of them.  Two such calls must not overlap on one device (each
- *     needs every compute unit; a wait that is never satisfied gives up
- *     after about 2^22 polls and sets that group's out_lat and lse to NaN);
- *   - otherwise mla_decode_partials followed by mla_decode_combine. */
+ * aligned, contents need no initialisation; calls that share a workspace
+ * must be ordered on one stream.  With a one-split plan on the MFMA kernel
+ * (plan->num_splits == 1, plan->kernel 1 or 2) over native rows the decode
+ * kernel normalises its rows and writes out_lat and lse itself: nothing is
+ * merged and the workspace is not touched; otherwise the call is
+ * mla_decode_partials followed by mla_decode_combine. */
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* q_cat,
                              const mla_cache_t* cache, float softmax_scale,
                              const mla_decode_plan_t* plan, void* out_lat, float* lse,

@@ -161,7 +161,8 @@ def test_plan_shapes_and_workspace_errors():
     lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
     cache = mla.latent_cache(data, lens, 64)
     plan = mla.decode_plan(128, 512, 64, torch.bfloat16, cache)
-    assert plan.kernel == 1 and plan.head_groups == 1
+    # Several splits per request: the 64-row form, two row groups per request.
+    assert plan.kernel == 2 and plan.head_groups == 2
     assert plan.split_tokens % 32 == 0 and plan.num_splits * plan.split_tokens >= T
     # bf16 partial outputs plus fp32 log-sum-exps
     assert plan.workspace_bytes >= B * plan.num_splits * 128 * (512 * 2 + 4)

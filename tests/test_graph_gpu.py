@@ -1,12 +1,10 @@
 """The decode step captured into a HIP graph through torch's graph API and
-replayed, in both forms: absorb -> mla_decode_attn (one launch, the splits
-merging each other's partials at counters in the workspace) -> W^UV, and
+replayed, in both call patterns: absorb -> mla_decode_attn -> W^UV, and
 absorb -> partials -> combine + W^UV.  Every replay must give the eager
 result bit for bit, with eager work and synchronisations between the
-replays, and a replay after the inputs change in place must follow them; the
-one-launch form must leave its counters zero after every replay.  No call of
-the step allocates, synchronises or clears memory, so the step is capturable
-as is."""
+replays, and a replay after the inputs change in place must follow them.
+No call of the step allocates, synchronises or clears memory, so the step is
+capturable as is."""
 
 import sys
 
@@ -28,7 +26,7 @@ def _log(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("form", ["one_launch", "two_phase"])
+@pytest.mark.parametrize("form", ["decode_attn", "partials_combine_out"])
 def test_step_graph_replays_match_eager(form):
     cfg = DSV2.replace(batch=6, len_lo=1, len_hi=1500, max_len=1536)
     case = make_case(cfg, 101, seq_lens=np.array([1500, 1, 700, 0, 1024, 33], np.int32))
@@ -48,17 +46,12 @@ def test_step_graph_replays_match_eager(form):
 
     def step():
         mla.absorb_q(q_c, q_r, dc.w_uk, out=q_cat)
-        if form == "one_launch":
+        if form == "decode_attn":
             mla.decode_attn(q_cat, dc.cache, cfg.scale, plan, o_lat, lse, ws)
             mla.out_uv(o_lat, dc.w_uv, out=o)
         else:
             mla.decode_partials(q_cat, dc.cache, cfg.scale, plan, ws)
             mla.decode_combine_out(dc.cache, plan, ws, dc.w_uv, o_lat, lse, out=o)
-
-    cb = (B * plan.head_groups * 8 + 255) // 256 * 256
-
-    def counters_zero():
-        return int(ws[plan.workspace_bytes - cb:plan.workspace_bytes].count_nonzero()) == 0
 
     step()
     torch.cuda.synchronize()
@@ -76,7 +69,6 @@ def test_step_graph_replays_match_eager(form):
         torch.cuda.synchronize()
         assert torch.equal(o, ref[0]) and torch.equal(o_lat, ref[1]), f"replay {rep}"
         assert torch.equal(torch.nan_to_num(lse, neginf=-1e30), torch.nan_to_num(ref[2], neginf=-1e30))
-        assert counters_zero(), f"replay {rep}"
     # New query values in the captured input buffers.
     q_c.copy_(dc2.q_c)
     q_r.copy_(dc2.q_r)

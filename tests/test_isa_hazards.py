@@ -189,8 +189,9 @@ def kernels():
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     ks = parse_kernels(r.stdout)
-    # contiguous / paged x (bf16 / low-bit rows) x (split partials, fused merge),
-    # and contiguous / paged bf16 direct
+    # 128-row groups: contiguous / paged x (bf16 / low-bit rows) split
+    # partials, and contiguous / paged bf16 direct; 64-row groups: contiguous
+    # / paged bf16 x (partials, direct)
     assert len(ks) == 10, sorted(ks)
     return ks
 
@@ -198,7 +199,7 @@ def kernels():
 def test_decode_kernel_has_no_mfma_hazards(kernels):
     for name, items in kernels.items():
         n_mfma = sum(1 for it in items if it[0] == "inst" and it[1].is_mfma)
-        assert n_mfma > 100, name
+        assert n_mfma > 60, name  # the 64-row form issues 18 + 34 + 16
         problems = check(items)
         assert not problems, f"{name}:\n" + "\n".join(problems[:20])
 

@@ -99,7 +99,8 @@ def test_bf16_causal(q_len, cfg_name, split):
     q, q_dev = _query(cfg, 40 + q_len, q_len)
     plan = mla.decode_plan(cfg.n_heads, cfg.d_latent, cfg.d_rope, torch.bfloat16, dc.cache,
                            split_tokens=split, q_len=q_len)
-    assert plan.q_len == q_len and plan.kernel == 1 and plan.head_groups == q_len
+    assert plan.q_len == q_len and plan.kernel in (1, 2)
+    assert plan.head_groups == q_len * (1 if plan.kernel == 1 else 2)
     o_lat, lse = mla.decode_attn(q_dev, dc.cache, cfg.scale, plan=plan)
     torch.cuda.synchronize()
     heads = np.arange(0, 128, 5)
@@ -195,7 +196,7 @@ def test_prefill_chunk(paged):
     q, q_dev = _query(cfg, 77, q_len)
     plan = mla.decode_plan(cfg.n_heads, cfg.d_latent, cfg.d_rope, torch.bfloat16, dc.cache,
                            q_len=q_len)
-    assert plan.kernel == 1 and plan.head_groups == q_len
+    assert plan.kernel in (1, 2) and plan.head_groups == q_len * (1 if plan.kernel == 1 else 2)
     o_lat, lse = mla.decode_attn(q_dev, dc.cache, cfg.scale, plan=plan)
     torch.cuda.synchronize()
     o_lat, lse = from_dev(o_lat), from_dev(lse)
