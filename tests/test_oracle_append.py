@@ -1,8 +1,9 @@
 """Pins for the cache-append oracle (oracle/append_ref.py), CPU only.
 
 Each pin rests on something other than the oracle's own formula: hand-worked
-rotations, identities every correct RoPE satisfies, YaRN's limiting cases,
-RMSNorm's closed forms, and brute-force scalar loops.  The planted-mistake
+rotations, identities every correct RoPE satisfies, YaRN's limiting cases and
+the linearity of its ramp in the number of turns, RMSNorm's closed forms, and
+brute-force scalar loops.  The planted-mistake
 tests check that plausible errors (a swapped sin/cos, a wrong sign, a wrong
 frequency exponent, a missing mean in RMSNorm, swapped halves of the row)
 fail at least one pin.
@@ -97,26 +98,89 @@ def test_rope_planted_mistakes_fail():
     assert rope_pin_failures(wrong_freq_rope)
 
 
-def test_yarn_frequencies():
-    d, base = 64, 10000.0
-    f = rope_frequencies(d, base)
-    # s = 1 leaves every frequency alone.
-    assert np.array_equal(rope_frequencies(d, base, 1.0), f)
-    fy = rope_frequencies(d, base, 40.0, 1.0, 32.0, 4096)
-    r = 4096 * f / (2 * math.pi)  # rotations over the original context
-    fast, slow = r > 32.0, r < 1.0
-    assert fast.any() and slow.any() and (~(fast | slow)).any()
-    # Pairs that turn more than beta times over 4K keep their frequency; pairs
-    # that turn less than alpha times are slowed down by s.
-    assert np.array_equal(fy[fast], f[fast])
-    assert np.allclose(fy[slow], f[slow] / 40.0, rtol=1e-15)
-    # In between, the frequency lies between the two and moves monotonically
-    # from f/s towards f as r grows.
+def yarn_pin_failures(freq_fn) -> list:
+    """Pins of YaRN's frequency interpolation (ai-library "DeepSeek-V2" notes,
+    "Long-Context Extension"; zeeklog notes: s = 40, alpha = 1, beta = 32 from
+    a 4K context) on freq_fn(d, base, s, alpha, beta, L): s = 1 is plain RoPE;
+    pairs that turn more than beta times over the original context keep their
+    frequency and those that turn fewer than alpha times are slowed by s; in
+    between, the blend weight h = (f'/f - 1/s) / (1 - 1/s) is an affine
+    function of the number of turns r (the ramp is linear in r), reaching 0 at
+    r = alpha and 1 at r = beta.  Returns the failures."""
+    bad = []
+    d, base, s, a, b, L = 64, 10000.0, 40.0, 1.0, 32.0, 4096
+    f = base ** (-2.0 * np.arange(d // 2) / d)
+    if not np.array_equal(freq_fn(d, base, 1.0, a, b, L), f):
+        bad.append("s = 1 changes the frequencies")
+    fy = freq_fn(d, base, s, a, b, L)
+    r = L * f / (2 * math.pi)  # rotations over the original context
+    fast, slow = r > b, r < a
     mid = ~(fast | slow)
-    ratio = fy / f
-    assert np.all(ratio[mid] > 1 / 40.0) and np.all(ratio[mid] < 1.0)
-    order = np.argsort(r[mid])
-    assert np.all(np.diff(ratio[mid][order]) > 0)
+    assert fast.any() and slow.any() and mid.sum() >= 3
+    if not np.array_equal(fy[fast], f[fast]):
+        bad.append("fast pairs changed")
+    if not np.allclose(fy[slow], f[slow] / s, rtol=1e-15):
+        bad.append("slow pairs not divided by s")
+    h = (fy / f - 1 / s) / (1 - 1 / s)
+    hm, rm = h[mid], r[mid]
+    # Affine in r: the line through the two extreme mid-band pairs predicts
+    # every other one, and it meets 0 at alpha and 1 at beta.
+    i0, i1 = np.argmin(rm), np.argmax(rm)
+    slope = (hm[i1] - hm[i0]) / (rm[i1] - rm[i0])
+    pred = hm[i0] + slope * (rm - rm[i0])
+    if not np.allclose(hm, pred, rtol=0, atol=1e-12):
+        bad.append("blend not linear in the number of turns")
+    if not (abs(hm[i0] + slope * (a - rm[i0])) < 1e-12 and
+            abs(hm[i0] + slope * (b - rm[i0]) - 1) < 1e-12):
+        bad.append("ramp does not run from alpha to beta")
+    return bad
+
+
+def test_yarn_frequencies():
+    assert yarn_pin_failures(rope_frequencies) == []
+
+
+def test_yarn_planted_mistakes_fail():
+    """Plausible slips in the ramp each fail a pin: blending the wavelengths
+    or the log frequencies instead of the frequencies, a ramp in wavelength
+    instead of turns, and the two ends of the ramp exchanged."""
+    def blend_wavelength(d, base, s, a, b, L):
+        f = rope_frequencies(d, base)
+        if s == 1.0:
+            return f
+        r = L * f / (2 * math.pi)
+        g = np.clip((r - a) / (b - a), 0, 1)
+        lam = (1 - g) * (2 * math.pi * s / f) + g * (2 * math.pi / f)
+        return 2 * math.pi / lam
+
+    def blend_log(d, base, s, a, b, L):
+        f = rope_frequencies(d, base)
+        if s == 1.0:
+            return f
+        r = L * f / (2 * math.pi)
+        g = np.clip((r - a) / (b - a), 0, 1)
+        return np.exp((1 - g) * np.log(f / s) + g * np.log(f))
+
+    def ramp_in_wavelength(d, base, s, a, b, L):
+        f = rope_frequencies(d, base)
+        if s == 1.0:
+            return f
+        lam_turns = L / (2 * math.pi / f)          # same r at the ends ...
+        r = np.where((lam_turns > a) & (lam_turns < b), L / (2 * math.pi) * f ** 0.5,
+                     lam_turns)                    # ... another measure inside
+        g = np.clip((r - a) / (b - a), 0, 1)
+        return (1 - g) * f / s + g * f
+
+    def ends_exchanged(d, base, s, a, b, L):
+        f = rope_frequencies(d, base)
+        if s == 1.0:
+            return f
+        r = L * f / (2 * math.pi)
+        g = np.clip((r - a) / (b - a), 0, 1)
+        return g * f / s + (1 - g) * f
+
+    for bad in (blend_wavelength, blend_log, ramp_in_wavelength, ends_exchanged):
+        assert yarn_pin_failures(bad), bad.__name__
 
 
 # ----------------------------------------------------------------------------

@@ -400,28 +400,28 @@ def test_scale_sign_and_zero(scale):
 def test_large_scores_rescale_path():
     """Scores that keep growing along the sequence (by ~30 in natural-log units
     over 300 tokens) push later tiles far past the running max, exercising the
-    accumulator rescale; the result must still match."""
+    accumulator rescale; the result must still match at the stated bf16
+    tolerances.  The softmax is then nearly one-hot, so o is close to single
+    cached rows: the rows are scaled by 1/4 and the query by 4 more (every
+    score unchanged), which keeps |o| at unit scale, where those tolerances
+    are stated."""
     cfg = SMALL
     lens = np.array([300, 300, 300], np.int32)
     case = make_case(cfg, 14, seq_lens=lens)
     from workload import round_to_bf16
-    q_np = round_to_bf16((draw_latent_query(cfg, 14) * 8.0).astype(np.float32))
+    q_np = round_to_bf16((draw_latent_query(cfg, 14) * 32.0).astype(np.float32))
     for b in range(cfg.batch):
         ramp = (np.arange(300, dtype=np.float32) / 1000.0)[:, None]
         case.cache[b, :300, :cfg.d_latent] += ramp * np.sign(q_np[b, 0, :cfg.d_latent])
-    case.cache = round_to_bf16(case.cache)
+    case.cache = round_to_bf16(case.cache * np.float32(0.25))
     dc = DevCase(case)
     o_lat, lse = mla.decode_attn(_bf16_dev(q_np), dc.cache, cfg.scale, split_tokens=320)
     torch.cuda.synchronize()
     o_ref, lse_ref = _latent_ref(case, q_np)
     # Head 0 of every request is the one whose scores ramp up.
     assert lse_ref[:, 0].min() > lse_ref[:, 1:].max() - 5
-    # These outputs reach |o| ~ 4.4, where one bf16 ulp is 2^-6: the absolute
-    # bound (stated for unit-scale data) is scaled by max|o|.
-    got = from_dev(o_lat)
-    scale = max(1.0, float(np.abs(o_ref).max()))
-    assert rel_l2(got, o_ref) <= 1e-2
-    assert max_abs(got, o_ref) <= 2e-2 * scale
+    assert np.abs(o_ref).max() < 1.5
+    assert_close(from_dev(o_lat), o_ref, "bf16", "o_lat")
     assert_close(from_dev(lse), lse_ref, "bf16", "lse")
 
 
