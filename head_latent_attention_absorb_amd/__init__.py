@@ -95,6 +95,12 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_attn.restype = ctypes.c_int
     L.mla_decode_attn.argtypes = [ctypes.POINTER(Dims), i32, vp, ctypes.POINTER(CacheDesc),
                                   ctypes.c_float, ctypes.POINTER(Plan), vp, vp, vp, sz, vp]
+    L.mla_decode_attn_noalloc.restype = ctypes.c_int
+    L.mla_decode_attn_noalloc.argtypes = [ctypes.POINTER(Dims), i32, vp,
+                                          ctypes.POINTER(CacheDesc), ctypes.c_float,
+                                          ctypes.POINTER(Plan), vp, vp, vp]
+    L.mla_decode_noalloc_max_bytes.restype = sz
+    L.mla_decode_noalloc_max_bytes.argtypes = []
     L.mla_decode_partials.restype = ctypes.c_int
     L.mla_decode_partials.argtypes = [ctypes.POINTER(Dims), i32, vp, ctypes.POINTER(CacheDesc),
                                       ctypes.c_float, ctypes.POINTER(Plan), vp, sz, vp]
@@ -312,6 +318,37 @@ def decode_attn(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,
         ctypes.byref(dims), B, _ptr(q_cat), ctypes.byref(desc), float(softmax_scale),
         ctypes.byref(plan), _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def decode_attn_noalloc(q_cat: torch.Tensor, cache: LatentCache, softmax_scale: float,
+                        plan: Optional[Plan] = None, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, stream=None,
+                        split_tokens: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_attn_noalloc: decode_attn with the library's static device
+    workspace (no workspace argument; the C call allocates nothing).  Pass
+    `out` and `lse` to keep the whole call allocation-free."""
+    B, q_len, nh, row = _query_shape(q_cat, plan)
+    if cache.data.shape[2] != row:
+        raise ValueError(f"cache row width {cache.data.shape[2]} != q_cat width {row}")
+    d_rope = int(cache.d_rope)
+    d_latent = row - d_rope
+    dev = q_cat.device
+    _require(cache.seq_lens, "seq_lens", (B,), torch.int32, dev)
+    dims = make_dims(nh, 1, d_rope, d_latent, _dtype_code(q_cat))
+    desc = cache.desc()
+    if plan is None:
+        plan = decode_plan(nh, d_latent, d_rope, q_cat.dtype, cache, split_tokens, q_len=q_len)
+    lead = _lead(B, q_len, q_cat.dim() == 4)
+    if out is None:
+        out = torch.empty(lead + (nh, d_latent), dtype=q_cat.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(lead + (nh,), dtype=torch.float32, device=dev)
+    _require(out, "out", lead + (nh, d_latent), q_cat.dtype, dev)
+    _require(lse, "lse", lead + (nh,), torch.float32, dev)
+    _check("mla_decode_attn_noalloc", lib().mla_decode_attn_noalloc(
+        ctypes.byref(dims), B, _ptr(q_cat), ctypes.byref(desc), float(softmax_scale),
+        ctypes.byref(plan), _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

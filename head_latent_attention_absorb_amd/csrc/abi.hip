@@ -14,10 +14,18 @@ using mla::DecodeArgs;
 
 constexpr int kMaxDevices = 64;
 
+// Workspace of mla_decode_attn_noalloc: a static device array, one copy per
+// device the library runs on, held until the process ends.  Host code never
+// passes `scratch` itself (on the host it is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, once per device, below.
+constexpr size_t kScratchBytes = size_t{48} << 20;
+__device__ __align__(256) static uint8_t scratch[kScratchBytes];
+
 struct DeviceInfo {
   bool valid = false;
   bool gfx950 = false;
   int cus = 0;
+  void* scratch = nullptr;  // device address of `scratch` (null if the lookup failed)
 };
 
 std::mutex g_dev_mu;
@@ -34,6 +42,11 @@ mla_status_t current_device(DeviceInfo* out) {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_DEVICE;
     d.cus = prop.multiProcessorCount;
     d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (d.gfx950) {
+      void* ptr = nullptr;
+      d.scratch = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess ? ptr : nullptr;
+      (void)hipGetLastError();
+    }
     d.valid = true;
   }
   if (!d.gfx950) return MLA_ERR_DEVICE;
@@ -384,6 +397,22 @@ mla_status_t mla_decode_combine(const mla_dims_t* dims, int32_t batch, const mla
   (void)hipGetLastError();
   return run_combine(a, p);
 }
+
+mla_status_t mla_decode_attn_noalloc(const mla_dims_t* dims, int32_t batch, const void* q_cat,
+                                     const mla_cache_t* cache, float softmax_scale,
+                                     const mla_decode_plan_t* plan, void* out_lat, float* lse,
+                                     void* stream) {
+  DeviceInfo dev;
+  mla_status_t st = current_device(&dev);
+  if (st != MLA_OK) return st;
+  if (dev.scratch == nullptr) return MLA_ERR_DEVICE;
+  // The plan's workspace must fit the static array; prepare_decode (through
+  // mla_decode_attn) returns MLA_ERR_WORKSPACE otherwise.
+  return mla_decode_attn(dims, batch, q_cat, cache, softmax_scale, plan, out_lat, lse,
+                         dev.scratch, kScratchBytes, stream);
+}
+
+size_t mla_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* q_cat,
                              const mla_cache_t* cache, float softmax_scale,

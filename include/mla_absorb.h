@@ -203,6 +203,25 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* 
                              const mla_decode_plan_t* plan, void* out_lat, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* mla_decode_attn for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments and errors, with no workspace argument.  The
+ * workspace is a static device array in the library, 48 MiB
+ * (mla_decode_noalloc_max_bytes()), one copy per device, held from the first
+ * call on that device until the process ends; the call allocates nothing.  A
+ * plan whose workspace_bytes exceed it -> MLA_ERR_WORKSPACE (nothing is
+ * enqueued); MLA_ERR_DEVICE if the array's device address cannot be found.
+ * Every call on one device shares its array: calls that may overlap on one
+ * device (different streams) race and must not be issued; the array's
+ * contents need no initialisation and are left undefined. */
+mla_status_t mla_decode_attn_noalloc(const mla_dims_t* dims, int32_t batch, const void* q_cat,
+                                     const mla_cache_t* cache, float softmax_scale,
+                                     const mla_decode_plan_t* plan, void* out_lat, float* lse,
+                                     void* stream);
+
+/* Size in bytes of mla_decode_attn_noalloc's static workspace (48 MiB). */
+size_t mla_decode_noalloc_max_bytes(void);
+
 /* The two phases of mla_decode_attn, for callers that merge partial results
  * themselves (for example across devices that each hold a slice of a long
  * cache) or time them separately.  mla_decode_attn(...) is exactly
