@@ -129,16 +129,14 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_counters(sha: str):
-    """HBM bytes per launch of the decode kernel from committed rocprofv3 PMC
-    counters, or None when absent or taken on a different kernel source."""
+def counters_for(sha: str):
+    """The committed rocprofv3 PMC counters of the decode kernel, or {} when
+    absent or taken on a different kernel source."""
     if not os.path.exists(COUNTERS_FILE):
-        return None
+        return {}
     with open(COUNTERS_FILE) as f:
         c = json.load(f)
-    if c.get("kernel_source_sha") != sha:
-        return None
-    return c.get("hbm_bytes_per_launch")
+    return c if c.get("kernel_source_sha") == sha else {}
 
 
 def cpu_baseline(entry: Entry, cfg, n_requests: int, min_seconds: float = 8.0):
@@ -607,6 +605,7 @@ def main():
     t_roof_us = max(step_bytes / (HBM_PEAK_GBPS * 1e9),
                     step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
     sha = kernel_sha()
+    counters = counters_for(sha) if name == WORKLOAD else {}
 
     result = {
         "metric": METRIC if name == WORKLOAD else
@@ -663,7 +662,13 @@ def main():
             "frac": (k2_tflops / MFMA_BF16_PEAK_TFLOPS if k2_mfma_bound
                      else k2_gbps / HBM_PEAK_GBPS),
             "achieved_GBps": k2_gbps,
-            "traffic": traffic_from_counters(sha) if name == WORKLOAD else None,
+            # Counter-measured (rocprofv3 --pmc, same kernel source only):
+            # HBM bytes per launch (FETCH_SIZE, WRITE_SIZE scaled by a plain
+            # copy's), the MFMA busy fraction (rocprofv3's MfmaUtil) and the
+            # MFMA flops the SQ counted.
+            "traffic": counters.get("hbm_bytes_per_launch"),
+            "mfma_util": counters.get("mfma", {}).get("mfma_util"),
+            "mfma_flops_counted": counters.get("mfma", {}).get("mfma_flops_counted"),
             "alg_bytes_per_launch": k2_bytes,
             "launch_us": decode_us,
             "mfma_tflops": k2_tflops,
