@@ -421,7 +421,7 @@ def main():
     lse = torch.empty(lead + (nh,), dtype=torch.float32, device=dev)
     o = torch.empty(lead + (nh, cfg.d_head), dtype=torch.bfloat16, device=dev)
     q_rows = q_cat.view(B * ql, nh, row)
-    direct = plan.num_splits == 1
+    direct = plan.direct
     form = f"{128 if plan.kernel == 1 else 64} query rows per workgroup"
     stream = torch.cuda.current_stream()
 

@@ -44,13 +44,24 @@ class CacheDesc(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [("split_tokens", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("kernel", ctypes.c_int32), ("head_groups", ctypes.c_int32),
-                ("q_len", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+                ("q_len", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+                ("partitions", ctypes.c_int32)]
+
+    @property
+    def balanced(self) -> bool:
+        """Partitions sized on the device from the lengths (split_tokens 0)."""
+        return self.split_tokens == 0
+
+    @property
+    def direct(self) -> bool:
+        """One uniform split per request: the decode kernel writes o_lat itself."""
+        return self.split_tokens > 0 and self.num_splits == 1 and self.kernel >= 1
 
     def __repr__(self):
         return (f"Plan(split_tokens={self.split_tokens}, num_splits={self.num_splits}, "
                 f"kernel={ {0: 'generic', 1: 'mfma-128rows', 2: 'mfma-64rows'}.get(self.kernel, self.kernel)}, "
                 f"head_groups={self.head_groups}, q_len={self.q_len}, "
-                f"workspace_bytes={self.workspace_bytes})")
+                f"workspace_bytes={self.workspace_bytes}, partitions={self.partitions})")
 
 
 class Rope(ctypes.Structure):

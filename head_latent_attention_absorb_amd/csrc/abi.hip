@@ -1,6 +1,7 @@
 // C ABI of the MLA absorbed-decode library: argument checks, split-KV
 // planning and kernel dispatch.  Declared in include/mla_absorb.h.
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <string.h>
@@ -100,18 +101,56 @@ size_t partial_elem_bytes(bool mfma) { return mfma ? 2 : sizeof(float); }
 // MFMA kernel the pair (log-sum-exp, reference max) of its unnormalised sum.
 size_t partial_stat_bytes(bool mfma) { return mfma ? 2 * sizeof(float) : sizeof(float); }
 
-// Workspace layout: partial rows, then their statistics.
-size_t partials_bytes(const mla_dims_t* d, int batch, int q_len, int num_splits, bool mfma) {
-  const size_t parts = static_cast<size_t>(batch) * num_splits * q_len * d->n_heads;
+// Workspace layout: partial rows of `partitions` (request, partition) pairs,
+// then their statistics, then (length-balanced plans) the partition table:
+// the partition length, each request's first partition and the count.
+size_t partials_bytes(const mla_dims_t* d, int q_len, int partitions, bool mfma) {
+  const size_t parts = static_cast<size_t>(partitions) * q_len * d->n_heads;
   return round256(parts * d->d_latent * partial_elem_bytes(mfma));
 }
-size_t stats_bytes(const mla_dims_t* d, int batch, int q_len, int num_splits, bool mfma) {
-  const size_t parts = static_cast<size_t>(batch) * num_splits * q_len * d->n_heads;
+size_t stats_bytes(const mla_dims_t* d, int q_len, int partitions, bool mfma) {
+  const size_t parts = static_cast<size_t>(partitions) * q_len * d->n_heads;
   return round256(parts * partial_stat_bytes(mfma));
 }
-size_t workspace_for(const mla_dims_t* d, int batch, int q_len, int num_splits, bool mfma) {
-  return partials_bytes(d, batch, q_len, num_splits, mfma) +
-         stats_bytes(d, batch, q_len, num_splits, mfma);
+size_t table_bytes(int batch, bool balanced) {
+  return balanced ? round256((static_cast<size_t>(batch) + 2) * sizeof(int32_t)) : 0;
+}
+size_t workspace_for(const mla_dims_t* d, int batch, int q_len, int partitions, bool mfma,
+                     bool balanced) {
+  return partials_bytes(d, q_len, partitions, mfma) + stats_bytes(d, q_len, partitions, mfma) +
+         table_bytes(batch, balanced);
+}
+
+// Bounds of a length-balanced plan: about `target` partitions (one
+// workgroup per compute unit), each at most c_max tokens, and the room the
+// launch keeps for them.
+struct BalancedBounds {
+  int target, c_max, capacity;
+};
+
+// Longest partition the kernels take: the cache's length rounded up to the
+// kernel's token granule; on the MFMA kernel over a paged cache at most 63
+// pages' worth (it keeps a partition's page ids in one register per lane,
+// so a partition may touch at most 64 pages).
+int partition_cap(const mla_cache_t* c, bool mfma) {
+  const int granule = mfma ? mla::kMfmaTokenGranule : 1;
+  const int max_len = c->max_len;
+  int cap = max_len > 0 ? (max_len + granule - 1) / granule * granule : granule;
+  if (mfma && c->page_table != nullptr)
+    cap = std::min(cap, (63 * c->page_size) / granule * granule);
+  return cap;
+}
+
+BalancedBounds balanced_bounds(int batch, int groups, int c_max, int max_len,
+                               const DeviceInfo& dev) {
+  BalancedBounds bb;
+  bb.target = std::max(1, dev.cus / groups);
+  bb.c_max = c_max;
+  // With c capped at c_max a request takes up to ceil(max_len / c_max)
+  // partitions, whatever the target.
+  const int per_request = max_len > 0 ? (max_len + c_max - 1) / c_max : 1;
+  bb.capacity = std::max(bb.target, batch * per_request);
+  return bb;
 }
 
 // form: -1 lets the planner choose the kernel form; 0, 1 or 2 asks for that
@@ -125,7 +164,7 @@ mla_status_t make_plan(const mla_dims_t* d, int batch, int q_len, const mla_cach
   const bool mfma = use_mfma(d, c);
   const int granule = mfma ? mla::kMfmaTokenGranule : 1;
   const int max_len = c->max_len;
-  const int len_cap = max_len > 0 ? (max_len + granule - 1) / granule * granule : granule;
+  const int c_max = partition_cap(c, mfma);
   // Split length for `groups` row groups per request: the caller's, or about
   // one workgroup per compute unit when every request is at max_len.
   auto choose_split = [&](int groups) {
@@ -141,14 +180,7 @@ mla_status_t make_plan(const mla_dims_t* d, int batch, int q_len, const mla_cach
       const int floor_tokens = mfma ? 2 * granule : 64;
       if (split < floor_tokens) split = floor_tokens;
     }
-    if (split > len_cap) split = len_cap;
-    if (mfma && c->page_table != nullptr) {
-      // The MFMA kernel keeps a partition's page ids in one register per
-      // lane: a partition may touch at most 64 pages.
-      const int max_split = (63 * c->page_size) / granule * granule;
-      if (split > max_split) split = max_split;
-    }
-    return split;
+    return std::min(split, c_max);
   };
   auto splits_of = [&](int split) { return max_len > 0 ? (max_len + split - 1) / split : 1; };
   // MFMA: 128 query rows per workgroup, or 64 when the 128-row plan has
@@ -171,14 +203,29 @@ mla_status_t make_plan(const mla_dims_t* d, int batch, int q_len, const mla_cach
     return MLA_ERR_DIMS;
   }
   const int groups = q_len * d->n_heads / rows;
-  const int split = choose_split(groups);
-  const int num_splits = splits_of(split);
-  plan->split_tokens = split;
-  plan->num_splits = num_splits;
   plan->kernel = kernel;
   plan->head_groups = groups;
   plan->q_len = q_len;
-  plan->workspace_bytes = workspace_for(d, batch, q_len, num_splits, mfma);
+  // Length-balanced partitions when the requests alone leave compute units
+  // idle: the device then sizes the partitions from the actual lengths
+  // (a uniform cut sized from max_len leaves the units of short requests
+  // idle and makes the longest request's partitions the critical path).
+  const bool balanced = mfma && split_req == 0 && batch >= 1 &&
+                        batch <= mla::kBalancedMaxBatch && max_len <= mla::kBalancedMaxLen &&
+                        static_cast<long long>(batch) * groups < dev.cus;
+  if (balanced) {
+    const BalancedBounds bb = balanced_bounds(batch, groups, c_max, max_len, dev);
+    plan->split_tokens = 0;
+    plan->num_splits = std::min(bb.capacity, std::max(1, (max_len + granule - 1) / granule));
+    plan->partitions = bb.capacity;
+  } else {
+    const int split = choose_split(groups);
+    plan->split_tokens = split;
+    plan->num_splits = splits_of(split);
+    plan->partitions = batch * plan->num_splits;
+  }
+  plan->workspace_bytes =
+      workspace_for(d, batch, q_len, plan->partitions, mfma, plan->split_tokens == 0);
   return MLA_OK;
 }
 
@@ -200,7 +247,7 @@ const char* mla_status_str(mla_status_t s) {
   return "MLA_ERR_UNKNOWN";
 }
 
-int32_t mla_abi_version(void) { return 5; }
+int32_t mla_abi_version(void) { return 6; }
 
 mla_status_t mla_quantize_rows(int64_t n_rows, int32_t width, int32_t src_dtype, const void* src,
                                void* dst, float* scales, void* stream) {
@@ -315,15 +362,14 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
     if (plan_out->split_tokens != plan->split_tokens ||
         plan_out->num_splits != plan->num_splits || plan_out->kernel != plan->kernel ||
         plan_out->head_groups != plan->head_groups || plan_out->q_len != plan->q_len ||
-        plan_out->workspace_bytes != plan->workspace_bytes)
+        plan_out->workspace_bytes != plan->workspace_bytes ||
+        plan_out->partitions != plan->partitions)
       return MLA_ERR_DIMS;
   }
   if (workspace == nullptr || workspace_bytes < plan_out->workspace_bytes)
     return MLA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MLA_ERR_ALIGN;
 
-  const size_t parts_n =
-      static_cast<size_t>(batch) * plan_out->num_splits * plan_out->q_len * dims->n_heads;
   a->batch = batch;
   a->n_heads = dims->n_heads;
   a->q_len = plan_out->q_len;
@@ -348,10 +394,18 @@ mla_status_t prepare_decode(const mla_dims_t* dims, int32_t batch, const void* q
   a->lse = lse;
   const bool mfma = plan_out->kernel >= 1;
   uint8_t* ws = static_cast<uint8_t*>(const_cast<void*>(workspace));
-  const size_t pb = partials_bytes(dims, batch, plan_out->q_len, plan_out->num_splits, mfma);
-  (void)parts_n;
+  const size_t pb = partials_bytes(dims, plan_out->q_len, plan_out->partitions, mfma);
+  const size_t sb = stats_bytes(dims, plan_out->q_len, plan_out->partitions, mfma);
   a->part_o = ws;
   a->part_lse = reinterpret_cast<float*>(ws + pb);
+  a->partitions = plan_out->partitions;
+  if (plan_out->split_tokens == 0) {
+    const BalancedBounds bb = balanced_bounds(batch, plan_out->head_groups,
+                                              partition_cap(cache, true), cache->max_len, dev);
+    a->part_target = bb.target;
+    a->part_max_tokens = bb.c_max;
+    a->part_table = reinterpret_cast<int32_t*>(ws + pb + sb);
+  }
   a->stream = static_cast<hipStream_t>(stream);
   return MLA_OK;
 }
@@ -427,7 +481,8 @@ mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* 
   (void)hipGetLastError();
   // One split per request: the MFMA kernel normalises its rows itself and
   // writes o_lat and lse, so there is nothing to merge.
-  a.direct = p.kernel >= 1 && p.num_splits == 1 && cache->row_format == MLA_ROWS_NATIVE;
+  a.direct = p.kernel >= 1 && p.split_tokens > 0 && p.num_splits == 1 &&
+             cache->row_format == MLA_ROWS_NATIVE;
   if ((st = run_partials(a, p)) != MLA_OK || a.direct) return st;
   return run_combine(a, p);
 }

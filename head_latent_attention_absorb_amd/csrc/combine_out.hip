@@ -16,10 +16,12 @@
 //   out[b, i, h] = sum_c o_lat[b, i, c] W^UV[i, c, h].
 //
 // One workgroup = one head i and R = 8 / P requests (8 waves, P waves per
-// request).  The MFMA partials are row-major bf16,
-// part_o[((b * n_rows + i) * S + s) * 512 + c], so every (request, split)
+// request).  The MFMA partials are row-major bf16, partition-major,
+// part_o[((off_b + s) * n_rows + i) * 512 + c], so every (request, split)
 // contributes one contiguous 1 KiB row; (lse_s, m_s) are an fp32 pair per
-// (request, split, head).  Wave p of a request merges splits p, p + P,
+// (partition, head).  off_b is b * S in a uniform plan; in a length-balanced
+// one the decode kernel leaves the partition length and every off_b in a
+// table behind the statistics.  Wave p of a request merges splits p, p + P,
 // p + 2P, ..., 8 latents per lane, with the loads of up to kBatch splits
 // (rows and statistics) in flight at once; with P > 1 the waves of a request
 // then merge their results through LDS.  P grows with the split count, so
@@ -59,8 +61,9 @@ template <bool kOut, int kB>
 __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
     const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, int batch, int n_rows, int heads_per_token, int q_len,
-    int split_tokens,
-    int num_splits, int p_log2, __bf16* __restrict__ out_lat, float* __restrict__ lse_out,
+    int split_tokens, int num_splits, const int32_t* __restrict__ part_table, int partitions,
+    int p_log2,
+    __bf16* __restrict__ out_lat, float* __restrict__ lse_out,
     const __bf16* __restrict__ w_uv, __bf16* __restrict__ out, int d_head) {
   __shared__ __attribute__((aligned(16))) uint8_t w_s[kOut ? kWBytes : 16];
   __shared__ __attribute__((aligned(16))) __bf16 o_s[kOut ? kRowsPerGroup * kOStride : 8];
@@ -99,8 +102,24 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   const bool live = b < batch;
   // The rows this query token sees: up to its own position.
   const int len = live ? seq_lens[b] - (q_len - 1 - i / heads_per_token) : 0;
-  // Split-minor partials: the S rows and statistics of (b, i) are contiguous.
-  const size_t lbase = (static_cast<size_t>(live ? b : 0) * n_rows + i) * num_splits;
+  // Partition length and the request's first partition.  A uniform plan
+  // knows both on the host; a length-balanced one reads them from the
+  // table, and then also its split count (one memory round trip in front of
+  // the partial loads, which therefore cover the used splits only).
+  int c = split_tokens, nk;
+  size_t pbase;
+  if (part_table != nullptr) {
+    c = part_table[0];
+    const int first = part_table[1 + (live ? b : 0)];
+    pbase = static_cast<size_t>(first);
+    // (the table's partitions lie within the launch's capacity)
+    const int used = min(used_splits(len, c), partitions - first);
+    nk = max(0, (used - p + P - 1) >> p_log2);
+  } else {
+    pbase = static_cast<size_t>(live ? b : 0) * num_splits;
+    nk = (num_splits - p + P - 1) >> p_log2;
+  }
+  const size_t lbase = pbase * n_rows + i;  // partition pbase's row i
   // This wave's splits are p + k * P, k < nk.  Single pass with a running max
   // over batches of kB of them.  The loads of a batch (rows and statistics)
   // are issued together with the length load, without waiting for it and
@@ -110,13 +129,12 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   // the request's length (never written: any bits) are dropped with selects
   // afterwards.  A wave's merge of its splits costs ceil(nk / kB) memory round
   // trips.
-  const int nk = (num_splits - p + P - 1) >> p_log2;
   float L = -INFINITY, W = 0.f;
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
   const uint16_t* row = part_o + lbase * kLat + seg * 8;
-  const size_t split_stride = kLat;
+  const size_t split_stride = static_cast<size_t>(n_rows) * kLat;
   int ns = 0;
   // One batch: returns false once the batch starts past the used splits.
   auto merge_batch = [&](int k0) {
@@ -126,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
     for (int j = 0; j < kB; ++j) {
       const size_t sidx = static_cast<size_t>(p + (min(k0 + j, nk - 1) << p_log2));
       v[j] = *reinterpret_cast<const bf16x8_t*>(row + sidx * split_stride);
-      const float2 ml = part_ml[lbase + sidx];
+      const float2 ml = part_ml[lbase + sidx * n_rows];
       x[j] = ml.x;
       y[j] = ml.y;
     }
@@ -134,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
     // compiler does not hoist its wait in front of them).
     int len_k = len;
     asm volatile("" : "+v"(len_k));
-    ns = used_splits(len_k, split_tokens);
+    ns = used_splits(len_k, c);
     if (p + (k0 << p_log2) >= ns) return false;
     bool use[kB];
 #pragma unroll
@@ -294,15 +312,22 @@ void launch_rows(const DecodeArgs& a, int p_log2, const dim3& grid, const void* 
   combine_rows_kernel<kOut, kB><<<grid, kThreads, 0, a.stream>>>(
       static_cast<const uint16_t*>(a.part_o), reinterpret_cast<const float2*>(a.part_lse),
       a.cache.seq_lens, a.batch, a.q_len * a.n_heads, a.n_heads, a.q_len, a.split_tokens,
-      a.num_splits, p_log2,
+      a.num_splits, a.split_tokens == 0 ? a.part_table : nullptr, a.partitions, p_log2,
       static_cast<__bf16*>(a.out_lat), a.lse, static_cast<const __bf16*>(w_uv),
       static_cast<__bf16*>(out), d_head);
+}
+
+// Splits per request the launch shape is sized for: all of them in a
+// uniform plan; in a length-balanced one the mean over the requests (a
+// request with more takes more batches of loads).
+int sizing_splits(const DecodeArgs& a) {
+  return a.split_tokens == 0 ? (a.partitions + a.batch - 1) / a.batch : a.num_splits;
 }
 
 template <bool kOut>
 void launch_rows_sized(const DecodeArgs& a, int p_log2, const dim3& grid, const void* w_uv,
                        void* out, int d_head) {
-  const int nk = (a.num_splits + (1 << p_log2) - 1) >> p_log2;  // splits of wave 0
+  const int nk = (sizing_splits(a) + (1 << p_log2) - 1) >> p_log2;  // splits of wave 0
   if (nk <= 2)
     launch_rows<kOut, 2>(a, p_log2, grid, w_uv, out, d_head);
   else if (nk <= 4)
@@ -327,7 +352,8 @@ hipError_t launch_combine_rows(const DecodeArgs& a, const void* w_uv, void* out,
   // head (counting every query token's rows): each of them streams its own
   // copy of W^UV[i] into LDS.
   int p_log2 = 0;
-  while (p_log2 < 3 && (a.num_splits + (1 << p_log2) - 1) >> p_log2 > kBatch) ++p_log2;
+  const int splits = sizing_splits(a);
+  while (p_log2 < 3 && (splits + (1 << p_log2) - 1) >> p_log2 > kBatch) ++p_log2;
   if (w_uv != nullptr)
     while (p_log2 > 0 &&
            a.q_len * ((a.batch + (kWaves >> p_log2) - 1) / (kWaves >> p_log2)) > 4)

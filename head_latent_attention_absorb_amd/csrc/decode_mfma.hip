@@ -101,6 +101,11 @@ struct MfmaParams {
   // Query rows per request: q_len tokens x heads_per_token heads, token-major.
   int n_rows, heads_per_token, q_len;
   int split_tokens, num_splits, head_groups, work_items;
+  // Length-balanced partitions (split_tokens == 0): about part_target
+  // partitions of at most part_max_tokens tokens, sized from the lengths of
+  // the batch requests; the partition table goes to part_table.
+  int batch, part_target, part_max_tokens;
+  int32_t* part_table;
   float scale_log2;       // softmax scale * log2(e)
   uint16_t* part_o;       // bf16 partials
   float2* part_ml;        // per (request, split, head): (base-2 log-sum-exp, m)
@@ -239,6 +244,131 @@ __device__ __forceinline__ int swz(int n, int chunk) {
   return (((chunk >> 3) * kTile + n) << 7) + (((chunk & 7) ^ swz_key(n)) << 4);
 }
 
+// Length-balanced partitions.  Cutting a request's rows into partitions
+// leaves the merged result unchanged up to rounding, so a launch may choose
+// the cut from the lengths themselves, on the device: one partition length c
+// for the whole batch, a multiple of 32 tokens, the smallest at which the
+// partition counts n_b = ceil(len_b / c) add up to at most `target` (one
+// workgroup per compute unit), capped at c_max (then the launch's capacity,
+// sized on the host for that cap, holds them).  Requests own consecutive
+// partition numbers, request b from off_b = n_0 + ... + n_(b-1).  Every wave
+// computes this on its own from seq_lens (lane l keeps the lengths of
+// requests kPer*l .. kPer*l + kPer-1 in registers; kPer = 1 up to 64
+// requests, 4 up to 256), with register-only cross-lane arithmetic (DPP,
+// lane swaps, ballots), so it costs a few hundred cycles and neither a
+// launch nor a host synchronisation.
+struct Partition {
+  int b = -1, s = 0, c = 32;  // b < 0: the item is past the last partition
+};
+
+// Sum over the wave, in every lane: within each row of 16 lanes by DPP lane
+// permutations (pairs, quads, halves of the row, the row), then across rows
+// with the 16- and 32-lane swaps (each adds a row group to its partner).
+__device__ __forceinline__ int wave_sum_int(int v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xf, 0xf, false);  // row_mirror
+  const unsigned u = static_cast<unsigned>(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned w = r16[0] + r16[1];
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return static_cast<int>(r32[0] + r32[1]);
+}
+
+// Sum of v over the lanes below this one (v >= 0), one bit plane at a time:
+// mbcnt counts the lanes below with the bit set.
+__device__ __forceinline__ int wave_exclusive_sum(int v) {
+  int excl = 0;
+  for (int bit = 0; bit < 31; ++bit) {
+    if (__ballot((v >> bit) != 0) == 0) break;
+    const unsigned long long m = __ballot(((v >> bit) & 1) != 0);
+    const int below = __builtin_amdgcn_mbcnt_hi(
+        static_cast<unsigned>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
+    excl += below << bit;
+  }
+  return excl;
+}
+
+// ceil(len / c) for 0 <= len <= 2^22 and 32 <= c (c a multiple of 32), with
+// rc ~ 1 / c: the fp32 quotient is within 1/8 of the exact one, which one
+// correction step each way absorbs.
+__device__ __forceinline__ int ceil_div_len(int len, int c, float rc) {
+  int q = static_cast<int>(static_cast<float>(len) * rc);
+  int r = len - q * c;
+  if (r < 0) { --q; r += c; }
+  if (r >= c) { ++q; r -= c; }
+  return q + (r > 0 ? 1 : 0);
+}
+
+template <int kPer>
+__device__ Partition balanced_partition(const int32_t* __restrict__ seq_lens, int batch,
+                                        int target, int c_max, int item, int lane,
+                                        int32_t* table) {
+  int len[kPer];
+  int sum = 0, nz = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int bb = lane * kPer + k;
+    len[k] = bb < batch ? seq_lens[bb] : 0;
+    sum += len[k];
+    nz += len[k] > 0 ? 1 : 0;
+  }
+  sum = wave_sum_int(sum);
+  nz = wave_sum_int(nz);
+  auto count = [&](int c) {
+    const float rc = __builtin_amdgcn_rcpf(static_cast<float>(c));
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) n += ceil_div_len(len[k], c, rc);
+    return wave_sum_int(n);
+  };
+  auto up32 = [](int x) { return (x + 31) / 32 * 32; };
+  // sum / target bounds c from below; sum / (target - nz) from above
+  // (n_b < len_b / c + 1 for every non-empty request).  Equal lengths meet
+  // the target at the lower bound, so that is tried first.
+  int lo = max(32, up32((sum + target - 1) / target));
+  int hi = target > nz ? up32((sum + (target - nz) - 1) / (target - nz)) : c_max;
+  hi = max(32, min(hi, c_max));
+  lo = min(lo, hi);
+  if (count(lo) > target) {
+    lo += 32;
+    while (lo < hi) {
+      const int mid = lo + (hi - lo) / 64 * 32;
+      if (count(mid) <= target) hi = mid; else lo = mid + 32;
+    }
+  }
+  const int c = lo;
+  const float rc = __builtin_amdgcn_rcpf(static_cast<float>(c));
+  int n[kPer], tot = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    n[k] = ceil_div_len(len[k], c, rc);
+    tot += n[k];
+  }
+  int off = wave_exclusive_sum(tot), mine = -1;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if (table != nullptr && lane * kPer + k < batch) table[1 + lane * kPer + k] = off;
+    // request (< 256) and partition (< 2^22 / 32) packed in one lane value
+    if (item >= off && item < off + n[k]) mine = (lane * kPer + k) << 23 | (item - off);
+    off += n[k];
+  }
+  if (table != nullptr && lane == 63) {
+    table[0] = c;
+    table[1 + batch] = off;  // lane 63's running sum is the total
+  }
+  Partition pt;
+  pt.c = c;
+  const unsigned long long hit = __ballot(mine >= 0);
+  if (hit != 0) {
+    const int v = __shfl(mine, __ffsll(static_cast<long long>(hit)) - 1, 64);
+    pt.b = v >> 23;
+    pt.s = v & 0x7fffff;
+  }
+  return pt;
+}
+
 // kDirect: one split, the rows are normalised and written to out_lat (with
 // lse) instead of partials; a separate instantiation keeps that epilogue out
 // of the split kernels.
@@ -281,15 +411,37 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
   if (work >= p.work_items) return;
   const int g = work % p.head_groups;
-  const int rest = work / p.head_groups;
-  const int s = rest % p.num_splits;
-  const int b = rest / p.num_splits;
+  const int item = work / p.head_groups;
+  // Partition `item` (all head groups of a partition are consecutive work
+  // ids, so they share an XCD): request b, its partition s of c tokens, and
+  // its number pidx in the partial layout.
+  int b, s, c, pidx;
+  if (p.split_tokens == 0) {
+    int32_t* table = work == 0 && wave == 0 ? p.part_table : nullptr;
+    const Partition pt =
+        p.batch <= 64 ? balanced_partition<1>(p.cache.seq_lens, p.batch, p.part_target,
+                                              p.part_max_tokens, item, lane, table)
+                      : balanced_partition<4>(p.cache.seq_lens, p.batch, p.part_target,
+                                              p.part_max_tokens, item, lane, table);
+    // The same in every lane; readfirstlane tells the compiler so (the
+    // addresses built from them stay in scalar registers).
+    b = __builtin_amdgcn_readfirstlane(pt.b);
+    if (b < 0) return;
+    s = __builtin_amdgcn_readfirstlane(pt.s);
+    c = __builtin_amdgcn_readfirstlane(pt.c);
+    pidx = item;
+  } else {
+    s = item % p.num_splits;
+    b = item / p.num_splits;
+    c = p.split_tokens;
+    pidx = item;
+  }
 
   // Query token j of the request (head group g covers rows g*kGH ..) sees
   // the rows up to its own position: q_len - 1 - j fewer than the request.
   const int len = p.cache.seq_lens[b] - (p.q_len - 1 - g * kGH / p.heads_per_token);
-  const int t0 = s * p.split_tokens;
-  const int t1 = min(t0 + p.split_tokens, len);
+  const int t0 = s * c;
+  const int t1 = min(t0 + c, len);
   const int hblock = g * (kGH / 32) + hb;
   const int head = hblock * 32 + l32;
   if (t0 >= t1) {
@@ -927,8 +1079,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   l = halves_sum(l);
 
   constexpr bool direct = kDirect;
-  // bf16 partial, split-minor per (request, row, split):
-  // part_o[((b * n_rows + row) * S + s) * 512 + c], written as accumulated
+  // bf16 partial, partition-major: part_o[(pidx * n_rows + row) * 512 + c]
+  // (with one split per request pidx = b, the layout of out_lat), written as
+  // accumulated
   // (relative to the running max m, not divided by l: the combine applies
   // both factors as one weight, which saves a multiply per element here).
   // Register v of latent block cb holds column cb*32 + (v/4)*8 + half*4 +
@@ -953,16 +1106,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
                                    ((kh * kWCB + cb) * 32 + gq * 8 + half * 4) * 2) = v4;
     }
   if constexpr (kHalf) __syncthreads();
-  // Split-minor layout: the S partial rows of one (request, row) are
-  // contiguous, so the combine reads each merge as one run.  With one split
-  // that is also the layout of out_lat.
+  // The workgroup's rows of one partition are contiguous.
   constexpr int kStRows = kHalf ? 16 : 32;  // rows this wave stores
-  const int splits = direct ? 1 : p.num_splits;
   uint16_t* dst = (direct ? p.out_lat : p.part_o) +
-                  ((static_cast<size_t>(b) * p.n_rows + hblock * 32 + kh * kStRows) * splits +
-                   (direct ? 0 : s)) * 512 +
+                  (static_cast<size_t>(pidx) * p.n_rows + hblock * 32 + kh * kStRows) * 512 +
                   lane * 8;
-  const size_t row_stride = static_cast<size_t>(splits) * 512;
+  constexpr size_t row_stride = 512;
   // Plain stores: the combine that reads the partials right after this
   // kernel finds them in the last-level cache (non-temporal stores make this
   // kernel slightly faster but the whole step slower).
@@ -975,8 +1124,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
       if (p.lse_out != nullptr)
         p.lse_out[static_cast<size_t>(b) * p.n_rows + head] = (m + __log2f(l)) * kLn2;
     } else {
-      p.part_ml[(static_cast<size_t>(b) * p.n_rows + head) * p.num_splits + s] =
-          make_float2(m + __log2f(l), m);
+      p.part_ml[static_cast<size_t>(pidx) * p.n_rows + head] = make_float2(m + __log2f(l), m);
     }
   }
 }
@@ -994,7 +1142,16 @@ hipError_t launch_partials_mfma(const DecodeArgs& a) {
   p.split_tokens = a.split_tokens;
   p.num_splits = a.num_splits;
   p.head_groups = a.head_groups;
-  p.work_items = a.batch * a.num_splits * a.head_groups;
+  p.work_items = a.partitions * a.head_groups;
+  p.batch = a.batch;
+  p.part_target = a.part_target;
+  p.part_max_tokens = a.part_max_tokens;
+  p.part_table = a.part_table;
+  if (a.split_tokens == 0 &&
+      (a.batch > kBalancedMaxBatch || a.cache.max_len > kBalancedMaxLen || a.direct ||
+       a.part_table == nullptr || a.part_target < 1 || a.part_max_tokens < 32 ||
+       a.part_max_tokens % 32 != 0))
+    return hipErrorInvalidValue;
   p.scale_log2 = a.softmax_scale * kLog2e;
   p.part_o = static_cast<uint16_t*>(a.part_o);
   p.part_ml = reinterpret_cast<float2*>(a.part_lse);

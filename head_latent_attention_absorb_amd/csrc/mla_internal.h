@@ -14,8 +14,13 @@ namespace mla {
 // writes fp32 sums normalised by their own softmax sum and the fp32
 // natural-log sum-exp, split-major ([request, split, row]); the MFMA kernel
 // writes bf16 sums relative to a reference max m (not normalised) and the
-// fp32 pair (log-sum-exp, m), both in base-2 log units, split-minor
-// ([request, row, split]: a merge reads one contiguous run).
+// fp32 pair (log-sum-exp, m), both in base-2 log units, partition-major
+// ([partition, row]): partition s of request b is number off_b + s, where
+// off_b = b * num_splits in a uniform plan and, in a length-balanced one
+// (MFMA only), the number of partitions of the requests before b.  The
+// balanced launch sizes its partitions on the device and leaves the
+// partition table behind the statistics: [0] the partition length c,
+// [1 + b] off_b, [1 + batch] the partition count.
 
 struct CacheView {
   const uint8_t* data;      // cache rows, (d_latent + d_rope) elements each
@@ -43,6 +48,13 @@ struct DecodeArgs {
   // MFMA kernel: query rows per workgroup, 128 or 64 (head_groups = q_len *
   // n_heads / group_rows).
   int32_t group_rows = 128;
+  // Partitions one launch has room for (batch * num_splits in a uniform
+  // plan).  Length-balanced plan (split_tokens == 0): the device picks the
+  // partition length, for about part_target partitions of at most
+  // part_max_tokens tokens, and writes the partition table to part_table.
+  int32_t partitions = 0;
+  int32_t part_target = 0, part_max_tokens = 0;
+  int32_t* part_table = nullptr;
   void* out_lat;
   float* lse;           // may be nullptr
   void* part_o;         // workspace: fp32 (generic kernel) or bf16 (MFMA kernel)
@@ -105,6 +117,12 @@ hipError_t launch_cache_append(int dtype, int batch, int d_model, int d_c, int d
 // bf16 per src_dtype).
 hipError_t launch_quantize_rows(int src_dtype, int64_t n_rows, int width, const void* src,
                                 void* dst, float* scales, hipStream_t stream);
+
+// Length-balanced plans: the most requests (each lane of a wave keeps four
+// lengths in registers while the device sizes the partitions) and the
+// longest cache (lengths convert exactly to fp32, and their sum fits int32).
+constexpr int kBalancedMaxBatch = 256;
+constexpr int kBalancedMaxLen = 1 << 22;
 
 // Constants of the MFMA decode kernel that the planner needs.
 constexpr int kMfmaHeadsPerGroup = 128;  // query rows of a workgroup (128-row form)

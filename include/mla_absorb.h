@@ -102,13 +102,24 @@ typedef struct {
   int32_t row_format;        /* mla_row_format_t                               */
 } mla_cache_t;
 
-/* Split-KV plan: each request's tokens are cut into partitions of
- * split_tokens tokens that run on different compute units and are merged by
- * their log-sum-exp weights.  Produced by mla_decode_plan or
- * mla_decode_plan_mq; every decode call takes its query count from it. */
+/* Split-KV plan: each request's tokens are cut into partitions that run on
+ * different compute units and are merged by their log-sum-exp weights.
+ * Produced by mla_decode_plan or mla_decode_plan_mq; every decode call takes
+ * its query count from it.
+ * Uniform plan (split_tokens > 0): partitions of split_tokens tokens, the
+ * same cut for every batch, sized from max_len.
+ * Length-balanced plan (split_tokens == 0; the MFMA kernel's default when the
+ * batch alone does not fill the compute units, at most 256 requests and
+ * max_len <= 2^22): the decode kernel reads seq_lens on the device and picks
+ * one partition length c (a multiple of 32 tokens) per call, the smallest
+ * for which the requests' partition counts ceil(seq_lens[b] / c) add up to
+ * at most one workgroup per compute unit; no host synchronisation.  The
+ * split of a request's rows changes only the rounding of the result. */
 typedef struct {
-  int32_t split_tokens;   /* tokens per partition                              */
-  int32_t num_splits;     /* partitions per request, ceil(max_len/split_tokens) */
+  int32_t split_tokens;   /* tokens per partition; 0: length-balanced plan     */
+  int32_t num_splits;     /* uniform: partitions per request,
+                             ceil(max_len/split_tokens); balanced: the most
+                             partitions one request can get                   */
   int32_t kernel;         /* 0 = generic fp32-VALU kernel; bf16 MFMA kernel with
                              1 = 128 or 2 = 64 query rows per workgroup (2:
                              chosen for several splits of at most 256 tokens;
@@ -118,6 +129,9 @@ typedef struct {
                              many groups                                      */
   int32_t q_len;          /* query tokens per request (1 = plain decode)       */
   size_t workspace_bytes; /* device bytes mla_decode_attn needs                */
+  int32_t partitions;     /* (request, partition) pairs one call has room for:
+                             batch * num_splits (uniform) or the balanced
+                             plan's capacity                                  */
 } mla_decode_plan_t;
 
 /* Device bytes of workspace mla_decode_attn needs for `batch` requests of
@@ -138,7 +152,8 @@ const char* mla_status_str(mla_status_t status);
  * mla_decode_plan_t.q_len and mla_decode_plan_mq; 3 added mla_cache_t.scales,
  * mla_cache_t.row_format and mla_quantize_rows; 4 added mla_prefill_expand and
  * mla_prefill_attn; 5 added mla_decode_workspace_bytes and the 64-row form of
- * the MFMA kernel, plan->kernel 2). */
+ * the MFMA kernel, plan->kernel 2; 6 added length-balanced plans and
+ * mla_decode_plan_t.partitions). */
 int32_t mla_abi_version(void);
 
 /* Absorb W^UK into the query (V2 read-through section 2.3; V3 read-through
@@ -194,10 +209,10 @@ mla_status_t mla_decode_plan_mq(const mla_dims_t* dims, int32_t batch, int32_t q
  * batch and cache bounds.  workspace: device, >= plan->workspace_bytes, 256-byte
  * aligned, contents need no initialisation; calls that share a workspace
  * must be ordered on one stream.  With a one-split plan on the MFMA kernel
- * (plan->num_splits == 1, plan->kernel 1 or 2) over native rows the decode
- * kernel normalises its rows and writes out_lat and lse itself: nothing is
- * merged and the workspace is not touched; otherwise the call is
- * mla_decode_partials followed by mla_decode_combine. */
+ * (plan->split_tokens > 0, plan->num_splits == 1, plan->kernel 1 or 2) over
+ * native rows the decode kernel normalises its rows and writes out_lat and
+ * lse itself: nothing is merged and the workspace is not touched; otherwise
+ * the call is mla_decode_partials followed by mla_decode_combine. */
 mla_status_t mla_decode_attn(const mla_dims_t* dims, int32_t batch, const void* q_cat,
                              const mla_cache_t* cache, float softmax_scale,
                              const mla_decode_plan_t* plan, void* out_lat, float* lse,
@@ -229,11 +244,13 @@ size_t mla_decode_noalloc_max_bytes(void);
  * stream with the same plan and workspace.
  *
  * mla_decode_partials: for every request b, split s and head i with tokens in
- *   [s*split_tokens, min((s+1)*split_tokens, seq_lens[b])), writes into the
- *   workspace the split's softmax-weighted latent sum and the fp32
- *   statistics that weight it in the merge (its natural-log sum-exp among
- *   them).  The workspace layout is private to the library and depends on
- *   plan->kernel.  Splits with no tokens are not written.
+ *   [s*c, min((s+1)*c, seq_lens[b])) (c = split_tokens, or in a balanced plan
+ *   the length this call picks), writes into the workspace the split's
+ *   softmax-weighted latent sum and the fp32 statistics that weight it in
+ *   the merge (its natural-log sum-exp among them), and in a balanced plan
+ *   the partition table the combine reads.  The workspace layout is private
+ *   to the library and depends on the plan.  Splits with no tokens are not
+ *   written.
  * mla_decode_combine: merges the used splits of each request, split s
  *   weighted by exp(lse_s - max_s lse_s) relative to its normalised sum, into
  *   out_lat (dims->dtype) and lse (fp32, may be NULL); it reads only seq_lens

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_absorb_q", "mla_decode_attn", "mla_out_uv", "mla_decode_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
-    assert L.mla_abi_version() == 5
+    assert L.mla_abi_version() == 6
 
 
 def test_status_strings():
@@ -43,10 +43,10 @@ def test_status_strings():
 
 
 def test_struct_sizes_match_header():
-    # mla_dims_t: 5 x int32; mla_cache_t: 3 pointers, 2 int32, int64; plan: 4 int32 + size_t.
+    # mla_dims_t: 5 x int32; mla_cache_t: 3 pointers, 2 int32, int64; plan: 5 int32, size_t, int32.
     assert ctypes.sizeof(mla.Dims) == 20
     assert ctypes.sizeof(mla.CacheDesc) == 56
-    assert ctypes.sizeof(mla.Plan) == 32
+    assert ctypes.sizeof(mla.Plan) == 40
     # mla_rope_t: 4 floats and an int32.
     assert ctypes.sizeof(mla.Rope) == 20
 
@@ -161,11 +161,19 @@ def test_plan_shapes_and_workspace_errors():
     lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
     cache = mla.latent_cache(data, lens, 64)
     plan = mla.decode_plan(128, 512, 64, torch.bfloat16, cache)
-    # Several splits per request: the 64-row form, two row groups per request.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # Several splits per request: the 64-row form, two row groups per request,
+    # and 16 requests x 2 groups leave compute units idle: a length-balanced
+    # plan with room for one workgroup per compute unit.
     assert plan.kernel == 2 and plan.head_groups == 2
-    assert plan.split_tokens % 32 == 0 and plan.num_splits * plan.split_tokens >= T
-    # bf16 partial outputs plus fp32 log-sum-exps
-    assert plan.workspace_bytes >= B * plan.num_splits * 128 * (512 * 2 + 4)
+    assert plan.split_tokens == 0 and plan.balanced
+    assert plan.partitions == cus // 2 and plan.num_splits == min(plan.partitions, T // 32)
+    # bf16 partial outputs plus fp32 (lse, m) pairs, plus the partition table
+    assert plan.workspace_bytes >= plan.partitions * 128 * (512 * 2 + 8) + 4 * (B + 2)
+    # A split length asked for gives a uniform plan.
+    up = mla.decode_plan(128, 512, 64, torch.bfloat16, cache, split_tokens=512)
+    assert (up.split_tokens, up.num_splits, up.partitions) == (512, T // 512, B * T // 512)
+    assert not up.balanced
     q = torch.zeros((B, 128, 576), dtype=torch.bfloat16, device="cuda")
     out = torch.empty((B, 128, 512), dtype=torch.bfloat16, device="cuda")
     ws = mla.workspace_for(plan, "cuda")
@@ -181,7 +189,7 @@ def test_plan_shapes_and_workspace_errors():
     assert st == 5
     # A plan whose split count does not match its split length is rejected.
     bad = mla.Plan(plan.split_tokens, plan.num_splits - 1, plan.kernel, plan.head_groups,
-                   plan.q_len, plan.workspace_bytes)
+                   plan.q_len, plan.workspace_bytes, plan.partitions)
     st = L.mla_decode_attn(ctypes.byref(d), B, q.data_ptr(), ctypes.byref(desc), 0.07,
                            ctypes.byref(bad), out.data_ptr(), None, ws.data_ptr(),
                            plan.workspace_bytes, None)
@@ -189,7 +197,14 @@ def test_plan_shapes_and_workspace_errors():
     # So is a plan whose query count was changed by hand (its head groups and
     # workspace no longer match), and a query count out of range.
     bad = mla.Plan(plan.split_tokens, plan.num_splits, plan.kernel, plan.head_groups,
-                   2, plan.workspace_bytes)
+                   2, plan.workspace_bytes, plan.partitions)
+    st = L.mla_decode_attn(ctypes.byref(d), B, q.data_ptr(), ctypes.byref(desc), 0.07,
+                           ctypes.byref(bad), out.data_ptr(), None, ws.data_ptr(),
+                           plan.workspace_bytes, None)
+    assert st == 2
+    # And a balanced plan whose capacity was changed by hand.
+    bad = mla.Plan(plan.split_tokens, plan.num_splits, plan.kernel, plan.head_groups,
+                   plan.q_len, plan.workspace_bytes, plan.partitions + 1)
     st = L.mla_decode_attn(ctypes.byref(d), B, q.data_ptr(), ctypes.byref(desc), 0.07,
                            ctypes.byref(bad), out.data_ptr(), None, ws.data_ptr(),
                            plan.workspace_bytes, None)

@@ -2,7 +2,8 @@
 replayed, in both call patterns: absorb -> mla_decode_attn -> W^UV, and
 absorb -> partials -> combine + W^UV.  Every replay must give the eager
 result bit for bit, with eager work and synchronisations between the
-replays, and a replay after the inputs change in place must follow them.
+replays, and a replay after the inputs (query values, then request lengths)
+change in place must follow them.
 No call of the step allocates, synchronises or clears memory, so the step is
 capturable as is."""
 
@@ -42,7 +43,7 @@ def test_step_graph_replays_match_eager(form):
     lse = torch.empty((B, nh), dtype=torch.float32, device="cuda")
     o = torch.empty((B, nh, cfg.d_head), dtype=torch.bfloat16, device="cuda")
 
-    assert plan.num_splits > 1
+    assert plan.num_splits > 1 and plan.balanced
 
     def step():
         mla.absorb_q(q_c, q_r, dc.w_uk, out=q_cat)
@@ -79,3 +80,12 @@ def test_step_graph_replays_match_eager(form):
     torch.cuda.synchronize()
     assert torch.equal(got, o)
     assert not torch.equal(got, ref[0])
+    # New lengths in the captured length buffer: the balanced plan's
+    # partitions are cut on the device at every call, so the replay follows.
+    dc.seq_lens.copy_(torch.tensor([1536, 2, 2, 1536, 900, 1], dtype=torch.int32))
+    g.replay()
+    torch.cuda.synchronize()
+    got, got_lat = o.clone(), o_lat.clone()
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(got, o) and torch.equal(got_lat, o_lat)

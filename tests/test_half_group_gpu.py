@@ -44,7 +44,7 @@ def _forced(plan, kernel):
     """The same split plan in the other form (rows per workgroup 128 or 64)."""
     groups = plan.q_len * 128 // (128 if kernel == 1 else 64)
     return mla.Plan(plan.split_tokens, plan.num_splits, kernel, groups, plan.q_len,
-                    plan.workspace_bytes)
+                    plan.workspace_bytes, plan.partitions)
 
 
 def _oracle(case, q_np, heads, q_len):

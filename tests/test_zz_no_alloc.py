@@ -47,7 +47,8 @@ def _both(cfg, seed, lens, split=0):
 
 
 def test_noalloc_matches_decode_attn_twice():
-    # First: the B=16 DeepSeek-V2 shape at T=4096 (the default plan, 8 splits).
+    # First: the B=16 DeepSeek-V2 shape at T=4096 (the default plan:
+    # length-balanced, 512-token partitions).
     _log("[noalloc] B=16 T=4096")
     o, l, o_ref, l_ref, plan = _both(DSV2, 3, [4096] * 16)
     assert plan.num_splits > 1
