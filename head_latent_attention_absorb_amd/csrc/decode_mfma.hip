@@ -259,6 +259,7 @@ __device__ __forceinline__ int swz(int n, int chunk) {
 // launch nor a host synchronisation.
 struct Partition {
   int b = -1, s = 0, c = 32;  // b < 0: the item is past the last partition
+  int len = 0;                // seq_lens[b]
 };
 
 // Sum over the wave, in every lane: within each row of 16 lanes by DPP lane
@@ -346,12 +347,15 @@ __device__ Partition balanced_partition(const int32_t* __restrict__ seq_lens, in
     n[k] = ceil_div_len(len[k], c, rc);
     tot += n[k];
   }
-  int off = wave_exclusive_sum(tot), mine = -1;
+  int off = wave_exclusive_sum(tot), mine = -1, mine_len = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     if (table != nullptr && lane * kPer + k < batch) table[1 + lane * kPer + k] = off;
     // request (< 256) and partition (< 2^22 / 32) packed in one lane value
-    if (item >= off && item < off + n[k]) mine = (lane * kPer + k) << 23 | (item - off);
+    if (item >= off && item < off + n[k]) {
+      mine = (lane * kPer + k) << 23 | (item - off);
+      mine_len = len[k];
+    }
     off += n[k];
   }
   if (table != nullptr && lane == 63) {
@@ -362,7 +366,9 @@ __device__ Partition balanced_partition(const int32_t* __restrict__ seq_lens, in
   pt.c = c;
   const unsigned long long hit = __ballot(mine >= 0);
   if (hit != 0) {
-    const int v = __shfl(mine, __ffsll(static_cast<long long>(hit)) - 1, 64);
+    const int src = __ffsll(static_cast<long long>(hit)) - 1;
+    const int v = __shfl(mine, src, 64);
+    pt.len = __shfl(mine_len, src, 64);
     pt.b = v >> 23;
     pt.s = v & 0x7fffff;
   }
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
   // Partition `item` (all head groups of a partition are consecutive work
   // ids, so they share an XCD): request b, its partition s of c tokens, and
   // its number pidx in the partial layout.
-  int b, s, c, pidx;
+  int b, s, c, pidx, req_len;
   if (p.split_tokens == 0) {
     int32_t* table = work == 0 && wave == 0 ? p.part_table : nullptr;
     const Partition pt =
@@ -429,17 +435,19 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(MfmaParams p) {
     if (b < 0) return;
     s = __builtin_amdgcn_readfirstlane(pt.s);
     c = __builtin_amdgcn_readfirstlane(pt.c);
+    req_len = __builtin_amdgcn_readfirstlane(pt.len);
     pidx = item;
   } else {
     s = item % p.num_splits;
     b = item / p.num_splits;
     c = p.split_tokens;
+    req_len = p.cache.seq_lens[b];
     pidx = item;
   }
 
   // Query token j of the request (head group g covers rows g*kGH ..) sees
   // the rows up to its own position: q_len - 1 - j fewer than the request.
-  const int len = p.cache.seq_lens[b] - (p.q_len - 1 - g * kGH / p.heads_per_token);
+  const int len = req_len - (p.q_len - 1 - g * kGH / p.heads_per_token);
   const int t0 = s * c;
   const int t1 = min(t0 + c, len);
   const int hblock = g * (kGH / 32) + hb;
