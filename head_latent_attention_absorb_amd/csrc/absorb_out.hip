@@ -107,14 +107,19 @@ __global__ __launch_bounds__(kThreads) void out_uv_kernel(
 // absorption: X = q^C (K = d_head = 128), W = W^UK (N = d_latent = 512)
 // output:     X = o_lat (K = d_latent = 512), W = W^UV (N = d_head = 128)
 // One workgroup owns head i and an NB-column block of W, stages that
-// [K x NB] block in LDS (the only HBM stream: every weight element is read
-// once), and computes all batch rows with v_mfma_f32_32x32x16_bf16.  The
-// 4 waves split the block into NS column sub-blocks of 32 and 4/NS K parts;
-// K parts are summed through LDS.  Batch rows are the A operand (M tiles of
-// 32, loaded straight from global memory, zero past `batch`); the weight is
-// the B operand, read with the transposing LDS read (within a 16-lane group,
-// lane i receives element i%4 of the 8-byte chunk addressed by lane 4j + i/4,
-// for j = 0..3).
+// [K x NB] block in LDS with direct-to-LDS loads, all issued at once (the
+// only HBM stream: every weight element is read once), and computes all
+// batch rows with v_mfma_f32_32x32x16_bf16.  The N / NB blocks of a head are
+// consecutive work ids, and consecutive work ids run on one XCD (workgroup x
+// runs on XCD x % 8): the blocks of a weight row are read from one L2 at
+// about the same time.  The 4 waves split the block into NS column
+// sub-blocks of 32 and 4/NS K parts; K parts are summed through LDS.  Batch
+// rows are the A operand (M tiles of 32, loaded straight from global memory,
+// zero past `batch`); the weight is the B operand, read with the transposing
+// LDS read (within a 16-lane group, lane i receives element i%4 of the
+// 8-byte chunk addressed by lane 4j + i/4, for j = 0..3).  Each M tile's
+// results pass through LDS so that every output row is written in 16-byte
+// pieces.
 template <int K, int NB, int NS>
 __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
     const __bf16* __restrict__ X, const __bf16* __restrict__ W, __bf16* __restrict__ Y,
@@ -124,11 +129,16 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
   constexpr int KW = K / KP;          // K range of one wave
   constexpr int KSTEPS = KW / 16;
   static_assert(NS * KP == 4 && KW % 16 == 0 && NB == NS * 32, "");
-  __shared__ __attribute__((aligned(16))) __bf16 w_s[K * NB];
-  __shared__ __attribute__((aligned(16))) float red[(KP > 1 ? KP - 1 : 1) * NS * 16 * 64];
+  __shared__ __attribute__((aligned(1024))) __bf16 w_s[K * NB];
+  __shared__ __attribute__((aligned(16))) float red[KP > 1 ? (KP - 1) * NS * 16 * 64 : 1];
+  __shared__ __attribute__((aligned(16))) __bf16 y_s[32 * NB];
 
-  const int i = blockIdx.y;
-  const int n0 = blockIdx.x * NB;
+  const int nblk = N / NB;
+  const int nwg = gridDim.x;  // a multiple of 8
+  const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  if (work >= n_heads * nblk) return;
+  const int i = work / nblk, blk = work - i * nblk;
+  const int n0 = blk * NB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const int ns = wave % NS, kp = wave / NS;
@@ -158,51 +168,35 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
   // HBM round trips overlap.
   load_a(0, a);
 
-  // The RoPE tail of the absorbed query is copied unchanged (absorption only),
-  // in 4-element vectors spread over the gridDim.x workgroups of this head.
-  // The first round is loaded here so that it overlaps the weight stream.
+  // Stage W[i][0:K][n0:n0+NB] (row-major, NB contiguous) in LDS, in the same
+  // layout: one wave instruction copies 1 KiB, rows of NB elements.
+  {
+    constexpr int kLanesPerRow = NB / 8;  // 16-byte chunks per row
+    constexpr int kRowsPerCopy = 64 / kLanesPerRow;
+    constexpr int kCopies = K / kRowsPerCopy;
+    static_assert(K % kRowsPerCopy == 0 && kCopies % 4 == 0, "");
+    const __bf16* src = W + (static_cast<size_t>(i) * K + lane / kLanesPerRow) * N + n0 +
+                        (lane % kLanesPerRow) * 8;
+    const unsigned base =
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS __bf16*)w_s));
+#pragma unroll 4
+    for (int j = wave; j < kCopies; j += 4)
+      load_to_lds16(src + static_cast<size_t>(j) * kRowsPerCopy * N, base + j * 1024);
+  }
+
+  // The RoPE tail of the absorbed query is copied unchanged (absorption
+  // only), in 4-element vectors spread over the nblk workgroups of this head.
   const int tail_q = tail_w / 4;
   const int tail_vecs = tail_src != nullptr ? batch * tail_q : 0;
-  const int tv0 = blockIdx.x * 256 + tid, tv_step = gridDim.x * 256;
-  auto tail_at = [&](int e) {
+  for (int e = blk * 256 + tid; e < tail_vecs; e += nblk * 256) {
     const int b = e / tail_q, r4 = e - b * tail_q;
-    return reinterpret_cast<const bf16x4_t*>(
-        tail_src + (static_cast<size_t>(b) * n_heads + i) * tail_w + r4 * 4);
-  };
-  auto tail_dst = [&](int e) {
-    const int b = e / tail_q, r4 = e - b * tail_q;
-    return reinterpret_cast<bf16x4_t*>(Y + (static_cast<size_t>(b) * n_heads + i) * y_row + N +
-                                       r4 * 4);
-  };
-  bf16x4_t tv;
-  if (tv0 < tail_vecs) tv = tail_at(tv0)[0];
-
-  // Stage W[i][0:K][n0:n0+NB] (row-major, NB contiguous): all loads first,
-  // then the LDS stores.
-  constexpr int kChunksPerRow = NB / 8;
-  constexpr int kLoads = K * kChunksPerRow / 256;
-  static_assert(K * kChunksPerRow % 256 == 0, "");
-  const __bf16* wsrc = W + static_cast<size_t>(i) * K * N + n0;
-  bf16x8_t wv[kLoads];
-#pragma unroll
-  for (int u = 0; u < kLoads; ++u) {
-    const int ch = tid + u * 256;
-    const int k = ch / kChunksPerRow, cc = ch - k * kChunksPerRow;
-    wv[u] = *reinterpret_cast<const bf16x8_t*>(wsrc + static_cast<size_t>(k) * N + cc * 8);
+    *reinterpret_cast<bf16x4_t*>(Y + (static_cast<size_t>(b) * n_heads + i) * y_row + N +
+                                 r4 * 4) =
+        *reinterpret_cast<const bf16x4_t*>(
+            tail_src + (static_cast<size_t>(b) * n_heads + i) * tail_w + r4 * 4);
   }
-#pragma unroll
-  for (int u = 0; u < kLoads; ++u) {
-    const int ch = tid + u * 256;
-    const int k = ch / kChunksPerRow, cc = ch - k * kChunksPerRow;
-    *reinterpret_cast<bf16x8_t*>(w_s + k * NB + cc * 8) = wv[u];
-  }
-  // Second half of the RoPE tail copy: store what was loaded above, then the
-  // further rounds needed when the tail has more vectors than the head's
-  // workgroups have threads.
-  if (tv0 < tail_vecs) {
-    tail_dst(tv0)[0] = tv;
-    for (int e = tv0 + tv_step; e < tail_vecs; e += tv_step) tail_dst(e)[0] = tail_at(e)[0];
-  }
+  // The weight block must have landed before the barrier publishes it.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int m0 = 0; m0 < batch; m0 += 32) {
@@ -234,23 +228,36 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[v] += red[((q * NS + ns) * 16 + v) * 64 + lane];
       }
-      __syncthreads();
     }
     if (kp == 0) {
       // Accumulator register v of this lane: row (v/4)*8 + half*4 + v%4, column l32.
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int bb = m0 + (v >> 2) * 8 + half * 4 + (v & 3);
-        if (bb < batch)
-          Y[(static_cast<size_t>(bb) * n_heads + i) * y_row + n0 + ns * 32 + l32] =
-              static_cast<__bf16>(acc[v]);
-      }
+      for (int v = 0; v < 16; ++v)
+        y_s[((v >> 2) * 8 + half * 4 + (v & 3)) * NB + ns * 32 + l32] =
+            static_cast<__bf16>(acc[v]);
     }
+    __syncthreads();
+    constexpr int kRowChunks = NB / 8;
+    for (int c = tid; c < 32 * kRowChunks; c += 256) {
+      const int r = c / kRowChunks, ch = c - r * kRowChunks;
+      if (m0 + r < batch)
+        *reinterpret_cast<bf16x8_t*>(Y + (static_cast<size_t>(m0 + r) * n_heads + i) * y_row +
+                                     n0 + ch * 8) =
+            *reinterpret_cast<const bf16x8_t*>(y_s + r * NB + ch * 8);
+    }
+    // y_s and red are rewritten by the next tile.
+    __syncthreads();
     if (m0 + 32 < batch) {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) a[ks] = a_next[ks];
     }
   }
+}
+
+// Launch shape of head_proj_mfma_kernel: one workgroup per (head, column
+// block), a multiple of the 8 XCDs.
+int head_proj_grid(int n_heads, int N, int NB) {
+  return (n_heads * (N / NB) + 7) / 8 * 8;
 }
 
 
@@ -549,7 +556,7 @@ hipError_t launch_absorb_q(int dtype, int batch, int n_heads, int d_head, int d_
     return launch_wide<128, 512, false>(p, stream);
   }
   if (dtype == 1 && d_head == 128 && d_latent % 128 == 0 && d_rope % 4 == 0) {
-    head_proj_mfma_kernel<128, 128, 4><<<dim3(d_latent / 128, n_heads), 256, 0, stream>>>(
+    head_proj_mfma_kernel<128, 128, 4><<<head_proj_grid(n_heads, d_latent, 128), 256, 0, stream>>>(
         static_cast<const __bf16*>(q_c), static_cast<const __bf16*>(w_uk),
         static_cast<__bf16*>(q_cat), batch, n_heads, d_latent, d_latent + d_rope,
         d_rope > 0 ? static_cast<const __bf16*>(q_r) : nullptr, d_rope);
@@ -619,7 +626,7 @@ hipError_t launch_out_uv(int dtype, int batch, int n_heads, int d_head, int d_la
     return launch_wide<512, 128, false>(p, stream);
   }
   if (dtype == 1 && d_latent == 512 && d_head % 64 == 0) {
-    head_proj_mfma_kernel<512, 64, 2><<<dim3(d_head / 64, n_heads), 256, 0, stream>>>(
+    head_proj_mfma_kernel<512, 64, 2><<<head_proj_grid(n_heads, d_head, 64), 256, 0, stream>>>(
         static_cast<const __bf16*>(out_lat), static_cast<const __bf16*>(w_uv),
         static_cast<__bf16*>(out), batch, n_heads, d_head, d_head, nullptr, 0);
     return hipGetLastError();

@@ -229,8 +229,10 @@ def test_tiny_f32_combine_out(seed):
     assert_close(from_dev(lse), lse_ref, "f32", "lse")
 
 
-def test_absorb_q_bf16_b16():
-    cfg = DSV2.replace(len_lo=1, len_hi=1, max_len=1)
+@pytest.mark.parametrize("batch", [1, 16, 33, 200])
+def test_absorb_q_bf16(batch):
+    """Decode row counts: one M tile, a ragged second tile, seven tiles."""
+    cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1)
     case = make_case(cfg, 2)
     dc = DevCase(case)
     q_cat = mla.absorb_q(dc.q_c, dc.q_r, dc.w_uk)
@@ -273,7 +275,7 @@ def test_out_uv_bf16_many_rows(batch):
                  "o")
 
 
-@pytest.mark.parametrize("batch", [1, 16, 128])
+@pytest.mark.parametrize("batch", [1, 16, 33, 128])
 def test_out_uv_bf16(batch):
     cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1)
     case = make_case(cfg, 4)
