@@ -141,3 +141,25 @@ def test_positions_outside_the_cache_write_nothing():
     exp[2, 100] = after[2, 100]
     assert np.array_equal(after, exp, equal_nan=True)
     assert_close(after[2, 100][None], rows[2][None], "bf16", "row")
+
+
+def test_workspace_reuse_across_batches():
+    """One workspace for calls of different batch sizes, never cleared: each
+    call writes the same rows as with a fresh workspace (the workspace carries
+    nothing from one call to the next)."""
+    ws = torch.full((1 << 20,), 0x7F, dtype=torch.uint8, device="cuda")
+    for batch in (16, 4, 16, 1):
+        cfg = DSV2.replace(batch=batch, max_len=64, len_lo=1, len_hi=64)
+        ac = make_append_case(cfg, 40 + batch)
+        args = [_dev(ac.h, cfg.dtype), _dev(ac.w_dkv, cfg.dtype), _dev(ac.w_kr, cfg.dtype),
+                _dev(ac.rms_weight, cfg.dtype), torch.from_numpy(ac.positions % 64).cuda()]
+        lens = torch.zeros(batch, dtype=torch.int32, device="cuda")
+        outs = []
+        for w in (ws, None):
+            data = torch.zeros((batch, 64, cfg.d_latent + cfg.d_rope), dtype=torch.bfloat16,
+                               device="cuda")
+            mla.cache_append(mla.latent_cache(data, lens, cfg.d_rope), *args, workspace=w)
+            torch.cuda.synchronize()
+            outs.append(data)
+        _log(f"[append reuse] batch={batch}")
+        assert torch.equal(outs[0], outs[1])
