@@ -327,12 +327,13 @@ __device__ Partition balanced_partition(const int32_t* __restrict__ seq_lens, in
   auto up32 = [](int x) { return (x + 31) / 32 * 32; };
   // sum / target bounds c from below; sum / (target - nz) from above
   // (n_b < len_b / c + 1 for every non-empty request).  Equal lengths meet
-  // the target at the lower bound, so that is tried first.
+  // the target at the lower bound, so that is tried first.  When the cap
+  // binds (lo == hi == c_max) c is the cap, whatever the count.
   int lo = max(32, up32((sum + target - 1) / target));
   int hi = target > nz ? up32((sum + (target - nz) - 1) / (target - nz)) : c_max;
   hi = max(32, min(hi, c_max));
   lo = min(lo, hi);
-  if (count(lo) > target) {
+  if (lo < hi && count(lo) > target) {
     lo += 32;
     while (lo < hi) {
       const int mid = lo + (hi - lo) / 64 * 32;

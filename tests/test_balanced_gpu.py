@@ -98,6 +98,10 @@ CASES = [
     ("paged_b128", dict(batch=128, max_len=2048, page_size=64), None, 1),
     ("paged_skew", dict(batch=5, max_len=8192, page_size=64), [8192, 1, 64, 4000, 0], 1),
     ("two_tokens", dict(batch=3, max_len=4096), [4096, 2, 333], 2),
+    # 24-token pages cap a partition at 1504 tokens (63 pages' worth, whatever
+    # the alignment); eight query tokens leave a target of 32 partitions, so
+    # the cap binds: c is the cap and the count exceeds the target
+    ("paged_cap_binds", dict(batch=2, max_len=30720, page_size=24), [30720, 30000], 8),
 ]
 
 
