@@ -238,7 +238,11 @@ def absorb_q(q_c: torch.Tensor, q_r: torch.Tensor, w_uk: torch.Tensor,
 def decode_plan(n_heads: int, d_latent: int, d_rope: int, dtype, cache: LatentCache,
                 split_tokens: int = 0, d_head: int = 1, q_len: int = 1) -> Plan:
     """Split-KV plan for `cache`; q_len > 1 plans the causal decode of the last
-    q_len positions of every request at once (mla_decode_plan_mq)."""
+    q_len positions of every request at once (mla_decode_plan_mq).
+    split_tokens > 0 asks for a uniform cut of that many tokens per partition;
+    0 lets the library choose: on the MFMA kernel usually a length-balanced
+    plan (Plan.balanced), whose partitions the decode kernel sizes from the
+    device's seq_lens at every call."""
     dims = make_dims(n_heads, d_head, d_rope, d_latent, dtype)
     plan = Plan()
     desc = cache.desc()
