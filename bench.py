@@ -367,6 +367,10 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests in the CPU oracle sample (0 skips it; default workload only)")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="every request at this many cached rows instead of the workload's "
+                         "lengths (single-layer contiguous workloads; a sweep of it splits "
+                         "the decode kernel's time into per-step and fixed costs)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a HIP graph instead of plain calls")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -385,6 +389,11 @@ def main():
 
     name = args.workload
     cfg = CONFIGS[name]
+    if args.seq_len > 0:
+        if cfg.paged or cfg.layers > 1 or cfg.form == "unabsorbed":
+            print("--seq-len applies to single-layer contiguous workloads", file=sys.stderr)
+            sys.exit(2)
+        cfg = cfg.replace(len_lo=args.seq_len, len_hi=args.seq_len, max_len=args.seq_len)
     if cfg.form == "unabsorbed":
         run_unabsorbed(args, cfg, name)
         return
@@ -605,11 +614,13 @@ def main():
     t_roof_us = max(step_bytes / (HBM_PEAK_GBPS * 1e9),
                     step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
     sha = kernel_sha()
-    counters = counters_for(sha) if name == WORKLOAD else {}
+    default_shape = name == WORKLOAD and args.seq_len == 0
+    counters = counters_for(sha) if default_shape else {}
 
     result = {
-        "metric": METRIC if name == WORKLOAD else
-                  f"MLA decode tokens/s and latent-cache HBM GB/s (% roofline), {name}",
+        "metric": METRIC if default_shape else
+                  f"MLA decode tokens/s and latent-cache HBM GB/s (% roofline), {name}"
+                  + (f", every request at {args.seq_len} rows" if args.seq_len else ""),
         # Tokens decoded per second: every query token of every request (the
         # verification workload decodes q_len per request and step).
         "value": B * ql / (ms_per_step * 1e-3),
@@ -688,7 +699,7 @@ def main():
             "achieved_GBps": ap_bytes / (kernels_us["cache_append"] * 1e-6) / 1e9,
             "timing": "events around the call inside the per-kernel pass",
         }
-    if args.cpu_requests > 0 and name == WORKLOAD:
+    if args.cpu_requests > 0 and default_shape:
         log(f"[bench] cpu baseline: oracle on {args.cpu_requests} requests")
         result["cpu_baseline"] = cpu_baseline(pool[0], cfg, args.cpu_requests)
     print(json.dumps(result), flush=True)
