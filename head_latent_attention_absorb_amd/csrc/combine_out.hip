@@ -109,10 +109,11 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   int c = split_tokens, nk;
   size_t pbase;
   if (part_table != nullptr) {
-    c = part_table[0];
-    const int first = part_table[1 + (live ? b : 0)];
+    // (clamped, so that a table the decode kernel did not write cannot
+    // send the loads outside the workspace)
+    c = max(part_table[0], 32);
+    const int first = min(max(part_table[1 + (live ? b : 0)], 0), partitions);
     pbase = static_cast<size_t>(first);
-    // (the table's partitions lie within the launch's capacity)
     const int used = min(used_splits(len, c), partitions - first);
     nk = max(0, (used - p + P - 1) >> p_log2);
   } else {
