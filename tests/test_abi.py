@@ -170,6 +170,8 @@ def test_plan_shapes_and_workspace_errors():
     assert plan.partitions == cus // 2 and plan.num_splits == min(plan.partitions, T // 32)
     # bf16 partial outputs plus fp32 (lse, m) pairs, plus the partition table
     assert plan.workspace_bytes >= plan.partitions * 128 * (512 * 2 + 8) + 4 * (B + 2)
+    # The exported size query returns this plan's workspace.
+    assert mla.decode_workspace_bytes(128, 512, 64, torch.bfloat16, B, T) == plan.workspace_bytes
     # A split length asked for gives a uniform plan.
     up = mla.decode_plan(128, 512, 64, torch.bfloat16, cache, split_tokens=512)
     assert (up.split_tokens, up.num_splits, up.partitions) == (512, T // 512, B * T // 512)
