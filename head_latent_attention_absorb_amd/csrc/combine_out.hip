@@ -82,7 +82,11 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   const int P = 1 << p_log2;                 // waves per request
   const int R = kWaves >> p_log2;            // requests per workgroup
   const int b0 = blockIdx.y * R;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // The wave index is made uniform so that the per-request values (length,
+  // partition table) come through scalar loads: those are waited for apart
+  // from the vector loads, which queue behind the W^UV stream issued first.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   if constexpr (kOut) {
     // Start W^UV[i] streaming into LDS: a linear copy of its d_latent x d_head
