@@ -260,6 +260,161 @@ int head_proj_grid(int n_heads, int N, int NB) {
   return (n_heads * (N / NB) + 7) / 8 * 8;
 }
 
+// The same product for more than one M tile of rows.  One workgroup owns head
+// i, an NB-column block of W and a chunk of MR rows; the weight block and the
+// chunk's rows are staged in LDS in one burst of direct-to-LDS loads (a
+// single memory round trip, where loading each tile's rows in turn would
+// expose one round trip per tile), each wave reads its weight fragments once
+// into registers, and the chunk's M tiles are multiplied from LDS.  LDS row r
+// holds X row r0 + r with its 16-byte chunk c in slot c ^ (r % 16), so that
+// the A-operand reads of 16 consecutive rows fall in 16 different bank
+// groups.  Rows past the batch are neither loaded nor stored.  The chunks
+// and column blocks of a head are consecutive work ids (one XCD: they share
+// the weight block through its L2).
+template <int K, int NB, int NS, int MR>
+__global__ __launch_bounds__(256) void head_proj_rows_kernel(
+    const __bf16* __restrict__ X, const __bf16* __restrict__ W, __bf16* __restrict__ Y,
+    int batch, int n_heads, int N, int y_row, const __bf16* __restrict__ tail_src,
+    int tail_w) {
+  constexpr int KP = 4 / NS;          // K parts
+  constexpr int KW = K / KP;          // K range of one wave
+  constexpr int KSTEPS = KW / 16;
+  constexpr int kXChunks = K / 8;     // 16-byte chunks per row
+  constexpr int kXRowsPerCopy = 64 / kXChunks;
+  static_assert(NS * KP == 4 && KW % 16 == 0 && NB == NS * 32 && MR % 32 == 0, "");
+  static_assert(kXChunks % 16 == 0 && 64 % kXChunks == 0, "rows of 128, 256 or 512 elements");
+  __shared__ __attribute__((aligned(1024))) __bf16 w_s[K * NB];
+  __shared__ __attribute__((aligned(1024))) __bf16 x_s[MR * K];
+  __shared__ __attribute__((aligned(16))) float red[KP > 1 ? (KP - 1) * NS * 16 * 64 : 1];
+  __shared__ __attribute__((aligned(16))) __bf16 y_s[32 * NB];
+
+  const int nblk = N / NB;
+  const int nchunk = (batch + MR - 1) / MR;
+  const int nwg = gridDim.x;  // a multiple of 8
+  const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  if (work >= n_heads * nblk * nchunk) return;
+  const int rc = work % nchunk;
+  const int hbk = work / nchunk;
+  const int i = hbk / nblk, blk = hbk - i * nblk;
+  const int n0 = blk * NB, r0 = rc * MR;
+  const int rows = min(MR, batch - r0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int ns = wave % NS, kp = wave / NS;
+
+  // Weight block W[i][0:K][n0:n0+NB], row-major as in global memory.
+  {
+    constexpr int kLanesPerRow = NB / 8;
+    constexpr int kRowsPerCopy = 64 / kLanesPerRow;
+    constexpr int kCopies = K / kRowsPerCopy;
+    static_assert(K % kRowsPerCopy == 0 && kCopies % 4 == 0, "");
+    const __bf16* src = W + (static_cast<size_t>(i) * K + lane / kLanesPerRow) * N + n0 +
+                        (lane % kLanesPerRow) * 8;
+    const unsigned base =
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS __bf16*)w_s));
+#pragma unroll 4
+    for (int j = wave; j < kCopies; j += 4)
+      load_to_lds16(src + static_cast<size_t>(j) * kRowsPerCopy * N, base + j * 1024);
+  }
+  // The chunk's rows, swizzled (see above); one instruction fills 1 KiB.
+  {
+    const int xr = lane / kXChunks, slot = lane % kXChunks;
+    const unsigned base =
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS __bf16*)x_s));
+    const int copies = (rows + kXRowsPerCopy - 1) / kXRowsPerCopy;
+    for (int j = wave; j < copies; j += 4) {
+      const int r = j * kXRowsPerCopy + xr;
+      const int b = r0 + min(r, rows - 1);
+      load_to_lds16(X + (static_cast<size_t>(b) * n_heads + i) * K + (slot ^ (r & 15)) * 8,
+                    base + j * 1024);
+    }
+  }
+
+  // The RoPE tail of the absorbed query is copied unchanged (absorption
+  // only), spread over the workgroups of this head.
+  const int tail_q = tail_w / 4;
+  const int tail_vecs = tail_src != nullptr ? batch * tail_q : 0;
+  for (int e = (blk * nchunk + rc) * 256 + tid; e < tail_vecs; e += nblk * nchunk * 256) {
+    const int b = e / tail_q, r4 = e - b * tail_q;
+    *reinterpret_cast<bf16x4_t*>(Y + (static_cast<size_t>(b) * n_heads + i) * y_row + N +
+                                 r4 * 4) =
+        *reinterpret_cast<const bf16x4_t*>(
+            tail_src + (static_cast<size_t>(b) * n_heads + i) * tail_w + r4 * 4);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // Weight fragments of this wave (transposing reads, as head_proj_mfma_kernel).
+  const int G = lane >> 4, r16 = lane & 15;
+  const int tr_k = ((G >> 1) << 3) + (r16 >> 2);
+  const int tr_n = ns * 32 + ((G & 1) << 4) + ((r16 & 3) << 2);
+  bf16x8_t bfr[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int k0 = kp * KW + ks * 16;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k) * NB + tr_n));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k + 4) * NB + tr_n));
+    bfr[ks] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  const int ntiles = (rows + 31) / 32;
+  for (int t = 0; t < ntiles; ++t) {
+    const int m0 = t * 32;
+    // A operand: row m0 + l32 (its swizzle key is l32 % 16), K slots
+    // kp*KW + ks*16 + half*8 .. +7.
+    const __bf16* xrow = x_s + (m0 + l32) * K;
+    f32x16_t acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int c = (kp * KW + ks * 16) / 8 + half;
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(xrow + (c ^ (l32 & 15)) * 8);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfr[ks], acc, 0, 0, 0);
+    }
+    if constexpr (KP > 1) {
+      if (kp > 0) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[(((kp - 1) * NS + ns) * 16 + v) * 64 + lane] = acc[v];
+      }
+      __syncthreads();
+      if (kp == 0) {
+#pragma unroll
+        for (int q = 0; q < KP - 1; ++q)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[v] += red[((q * NS + ns) * 16 + v) * 64 + lane];
+      }
+    }
+    if (kp == 0) {
+      // Accumulator register v of this lane: row (v/4)*8 + half*4 + v%4, column l32.
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        y_s[((v >> 2) * 8 + half * 4 + (v & 3)) * NB + ns * 32 + l32] =
+            static_cast<__bf16>(acc[v]);
+    }
+    __syncthreads();
+    constexpr int kRowChunks = NB / 8;
+    for (int c = tid; c < 32 * kRowChunks; c += 256) {
+      const int r = c / kRowChunks, ch = c - r * kRowChunks;
+      if (m0 + r < rows)
+        *reinterpret_cast<bf16x8_t*>(
+            Y + (static_cast<size_t>(r0 + m0 + r) * n_heads + i) * y_row + n0 + ch * 8) =
+            *reinterpret_cast<const bf16x8_t*>(y_s + r * NB + ch * 8);
+    }
+    // y_s and red are rewritten by the next tile.
+    __syncthreads();
+  }
+}
+
+// Launch shape of head_proj_rows_kernel: one workgroup per (head, column
+// block, chunk of MR rows), a multiple of the 8 XCDs.
+int head_proj_rows_grid(int n_heads, int N, int NB, int batch, int MR) {
+  return (n_heads * (N / NB) * ((batch + MR - 1) / MR) + 7) / 8 * 8;
+}
+
 
 // The same products for many rows: a workgroup owns head i and a run of
 // rows_per_wg rows of one request, stages the whole weight of the head in LDS
@@ -529,8 +684,14 @@ hipError_t launch_wide(WideArgs p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Row count from which the wide form replaces head_proj_mfma_kernel.
+// Row count from which the wide form replaces head_proj_mfma_kernel (and,
+// above one M tile, head_proj_rows_kernel).
 constexpr int kWideRows = 256;
+// Rows per workgroup of head_proj_rows_kernel: absorption (128-wide rows,
+// 32 KiB beside a 32 KiB weight block) and output (512-wide rows, 64 KiB
+// beside a 64 KiB weight block).
+constexpr int kChunkRowsQ = 128;
+constexpr int kChunkRowsO = 64;
 }  // namespace
 
 hipError_t launch_absorb_q(int dtype, int batch, int n_heads, int d_head, int d_rope,
@@ -554,6 +715,14 @@ hipError_t launch_absorb_q(int dtype, int batch, int n_heads, int d_head, int d_
     p.tail_w = d_rope;
     p.tail_row = static_cast<long long>(n_heads) * d_rope;
     return launch_wide<128, 512, false>(p, stream);
+  }
+  if (dtype == 1 && d_head == 128 && d_latent % 128 == 0 && d_rope % 4 == 0 && batch > 32) {
+    head_proj_rows_kernel<128, 128, 4, kChunkRowsQ>
+        <<<head_proj_rows_grid(n_heads, d_latent, 128, batch, kChunkRowsQ), 256, 0, stream>>>(
+            static_cast<const __bf16*>(q_c), static_cast<const __bf16*>(w_uk),
+            static_cast<__bf16*>(q_cat), batch, n_heads, d_latent, d_latent + d_rope,
+            d_rope > 0 ? static_cast<const __bf16*>(q_r) : nullptr, d_rope);
+    return hipGetLastError();
   }
   if (dtype == 1 && d_head == 128 && d_latent % 128 == 0 && d_rope % 4 == 0) {
     head_proj_mfma_kernel<128, 128, 4><<<head_proj_grid(n_heads, d_latent, 128), 256, 0, stream>>>(
@@ -624,6 +793,13 @@ hipError_t launch_out_uv(int dtype, int batch, int n_heads, int d_head, int d_la
     p.y_row = static_cast<long long>(n_heads) * d_head;
     p.y_head = d_head;
     return launch_wide<512, 128, false>(p, stream);
+  }
+  if (dtype == 1 && d_latent == 512 && d_head % 64 == 0 && batch > 32) {
+    head_proj_rows_kernel<512, 64, 2, kChunkRowsO>
+        <<<head_proj_rows_grid(n_heads, d_head, 64, batch, kChunkRowsO), 256, 0, stream>>>(
+            static_cast<const __bf16*>(out_lat), static_cast<const __bf16*>(w_uv),
+            static_cast<__bf16*>(out), batch, n_heads, d_head, d_head, nullptr, 0);
+    return hipGetLastError();
   }
   if (dtype == 1 && d_latent == 512 && d_head % 64 == 0) {
     head_proj_mfma_kernel<512, 64, 2><<<head_proj_grid(n_heads, d_head, 64), 256, 0, stream>>>(

@@ -229,9 +229,10 @@ def test_tiny_f32_combine_out(seed):
     assert_close(from_dev(lse), lse_ref, "f32", "lse")
 
 
-@pytest.mark.parametrize("batch", [1, 16, 33, 200])
+@pytest.mark.parametrize("batch", [1, 16, 33, 129, 200])
 def test_absorb_q_bf16(batch):
-    """Decode row counts: one M tile, a ragged second tile, seven tiles."""
+    """Decode row counts: one M tile, a ragged second tile, a second chunk of
+    one row, seven tiles over two chunks."""
     cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1)
     case = make_case(cfg, 2)
     dc = DevCase(case)
@@ -275,7 +276,7 @@ def test_out_uv_bf16_many_rows(batch):
                  "o")
 
 
-@pytest.mark.parametrize("batch", [1, 16, 33, 128])
+@pytest.mark.parametrize("batch", [1, 16, 33, 128, 200])
 def test_out_uv_bf16(batch):
     cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1)
     case = make_case(cfg, 4)
@@ -283,6 +284,29 @@ def test_out_uv_bf16(batch):
     o = mla.out_uv(_bf16_dev(o_lat_np), DevCase(case).w_uv)
     torch.cuda.synchronize()
     assert_close(from_dev(o), oracle.project_out(o_lat_np, case.w_uv), "bf16", "o")
+
+
+@pytest.mark.parametrize("batch", [33, 65, 129, 200, 255])
+def test_projections_row_chunks_match_one_tile(batch):
+    """Above one M tile (32 rows) both projections stage chunks of rows in
+    LDS (128 rows for absorption, 64 for the output); each row's product has
+    the same operands and summation order as with one tile, so the first and
+    the last rows of the batch, computed again as batches of their own (one
+    tile), must come out bit for bit the same."""
+    cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1)
+    case = make_case(cfg, 7)
+    dc = DevCase(case)
+    o_lat = _bf16_dev(draw_latent_output(cfg, 7))
+    _log(f"[projection row chunks] batch={batch}")
+    q_cat = from_dev(mla.absorb_q(dc.q_c, dc.q_r, dc.w_uk))
+    o = from_dev(mla.out_uv(o_lat, dc.w_uv))
+    for lo, hi in ((0, 16), (batch - min(batch, 32) + 1, batch)):
+        q_part = from_dev(mla.absorb_q(dc.q_c[lo:hi].contiguous(), dc.q_r[lo:hi].contiguous(),
+                                       dc.w_uk))
+        o_part = from_dev(mla.out_uv(o_lat[lo:hi].contiguous(), dc.w_uv))
+        torch.cuda.synchronize()
+        assert np.array_equal(q_cat[lo:hi], q_part), f"q_cat rows {lo}..{hi - 1}"
+        assert np.array_equal(o[lo:hi], o_part), f"o rows {lo}..{hi - 1}"
 
 
 # ----------------------------------------------------------------------------
