@@ -177,19 +177,50 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(AppendParams p) {
   static_assert(kThreads == 256, "the block reductions below read four waves");
   const int b = blockIdx.x;
   const int n_total = p.d_c + p.d_r;
+  // What does not depend on the slices is requested first, so that its
+  // memory round trips overlap theirs: the position, then the page it falls
+  // in (clamped into the table; positions outside the cache write nothing),
+  // and the RMSNorm weights of the first kGam * kThreads latents.
+  const int pos = p.pos[b];
+  const T* gamma = static_cast<const T*>(p.gamma);
+  constexpr int kGam = 4;
+  // (Loads are unconditional, at clamped indexes, and unused values are
+  // dropped afterwards: a branch around a load makes the compiler wait for
+  // it where the branches join, one memory round trip per load.)
+  // The weights stay in their storage type until used (converting them
+  // here would make the compiler wait for them before the slices' loads).
+  T gam[kGam];
+#pragma unroll
+  for (int j = 0; j < kGam; ++j)
+    gam[j] = gamma[min(static_cast<int>(threadIdx.x) + j * kThreads, p.d_c - 1)];
+  const int pos_c = min(max(pos, 0), p.cache.max_len - 1);
+  int page = 0;
+  if (p.cache.page_table != nullptr)
+    page = p.cache.page_table[static_cast<size_t>(b) * p.cache.max_pages +
+                              pos_c / p.cache.page_size];
   // The slices' loads of kCols columns per thread are all issued before they
   // are summed (one memory round trip for up to kCols * kThreads columns).
+  // The first chunk is peeled off the loop: at a loop header the compiler
+  // waits for the loads issued above.
   constexpr int kCols = 3;
-  for (int n0 = threadIdx.x; n0 < n_total; n0 += kCols * kThreads) {
+  auto sum_chunk = [&](int n0) {
     float v[kCols][kMaxParts];
 #pragma unroll
     for (int c = 0; c < kCols; ++c) {
-      const int n = n0 + c * kThreads;
+      const int n = min(n0 + c * kThreads, n_total - 1);
 #pragma unroll
       for (int s = 0; s < kMaxParts; ++s)
-        v[c][s] = (s < p.parts && n < n_total)
-                      ? p.part[(static_cast<size_t>(s) * p.batch + b) * n_total + n] : 0.f;
+        v[c][s] = p.part[(static_cast<size_t>(min(s, p.parts - 1)) * p.batch + b) * n_total + n];
     }
+    // (Pinned here, so that the compiler cannot sink loads into the
+    // conditional stores below, behind the first ones' wait.)
+#pragma unroll
+    for (int c = 0; c < kCols; ++c)
+#pragma unroll
+      for (int s = 0; s < kMaxParts; ++s) {
+        asm volatile("" : "+v"(v[c][s]));
+        if (s >= p.parts) v[c][s] = 0.f;
+      }
 #pragma unroll
     for (int c = 0; c < kCols; ++c) {
       float t = 0.f;
@@ -197,7 +228,10 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(AppendParams p) {
       for (int s = 0; s < kMaxParts; ++s) t += v[c][s];
       if (n0 + c * kThreads < n_total) y[n0 + c * kThreads] = t;
     }
-  }
+  };
+  sum_chunk(threadIdx.x);
+  for (int n0 = threadIdx.x + kCols * kThreads; n0 < n_total; n0 += kCols * kThreads)
+    sum_chunk(n0);
   __syncthreads();
   float ss = 0.f;
   for (int n = threadIdx.x; n < p.d_c; n += kThreads) ss += y[n] * y[n];
@@ -208,20 +242,20 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(AppendParams p) {
   for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
   const float inv = 1.f / sqrtf(tot / p.d_c + p.eps);
 
-  const int pos = p.pos[b];
   if (pos < 0 || pos >= p.cache.max_len) return;
-  size_t phys;
-  if (p.cache.page_table == nullptr) {
-    phys = static_cast<size_t>(b) * p.cache.max_len + pos;
-  } else {
-    const int page = p.cache.page_table[static_cast<size_t>(b) * p.cache.max_pages +
-                                        pos / p.cache.page_size];
-    phys = static_cast<size_t>(page) * p.cache.page_size + pos % p.cache.page_size;
-  }
+  const size_t phys =
+      p.cache.page_table == nullptr
+          ? static_cast<size_t>(b) * p.cache.max_len + pos
+          : static_cast<size_t>(page) * p.cache.page_size + pos % p.cache.page_size;
   // The finished row, in place in y: the normalised latent, then the rotated
   // key pairs.
-  const T* gamma = static_cast<const T*>(p.gamma);
-  for (int n = threadIdx.x; n < p.d_c; n += kThreads) y[n] = y[n] * inv * ld(gamma + n);
+#pragma unroll
+  for (int j = 0; j < kGam; ++j) {
+    const int n = threadIdx.x + j * kThreads;
+    if (n < p.d_c) y[n] = y[n] * inv * static_cast<float>(gam[j]);
+  }
+  for (int n = threadIdx.x + kGam * kThreads; n < p.d_c; n += kThreads)
+    y[n] = y[n] * inv * ld(gamma + n);
   for (int i = threadIdx.x; i < p.d_r / 2; i += kThreads) {
     // The angle is reduced modulo 2 pi in fp64; the reduced angle's sine and
     // cosine are fp32-accurate.
