@@ -88,16 +88,22 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+  // W^UV rows of 128 elements (256 bytes, the width of the 64 banks) are
+  // stored with their 16-byte chunk c in slot c ^ 4 (row % 4): the
+  // transposing reads of the product below address four consecutive rows at
+  // once, which would otherwise fall in the same banks.
+  const int w_swz = d_head == kMaxHead ? 4 : 0;
   if constexpr (kOut) {
-    // Start W^UV[i] streaming into LDS: a linear copy of its d_latent x d_head
-    // bf16 elements, 1 KiB per wave instruction.
+    // Start W^UV[i] streaming into LDS, 1 KiB (four 256-byte rows at d_head
+    // 128) per wave instruction.
     const uint8_t* src = reinterpret_cast<const uint8_t*>(w_uv) +
-                         static_cast<size_t>(i % heads_per_token) * kLat * d_head * 2 + lane * 16;
+                         static_cast<size_t>(i % heads_per_token) * kLat * d_head * 2;
     const unsigned base = static_cast<unsigned>(
         reinterpret_cast<uintptr_t>((MLA_LDS uint8_t*)w_s));
     const int chunks = kLat * d_head * 2 / 1024;
+    const int lane_src = (lane & ~15) | ((lane & 15) ^ (w_swz * ((lane >> 4) & 3)));
     for (int j = wave; j < chunks; j += kThreads / 64)
-      load_to_lds16(src + j * 1024, base + j * 1024);
+      load_to_lds16(src + j * 1024 + lane_src * 16, base + j * 1024);
   }
 
   // Merge: this wave's request r and split subset p, 8 latents per lane.
@@ -280,10 +286,12 @@ __global__ __launch_bounds__(kThreads) void combine_rows_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) a[e] = static_cast<__bf16>(0.f);
           }
+          // (row k0 + tr_k and row k0 + tr_k + 4 have the same swizzle)
+          const int col = ((((nb * 32 + tr_n) >> 3) ^ (w_swz * (tr_k & 3))) << 3) | (tr_n & 7);
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (MLA_LDS i16x4_t*)(wl + (k0 + tr_k) * d_head + nb * 32 + tr_n));
+              (MLA_LDS i16x4_t*)(wl + (k0 + tr_k) * d_head + col));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (MLA_LDS i16x4_t*)(wl + (k0 + tr_k + 4) * d_head + nb * 32 + tr_n));
+              (MLA_LDS i16x4_t*)(wl + (k0 + tr_k + 4) * d_head + col));
           const bf16x8_t bop = __builtin_bit_cast(
               bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc2, 0, 0, 0);
