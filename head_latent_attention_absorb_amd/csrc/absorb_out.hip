@@ -102,6 +102,14 @@ __global__ __launch_bounds__(kThreads) void out_uv_kernel(
   }
 }
 
+// Weight blocks of 128 columns (256-byte rows, the width of the 64 LDS banks)
+// are staged with the 16-byte chunk c of row r in slot c ^ 4 (r % 4): the
+// transposing reads address four consecutive rows at once, which would
+// otherwise fall in the same banks.  Narrower blocks are stored as they are.
+template <int NB>
+__device__ __forceinline__ int w_slot_of(int chunk, int row) {
+  return NB == 128 ? chunk ^ ((row & 3) << 2) : chunk;
+}
 // bf16 MFMA form of both products, for the DeepSeek-V2 widths:
 //   Y[b, i, n] = sum_{k < K} X[b, i, k] W[i, k, n]      (n < N, per head i)
 // absorption: X = q^C (K = d_head = 128), W = W^UK (N = d_latent = 512)
@@ -147,6 +155,9 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
   const int G = lane >> 4, r16 = lane & 15;
   const int tr_k = ((G >> 1) << 3) + (r16 >> 2);
   const int tr_n = ns * 32 + ((G & 1) << 4) + ((r16 & 3) << 2);
+  // (its slot in the swizzled weight block: rows k0 + tr_k and k0 + tr_k + 4,
+  // k0 a multiple of 16, share the row's swizzle)
+  const int tr_col = (w_slot_of<NB>(tr_n >> 3, tr_k) << 3) | (tr_n & 7);
 
   // A operand fragments of one 32-row M tile: row m0 + l32, K elements
   // kp*KW + ks*16 + half*8 .. +7.  Rows past `batch` are zero.
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
     constexpr int kCopies = K / kRowsPerCopy;
     static_assert(K % kRowsPerCopy == 0 && kCopies % 4 == 0, "");
     const __bf16* src = W + (static_cast<size_t>(i) * K + lane / kLanesPerRow) * N + n0 +
-                        (lane % kLanesPerRow) * 8;
+                        w_slot_of<NB>(lane % kLanesPerRow, lane / kLanesPerRow) * 8;
     const unsigned base =
         static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS __bf16*)w_s));
 #pragma unroll 4
@@ -209,9 +220,9 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const int k0 = kp * KW + ks * 16;
       const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k) * NB + tr_n));
+          (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k) * NB + tr_col));
       const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k + 4) * NB + tr_n));
+          (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k + 4) * NB + tr_col));
       const bf16x8_t bop =
           __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bop, acc, 0, 0, 0);
@@ -310,7 +321,7 @@ __global__ __launch_bounds__(256) void head_proj_rows_kernel(
     constexpr int kCopies = K / kRowsPerCopy;
     static_assert(K % kRowsPerCopy == 0 && kCopies % 4 == 0, "");
     const __bf16* src = W + (static_cast<size_t>(i) * K + lane / kLanesPerRow) * N + n0 +
-                        (lane % kLanesPerRow) * 8;
+                        w_slot_of<NB>(lane % kLanesPerRow, lane / kLanesPerRow) * 8;
     const unsigned base =
         static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS __bf16*)w_s));
 #pragma unroll 4
@@ -349,14 +360,17 @@ __global__ __launch_bounds__(256) void head_proj_rows_kernel(
   const int G = lane >> 4, r16 = lane & 15;
   const int tr_k = ((G >> 1) << 3) + (r16 >> 2);
   const int tr_n = ns * 32 + ((G & 1) << 4) + ((r16 & 3) << 2);
+  // (its slot in the swizzled weight block: rows k0 + tr_k and k0 + tr_k + 4,
+  // k0 a multiple of 16, share the row's swizzle)
+  const int tr_col = (w_slot_of<NB>(tr_n >> 3, tr_k) << 3) | (tr_n & 7);
   bf16x8_t bfr[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     const int k0 = kp * KW + ks * 16;
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k) * NB + tr_n));
+        (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k) * NB + tr_col));
     const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k + 4) * NB + tr_n));
+        (MLA_LDS i16x4_t*)(w_s + (k0 + tr_k + 4) * NB + tr_col));
     bfr[ks] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
