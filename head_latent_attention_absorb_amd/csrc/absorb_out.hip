@@ -102,13 +102,17 @@ __global__ __launch_bounds__(kThreads) void out_uv_kernel(
   }
 }
 
-// Weight blocks of 128 columns (256-byte rows, the width of the 64 LDS banks)
-// are staged with the 16-byte chunk c of row r in slot c ^ 4 (r % 4): the
-// transposing reads address four consecutive rows at once, which would
-// otherwise fall in the same banks.  Narrower blocks are stored as they are.
+// The transposing reads of a weight block address four consecutive rows at
+// once (the same columns of each), which would fall in the same banks where
+// the rows are a multiple of 256 bytes (the width of the 64 LDS banks)
+// apart.  The 16-byte chunk c of row r is therefore staged in slot
+//   c ^ 4 (r % 4)          for 128-column blocks (256-byte rows),
+//   c ^ 4 ((r / 2) % 2)    for 64-column blocks (two 128-byte rows per 256 bytes),
+// which puts the four rows' chunks in different banks.
 template <int NB>
 __device__ __forceinline__ int w_slot_of(int chunk, int row) {
-  return NB == 128 ? chunk ^ ((row & 3) << 2) : chunk;
+  static_assert(NB == 128 || NB == 64, "");
+  return NB == 128 ? chunk ^ ((row & 3) << 2) : chunk ^ (((row >> 1) & 1) << 2);
 }
 // bf16 MFMA form of both products, for the DeepSeek-V2 widths:
 //   Y[b, i, n] = sum_{k < K} X[b, i, k] W[i, k, n]      (n < N, per head i)
