@@ -142,8 +142,9 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
 
   // Tile loads: instruction j of the stage (wave j % kWaves issues it) fills
   // 1 KiB: j < 16 the k^C rows (16 units of 16 bytes per 256-byte row, unit
-  // c at c ^ (row & 15)), j < 24 the k^R rows (8 units per 128-byte row, unit
-  // c at c ^ (row & 7)), else the value rows (16 units per row, unit v at
+  // c at c ^ (row & 15)), j < 24 the k^R rows (8 units per 128-byte row, two
+  // rows per 256 bytes of banks, unit c at c ^ ((row >> 1) & 7)), else the
+  // value rows (16 units per row, unit v at
   // v ^ ((row & 3) << 2), i.e. 8-byte unit u at u ^ ((row & 3) << 3)).  Rows
   // past the length repeat row len - 1 (finite values, masked to weight 0).
   const __bf16* kc_base = p.k_c + (static_cast<size_t>(b) * p.n_heads + i) * p.max_len * kDh;
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
       } else if (j < 24) {
         const int unit = (j - 16) * 64 + lane, r = unit >> 3, c = unit & 7;
         const int row = min(t * kTile + r, len - 1);
-        src = cr_base + static_cast<size_t>(row) * kRow + ((c ^ (r & 7)) << 3);
+        src = cr_base + static_cast<size_t>(row) * kRow + ((c ^ ((r >> 1) & 7)) << 3);
       } else {
         const int unit = (j - 24) * 64 + lane, r = unit >> 4, c = unit & 15;
         const int row = min(t * kTile + r, len - 1);
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
             kf = *reinterpret_cast<const bf16x8_t*>(st + r * 256 + (((ks * 2 + half) ^ (r & 15)) << 4));
           else
             kf = *reinterpret_cast<const bf16x8_t*>(st + kKcBytes + r * 128 +
-                                                    ((((ks - 8) * 2 + half) ^ (r & 7)) << 4));
+                                                    ((((ks - 8) * 2 + half) ^ ((r >> 1) & 7)) << 4));
 #pragma unroll
           for (int qt = 0; qt < kQT; ++qt)
             s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qt][ks], s[qt], 0, 0, 0);
