@@ -286,6 +286,29 @@ def test_out_uv_bf16(batch):
     assert_close(from_dev(o), oracle.project_out(o_lat_np, case.w_uv), "bf16", "o")
 
 
+@pytest.mark.parametrize("batch", [1, 40])
+def test_projections_other_widths_bf16(batch):
+    """The bf16 projection kernels at widths other than DeepSeek-V2's: d_c = 256
+    (two 128-column blocks of W^UK per head) for the absorption and d_h = 64
+    (one 64-column block of W^UV) for the output, with one M tile and with two
+    (the row-chunk form), against the oracle."""
+    cfg = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1, n_heads=24, d_latent=256)
+    case = make_case(cfg, 8)
+    dc = DevCase(case)
+    _log(f"[projection widths] batch={batch} d_c=256")
+    q_cat = mla.absorb_q(dc.q_c, dc.q_r, dc.w_uk)
+    torch.cuda.synchronize()
+    assert_close(from_dev(q_cat), oracle.absorb_query(case.q_c, case.q_r, case.w_uk), "bf16",
+                 "q_cat")
+    cfg_o = DSV2.replace(batch=batch, len_lo=1, len_hi=1, max_len=1, n_heads=24, d_head=64)
+    case_o = make_case(cfg_o, 9)
+    o_lat_np = draw_latent_output(cfg_o, 9)
+    _log(f"[projection widths] batch={batch} d_h=64")
+    o = mla.out_uv(_bf16_dev(o_lat_np), DevCase(case_o).w_uv)
+    torch.cuda.synchronize()
+    assert_close(from_dev(o), oracle.project_out(o_lat_np, case_o.w_uv), "bf16", "o")
+
+
 @pytest.mark.parametrize("batch", [33, 65, 129, 200, 255])
 def test_projections_row_chunks_match_one_tile(batch):
     """Above one M tile (32 rows) both projections stage chunks of rows in
