@@ -120,18 +120,18 @@ __device__ __forceinline__ int w_slot_of(int chunk, int row) {
 // output:     X = o_lat (K = d_latent = 512), W = W^UV (N = d_head = 128)
 // One workgroup owns head i and an NB-column block of W, stages that
 // [K x NB] block in LDS with direct-to-LDS loads, all issued at once (the
-// only HBM stream: every weight element is read once), and computes all
-// batch rows with v_mfma_f32_32x32x16_bf16.  The N / NB blocks of a head are
+// only HBM stream: every weight element is read once), and computes the
+// batch's rows (at most 32: one M tile; larger batches run on
+// head_proj_rows_kernel) with v_mfma_f32_32x32x16_bf16.  The N / NB blocks of a head are
 // consecutive work ids, and consecutive work ids run on one XCD (workgroup x
 // runs on XCD x % 8): the blocks of a weight row are read from one L2 at
 // about the same time.  The 4 waves split the block into NS column
 // sub-blocks of 32 and 4/NS K parts; K parts are summed through LDS.  Batch
-// rows are the A operand (M tiles of 32, loaded straight from global memory,
-// zero past `batch`); the weight is the B operand, read with the transposing
-// LDS read (within a 16-lane group, lane i receives element i%4 of the
-// 8-byte chunk addressed by lane 4j + i/4, for j = 0..3).  Each M tile's
-// results pass through LDS so that every output row is written in 16-byte
-// pieces.
+// rows are the A operand (loaded straight from global memory, zero past
+// `batch`); the weight is the B operand, read with the transposing LDS read
+// (within a 16-lane group, lane i receives element i%4 of the 8-byte chunk
+// addressed by lane 4j + i/4, for j = 0..3).  The results pass through LDS
+// so that every output row is written in 16-byte pieces.
 template <int K, int NB, int NS>
 __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
     const __bf16* __restrict__ X, const __bf16* __restrict__ W, __bf16* __restrict__ Y,
@@ -163,25 +163,23 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
   // k0 a multiple of 16, share the row's swizzle)
   const int tr_col = (w_slot_of<NB>(tr_n >> 3, tr_k) << 3) | (tr_n & 7);
 
-  // A operand fragments of one 32-row M tile: row m0 + l32, K elements
-  // kp*KW + ks*16 + half*8 .. +7.  Rows past `batch` are zero.
-  bf16x8_t a[KSTEPS], a_next[KSTEPS];
-  auto load_a = [&](int m0, bf16x8_t(&dst)[KSTEPS]) {
-    const int b = m0 + l32;
-    const __bf16* xrow = X + (static_cast<size_t>(b) * n_heads + i) * K + kp * KW + half * 8;
+  // A operand fragments of the M tile (batch <= 32 rows; more rows run on
+  // head_proj_rows_kernel): row l32, K elements kp*KW + ks*16 + half*8 .. +7.
+  // Rows past `batch` are zero.  They are requested before the weight block
+  // so that both HBM round trips overlap.
+  bf16x8_t a[KSTEPS];
+  {
+    const __bf16* xrow = X + (static_cast<size_t>(l32) * n_heads + i) * K + kp * KW + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      if (b < batch) {
-        dst[ks] = *reinterpret_cast<const bf16x8_t*>(xrow + ks * 16);
+      if (l32 < batch) {
+        a[ks] = *reinterpret_cast<const bf16x8_t*>(xrow + ks * 16);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dst[ks][j] = static_cast<__bf16>(0.f);
+        for (int j = 0; j < 8; ++j) a[ks][j] = static_cast<__bf16>(0.f);
       }
     }
-  };
-  // The first tile's rows are requested before the weight block so that both
-  // HBM round trips overlap.
-  load_a(0, a);
+  }
 
   // Stage W[i][0:K][n0:n0+NB] (row-major, NB contiguous) in LDS, in the same
   // layout: one wave instruction copies 1 KiB, rows of NB elements.
@@ -194,9 +192,11 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
                         w_slot_of<NB>(lane % kLanesPerRow, lane / kLanesPerRow) * 8;
     const unsigned base =
         static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS __bf16*)w_s));
-#pragma unroll 4
-    for (int j = wave; j < kCopies; j += 4)
+#pragma unroll
+    for (int jj = 0; jj < kCopies / 4; ++jj) {
+      const int j = jj * 4 + wave;
       load_to_lds16(src + static_cast<size_t>(j) * kRowsPerCopy * N, base + j * 1024);
+    }
   }
 
   // The RoPE tail of the absorbed query is copied unchanged (absorption
@@ -214,9 +214,7 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int m0 = 0; m0 < batch; m0 += 32) {
-    // The next M tile's rows are requested before this tile's products.
-    if (m0 + 32 < batch) load_a(m0 + 32, a_next);
+  {
     f32x16_t acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
@@ -255,16 +253,10 @@ __global__ __launch_bounds__(256) void head_proj_mfma_kernel(
     constexpr int kRowChunks = NB / 8;
     for (int c = tid; c < 32 * kRowChunks; c += 256) {
       const int r = c / kRowChunks, ch = c - r * kRowChunks;
-      if (m0 + r < batch)
-        *reinterpret_cast<bf16x8_t*>(Y + (static_cast<size_t>(m0 + r) * n_heads + i) * y_row +
+      if (r < batch)
+        *reinterpret_cast<bf16x8_t*>(Y + (static_cast<size_t>(r) * n_heads + i) * y_row +
                                      n0 + ch * 8) =
             *reinterpret_cast<const bf16x8_t*>(y_s + r * NB + ch * 8);
-    }
-    // y_s and red are rewritten by the next tile.
-    __syncthreads();
-    if (m0 + 32 < batch) {
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) a[ks] = a_next[ks];
     }
   }
 }
@@ -328,9 +320,11 @@ __global__ __launch_bounds__(256) void head_proj_rows_kernel(
                         w_slot_of<NB>(lane % kLanesPerRow, lane / kLanesPerRow) * 8;
     const unsigned base =
         static_cast<unsigned>(reinterpret_cast<uintptr_t>((MLA_LDS __bf16*)w_s));
-#pragma unroll 4
-    for (int j = wave; j < kCopies; j += 4)
+#pragma unroll
+    for (int jj = 0; jj < kCopies / 4; ++jj) {
+      const int j = jj * 4 + wave;
       load_to_lds16(src + static_cast<size_t>(j) * kRowsPerCopy * N, base + j * 1024);
+    }
   }
   // The chunk's rows, swizzled (see above); one instruction fills 1 KiB.
   {
