@@ -96,6 +96,9 @@ CASES = [
     ("skew_with_empty", dict(batch=8, max_len=4096), [0, 4096, 0, 5, 33, 0, 1, 2047], 1),
     ("ragged_long", dict(batch=4, max_len=32768), [32768, 16384, 20001, 17], 1),
     ("paged_b128", dict(batch=128, max_len=2048, page_size=64), None, 1),
+    # near the largest balanced batch on 256 compute units (batch x head
+    # groups must stay below the CU count): four lengths per planner lane
+    ("b200_ragged", dict(batch=200, max_len=1024), None, 1),
     ("paged_skew", dict(batch=5, max_len=8192, page_size=64), [8192, 1, 64, 4000, 0], 1),
     ("two_tokens", dict(batch=3, max_len=4096), [4096, 2, 333], 2),
     # 24-token pages cap a partition at 1504 tokens (63 pages' worth, whatever
