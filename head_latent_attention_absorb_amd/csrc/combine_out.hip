@@ -341,7 +341,10 @@ template <bool kOut>
 void launch_rows_sized(const DecodeArgs& a, int p_log2, const dim3& grid, const void* w_uv,
                        void* out, int d_head) {
   const int nk = (sizing_splits(a) + (1 << p_log2) - 1) >> p_log2;  // splits of wave 0
-  if (nk <= 2)
+  // (A mean of two splits per wave takes batches of four: in a length-balanced
+  // plan the longer requests hold more than the mean, and a second batch is a
+  // second memory round trip.)
+  if (nk <= 1)
     launch_rows<kOut, 2>(a, p_log2, grid, w_uv, out, d_head);
   else if (nk <= 4)
     launch_rows<kOut, 4>(a, p_log2, grid, w_uv, out, d_head);
